@@ -1,0 +1,108 @@
+"""Host-side analysis of scheduling: task-trace decoding, tail idle time,
+scheduling overhead, and the small formulas the Weave write-ups use to reason
+about wave tails and speedups.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict
+
+import numpy as np
+
+KIND_SHIFT = 27
+KINDS = {1: "ROUTE", 2: "POS", 3: "PERM", 4: "UP", 5: "DOWN", 6: "SUP", 7: "SDOWN"}
+CLOCK_HZ = 100e6   # s_memrealtime rate
+
+
+def wave_tail(slots: int, blocks: int) -> Dict[str, float]:
+    """Hardware wave quantisation: `blocks` equal blocks on `slots` resident
+    slots run in ceil(blocks/slots) waves; the last wave leaves
+    slots*waves - blocks slots idle (xxqk.cn/news/665650 s1.1 and
+    m.xxqk.cn/news/657744 s1.2 work this example)."""
+    waves = -(-blocks // slots)
+    last = blocks - (waves - 1) * slots
+    idle = slots * waves - blocks
+    return {"waves": waves, "last_wave_blocks": last, "idle_slots": idle,
+            "efficiency": blocks / float(slots * waves)}
+
+
+def amdahl(r: float, s: float) -> float:
+    """End-to-end speedup when a fraction r of the time is sped up s-fold
+    (xxqk.cn/news/665650 s3.4)."""
+    return 1.0 / ((1.0 - r) + r / s)
+
+
+def idle_bound(alpha: float) -> float:
+    """Upper bound on the gain from filling an idle fraction alpha of SM time
+    (xxqk.cn/news/665650 s4.1)."""
+    return 1.0 / (1.0 - alpha)
+
+
+def overlap_efficiency(t: float, a: float, b: float) -> float:
+    """1 - (t - max(a,b)) / min(a,b): 1 when the shorter of two overlapped
+    streams is fully hidden, 0 when they serialise (hncyxsy.com/news/277526,
+    multi-stream overlap section)."""
+    return 1.0 - (t - max(a, b)) / min(a, b)
+
+
+def decode_trace(raw: np.ndarray) -> Dict[str, np.ndarray]:
+    """Records of 4 uint64: claim requested, task start, task body end, meta
+    (task id | worker << 32 | xcc << 48).  Unused (zero) records dropped."""
+    raw = np.asarray(raw).view(np.uint64).reshape(-1, 4)
+    used = raw[:, 2] != 0
+    raw = raw[used]
+    meta = raw[:, 3]
+    task = (meta & np.uint64(0xffffffff)).astype(np.int64)
+    return {
+        "t_req": raw[:, 0].astype(np.int64),
+        "t_start": raw[:, 1].astype(np.int64),
+        "t_end": raw[:, 2].astype(np.int64),
+        "task": task,
+        "kind": task >> KIND_SHIFT,
+        "payload": task & ((1 << KIND_SHIFT) - 1),
+        "worker": ((meta >> np.uint64(32)) & np.uint64(0xffff)).astype(np.int64),
+        "xcc": ((meta >> np.uint64(48)) & np.uint64(0xff)).astype(np.int64),
+    }
+
+
+def schedule_stats(tr: Dict[str, np.ndarray], workers: int) -> Dict[str, float]:
+    """Busy, claim-wait and tail-idle shares of worker time over the kernel.
+
+    Kernel span = first claim to last task end.  A worker is busy while it
+    runs a task body; claim overhead is the time from asking for a task to
+    starting it; tail idle is, per worker, the time from its last task end to
+    the kernel end, summed over workers."""
+    if tr["t_end"].size == 0:
+        return {}
+    t0 = int(tr["t_req"].min())
+    t1 = int(tr["t_end"].max())
+    span = max(1, t1 - t0)
+    busy = float(np.sum(tr["t_end"] - tr["t_start"]))
+    wait = float(np.sum(tr["t_start"] - tr["t_req"]))
+    last_end = {}
+    for w, e in zip(tr["worker"], tr["t_end"]):
+        last_end[int(w)] = max(last_end.get(int(w), 0), int(e))
+    tail = float(sum(t1 - e for e in last_end.values()) + (workers - len(last_end)) * span)
+    total = float(span) * workers
+    return {
+        "span_us": span / CLOCK_HZ * 1e6,
+        "busy_frac": busy / total,
+        "claim_wait_frac": wait / total,
+        "tail_idle_frac": tail / total,
+        "tasks": int(tr["t_end"].size),
+    }
+
+
+def by_kind(tr: Dict[str, np.ndarray]) -> Dict[str, Dict[str, float]]:
+    out = {}
+    for k, name in KINDS.items():
+        m = tr["kind"] == k
+        if m.any():
+            d = (tr["t_end"][m] - tr["t_start"][m]) / CLOCK_HZ * 1e6
+            out[name] = {"n": int(m.sum()), "mean_us": float(d.mean()), "sum_us": float(d.sum())}
+    return out
+
+
+def geomean(xs) -> float:
+    xs = [x for x in xs if x and x > 0]
+    return math.exp(sum(math.log(x) for x in xs) / len(xs)) if xs else float("nan")

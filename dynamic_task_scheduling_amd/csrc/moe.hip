@@ -1,0 +1,389 @@
+// moe.hip -- host side of the C ABI declared in include/moe.h: descriptor
+// validation, workspace carving, and the launches of each scheduling mode.
+// All device work lives in sched.hpp / stages.hpp / tile.hpp.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "sched.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxWorkersBound = 4096;  // queue slack for the largest grid
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  Params p;          // geometry only (pointers filled by carve)
+  int esz;
+  size_t off_ctrl, off_slots, off_logits, off_idx, off_w, off_hist, off_rtb, off_counts,
+      off_offsets, off_eorder, off_perm, off_rw, off_slotpos, off_mtiles, off_cnt_perm,
+      off_cnt_down, off_cnt_sdown, off_perm_list, off_xp, off_h, off_hs, total;
+};
+
+int validate(const moe_desc* d) {
+  if (!d) return MOE_ERR_ARG;
+  if (d->T < 0 || d->d <= 0 || d->E < 1 || d->E > kMaxE || d->k < 1 || d->k > kMaxK ||
+      d->k > d->E || d->f <= 0)
+    return MOE_ERR_ARG;
+  const int e_end = d->e_end > 0 ? d->e_end : d->E;
+  if (d->e_begin < 0 || e_end > d->E || d->e_begin >= e_end) return MOE_ERR_ARG;
+  if (d->n_shared < 0 || d->n_shared > 4) return MOE_ERR_ARG;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_ARG;
+  if (d->mode < MOE_DYNAMIC || d->mode > MOE_MULTI_KERNEL) return MOE_ERR_ARG;
+  if (d->split_policy < MOE_SPLIT_COST_MODEL || d->split_policy > MOE_SPLIT_NONE) return MOE_ERR_ARG;
+  if (d->split_k < 0 || d->split_k > 8) return MOE_ERR_ARG;
+  if (d->d % kBN || d->f % kBN) return MOE_ERR_UNSUPPORTED;
+  if (d->n_shared > 0 && (d->f_shared <= 0 || d->f_shared % kBN)) return MOE_ERR_UNSUPPORTED;
+  if ((d->flags & MOE_FLAG_TRACE) && (!d->trace || d->trace_cap <= 0)) return MOE_ERR_ARG;
+  // the queue ids must fit the payload field
+  const long long rows = (long long)d->T * d->k;
+  const long long mt = rows / 128 + (e_end - d->e_begin);
+  if (mt * (d->d / kBN) * 8 >= (1ll << kKindShift)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+void make_layout(const moe_desc* d, Layout* L) {
+  Params& p = L->p;
+  memset(&p, 0, sizeof p);
+  p.T = d->T;
+  p.d = d->d;
+  p.E = d->E;
+  p.k = d->k;
+  p.f = d->f;
+  p.e_begin = d->e_begin;
+  const int e_end = d->e_end > 0 ? d->e_end : d->E;
+  p.E_loc = e_end - d->e_begin;
+  p.n_shared = d->n_shared;
+  p.fs = d->n_shared > 0 ? d->f_shared : kBN;
+  p.dtype = d->dtype;
+  L->esz = d->dtype == MOE_BF16 ? 2 : 4;
+  p.n_rt = (d->T + kTB - 1) / kTB;
+  p.hist_ld = std::max(4, (p.n_rt + 3) / 4 * 4);
+  p.n_up_n = d->f / kBN;
+  p.n_down_n = d->d / kBN;
+  int sk = d->split_k;
+  if (sk == 0) sk = std::max(1, std::min(8, d->f / 3584));
+  p.splitk = std::min(sk, p.n_up_n);
+  p.n_s_up_n = p.fs / kBN;
+  p.n_smt = (d->T + 127) / 128;
+  // rows per permute task: about 256 KB moved, a power of two in [8, 128]
+  int pr = 128;
+  while (pr > 8 && (long long)pr * d->d * L->esz > 262144) pr >>= 1;
+  p.perm_rows = pr;
+  p.pch = 128 / pr;
+  const long long R = (long long)d->T * d->k;
+  p.max_mt = (int)(R / 128 + p.E_loc + 1);
+  p.max_perm = (int)((R + pr - 1) / pr + p.max_mt);
+  p.n_sup = p.n_shared * p.n_smt * p.n_s_up_n;
+  p.n_sdown = p.n_shared * p.n_smt * p.n_down_n;
+  const long long qa = 2ll * p.n_rt + p.n_sup;
+  const long long qc = (long long)p.max_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sdown +
+                       p.max_perm;
+  p.q_cap = (int)(std::max(qa, qc) + kMaxWorkersBound);
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + std::max<size_t>(bytes, 1));
+    return at;
+  };
+  const size_t Tk = (size_t)d->T * d->k;
+  L->off_ctrl = take(sizeof(int) * CW_COUNT * kCtrlStride);
+  L->off_slots = take(sizeof(int) * (size_t)kNumQueues * p.q_cap);
+  L->off_logits = take(sizeof(float) * (size_t)d->T * d->E);
+  L->off_idx = take(sizeof(int) * Tk);
+  L->off_w = take(sizeof(float) * Tk);
+  L->off_hist = take(sizeof(int) * (size_t)p.E_loc * p.hist_ld);
+  L->off_rtb = take(sizeof(int) * (size_t)p.E_loc * p.hist_ld);
+  L->off_counts = take(sizeof(int) * p.E_loc);
+  L->off_offsets = take(sizeof(int) * (p.E_loc + 1));
+  L->off_eorder = take(sizeof(int) * p.E_loc);
+  L->off_perm = take(sizeof(int) * Tk);
+  L->off_rw = take(sizeof(float) * Tk);
+  L->off_slotpos = take(sizeof(int) * Tk);
+  L->off_mtiles = take(sizeof(MTile) * p.max_mt);
+  L->off_cnt_perm = take(sizeof(int) * p.max_mt);
+  L->off_cnt_down = take(sizeof(int) * (size_t)p.max_mt * p.splitk);
+  L->off_cnt_sdown = take(sizeof(int) * (size_t)std::max(1, p.n_shared * p.n_smt));
+  L->off_perm_list = take(sizeof(int) * p.max_perm);
+  L->off_xp = take((size_t)L->esz * Tk * d->d);
+  L->off_h = take((size_t)L->esz * Tk * d->f);
+  L->off_hs = take((size_t)L->esz * d->n_shared * d->T * (d->n_shared ? d->f_shared : 0));
+  L->total = o;
+}
+
+void carve(Layout* L, void* ws) {
+  Params& p = L->p;
+  char* b = static_cast<char*>(ws);
+  p.ctrl = reinterpret_cast<int*>(b + L->off_ctrl);
+  p.slots = reinterpret_cast<int*>(b + L->off_slots);
+  p.logits = reinterpret_cast<float*>(b + L->off_logits);
+  p.idx = reinterpret_cast<int*>(b + L->off_idx);
+  p.w = reinterpret_cast<float*>(b + L->off_w);
+  p.hist = reinterpret_cast<int*>(b + L->off_hist);
+  p.rt_base = reinterpret_cast<int*>(b + L->off_rtb);
+  p.counts = reinterpret_cast<int*>(b + L->off_counts);
+  p.offsets = reinterpret_cast<int*>(b + L->off_offsets);
+  p.eorder = reinterpret_cast<int*>(b + L->off_eorder);
+  p.perm = reinterpret_cast<int*>(b + L->off_perm);
+  p.rw = reinterpret_cast<float*>(b + L->off_rw);
+  p.slot_pos = reinterpret_cast<int*>(b + L->off_slotpos);
+  p.mtiles = reinterpret_cast<MTile*>(b + L->off_mtiles);
+  p.cnt_perm = reinterpret_cast<int*>(b + L->off_cnt_perm);
+  p.cnt_down = reinterpret_cast<int*>(b + L->off_cnt_down);
+  p.cnt_sdown = reinterpret_cast<int*>(b + L->off_cnt_sdown);
+  p.perm_list = reinterpret_cast<int*>(b + L->off_perm_list);
+  p.Xp = b + L->off_xp;
+  p.H = b + L->off_h;
+  p.Hs = b + L->off_hs;
+}
+
+// Resident persistent workgroups per CU for each kernel, per device.
+struct DevInfo {
+  int cus = 0;
+  int bpc[2][2] = {{0, 0}, {0, 0}};  // [dtype][dynamic, static]
+};
+std::mutex g_mu;
+DevInfo g_dev[64];
+
+int dev_info(int dev, DevInfo* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  DevInfo& di = g_dev[dev];
+  if (di.cus == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MOE_ERR_HIP;
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_dynamic<float>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    di.bpc[0][0] = b;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_static<float>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    di.bpc[0][1] = b;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_dynamic<bf16_t>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    di.bpc[1][0] = b;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_static<bf16_t>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    di.bpc[1][1] = b;
+    di.cus = cus;
+  }
+  *out = di;
+  return MOE_OK;
+}
+
+int workers_for(const moe_desc* d, int* workers, int* cus, int* bpc) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  DevInfo di;
+  int rc = dev_info(dev, &di);
+  if (rc) return rc;
+  const int b = di.bpc[d->dtype == MOE_BF16][d->mode == MOE_STATIC_PARTITION];
+  if (b < 1) return MOE_ERR_UNSUPPORTED;
+  int w = di.cus * b;
+  if (d->max_workers > 0) w = std::min(w, d->max_workers);
+  *workers = std::min(w, kMaxWorkersBound);
+  if (cus) *cus = di.cus;
+  if (bpc) *bpc = b;
+  return MOE_OK;
+}
+
+#define HIP_OK(x)                          \
+  do {                                     \
+    if ((x) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+template <typename Elem>
+int launch_layer(const moe_desc* d, Params& p, hipStream_t s) {
+  const int reset_blocks = (int)std::min<long long>(
+      1024, ((long long)kNumQueues * p.q_cap + kThreads - 1) / kThreads + 1);
+  hipLaunchKernelGGL(k_reset, dim3(reset_blocks), dim3(kThreads), 0, s, p);
+  HIP_OK(hipGetLastError());
+  if (d->mode == MOE_DYNAMIC) {
+    hipLaunchKernelGGL(k_dynamic<Elem>, dim3(p.workers), dim3(kThreads), 0, s, p);
+  } else if (d->mode == MOE_STATIC_PARTITION) {
+    hipLaunchKernelGGL(k_static<Elem>, dim3(p.workers), dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+    HIP_OK(hipGetLastError());
+    hipLaunchKernelGGL(k_stage_build<Elem>, dim3(1), dim3(kThreads), 0, s, p);
+    HIP_OK(hipGetLastError());
+    hipLaunchKernelGGL(k_stage_pos<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+    HIP_OK(hipGetLastError());
+    hipLaunchKernelGGL(k_stage_perm<Elem>, dim3(p.max_perm), dim3(kThreads), 0, s, p);
+    HIP_OK(hipGetLastError());
+    hipLaunchKernelGGL(k_stage_up<Elem>, dim3(p.max_mt * p.n_up_n + p.n_sup), dim3(kThreads), 0, s, p);
+    HIP_OK(hipGetLastError());
+    hipLaunchKernelGGL(k_stage_down<Elem>, dim3(p.max_mt * p.n_down_n * p.splitk + p.n_sdown),
+                       dim3(kThreads), 0, s, p);
+  }
+  HIP_OK(hipGetLastError());
+  return MOE_OK;
+}
+
+int copy_routing(const moe_desc* d, const Params& p, const moe_routing* r, hipStream_t s) {
+  if (!r) return MOE_OK;
+  const size_t Tk = (size_t)d->T * d->k;
+  auto cp = [&](void* dst, const void* src, size_t bytes) {
+    if (!dst || bytes == 0) return hipSuccess;
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+  };
+  HIP_OK(cp(r->logits, p.logits, sizeof(float) * d->T * d->E));
+  HIP_OK(cp(r->topk_idx, p.idx, sizeof(int) * Tk));
+  HIP_OK(cp(r->topk_w, p.w, sizeof(float) * Tk));
+  HIP_OK(cp(r->expert_counts, p.counts, sizeof(int) * p.E_loc));
+  HIP_OK(cp(r->offsets, p.offsets, sizeof(int) * (p.E_loc + 1)));
+  HIP_OK(cp(r->perm, p.perm, sizeof(int) * Tk));
+  HIP_OK(cp(r->slot_pos, p.slot_pos, sizeof(int) * Tk));
+  return MOE_OK;
+}
+
+int fill_params(const moe_desc* d, Layout* L, void* ws, size_t ws_bytes) {
+  int rc = validate(d);
+  if (rc) return rc;
+  make_layout(d, L);
+  if (!ws || ws_bytes < L->total) return MOE_ERR_WORKSPACE;
+  carve(L, ws);
+  Params& p = L->p;
+  rc = workers_for(d, &p.workers, nullptr, nullptr);
+  if (rc) return rc;
+  p.mode = d->mode;
+  p.split_policy = d->split_policy;
+  p.fixed_mem = d->fixed_mem_workers;
+  p.flags = d->flags;
+  if (!(p.flags & MOE_FLAG_REF_SYNC)) p.flags |= MOE_FLAG_PHASE_SYNC;
+  const long long ms = d->timeout_ms > 0 ? d->timeout_ms : 2000;
+  p.timeout_ticks = ms * 100000ll;  // 100 MHz constant clock
+  // cost model constants: per-CU bf16 MFMA rate at ~50% of peak, per-CU
+  // gather bandwidth, and device HBM bandwidth (measured on MI355X)
+  p.cm_mfma_rate = (d->dtype == MOE_BF16 ? 4.9e12f : 0.3e12f);
+  p.cm_cu_bw = 60e9f;
+  p.cm_hbm_bw = 6.0e12f;
+  p.cm_slack = 0.5f;
+  p.trace = (d->flags & MOE_FLAG_TRACE) ? d->trace : nullptr;
+  p.trace_cap = d->trace_cap;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_desc* d) {
+  if (validate(d) != MOE_OK) return 0;
+  Layout L;
+  make_layout(d, &L);
+  return L.total;
+}
+
+int moe_query(const moe_desc* d, moe_info* info) {
+  int rc = validate(d);
+  if (rc) return rc;
+  if (!info) return MOE_ERR_ARG;
+  Layout L;
+  make_layout(d, &L);
+  memset(info, 0, sizeof *info);
+  rc = workers_for(d, &info->workers, &info->cus, &info->blocks_per_cu);
+  if (rc) return rc;
+  info->route_tiles = L.p.n_rt;
+  info->up_ntiles = L.p.n_up_n;
+  info->down_ntiles = L.p.n_down_n;
+  info->split_k = L.p.splitk;
+  info->permute_rows = L.p.perm_rows;
+  info->max_mtiles = L.p.max_mt;
+  info->max_tasks = L.p.q_cap;
+  info->workspace_bytes = L.total;
+  return MOE_OK;
+}
+
+int moe_layer(const moe_desc* d, const void* x, const moe_weights* w, float* y,
+              const moe_routing* routing, void* workspace, size_t ws_bytes, void* stream) {
+  Layout L;
+  int rc = fill_params(d, &L, workspace, ws_bytes);
+  if (rc) return rc;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !w || !y || !w->w_router || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_ARG;
+  if (d->n_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_ARG;
+  Params& p = L.p;
+  p.x = x;
+  p.wr = w->w_router;
+  p.bias = w->router_bias;
+  p.wg = w->w_gate;
+  p.wu = w->w_up;
+  p.wd = w->w_down;
+  p.sg = w->ws_gate;
+  p.su = w->ws_up;
+  p.sd = w->ws_down;
+  p.y = y;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = d->dtype == MOE_BF16 ? launch_layer<bf16_t>(d, p, s) : launch_layer<float>(d, p, s);
+  if (rc) return rc;
+  rc = copy_routing(d, p, routing, s);
+  if (rc) return rc;
+  if (d->flags & MOE_FLAG_CHECK) return moe_last_device_error(d, workspace, stream);
+  return MOE_OK;
+}
+
+int moe_route_from_logits(const moe_desc* d, const float* logits, const moe_routing* routing,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  Layout L;
+  int rc = fill_params(d, &L, workspace, ws_bytes);
+  if (rc) return rc;
+  if (d->T == 0) return MOE_OK;
+  if (!logits) return MOE_ERR_ARG;
+  Params& p = L.p;
+  p.route_from_logits = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_OK(hipMemcpyAsync(p.logits, logits, sizeof(float) * d->T * d->E, hipMemcpyDeviceToDevice, s));
+  const int reset_blocks = (int)std::min<long long>(
+      1024, ((long long)kNumQueues * p.q_cap + kThreads - 1) / kThreads + 1);
+  hipLaunchKernelGGL(k_reset, dim3(reset_blocks), dim3(kThreads), 0, s, p);
+  HIP_OK(hipGetLastError());
+  if (d->dtype == MOE_BF16) {
+    hipLaunchKernelGGL(k_stage_route<bf16_t>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_stage_build<bf16_t>, dim3(1), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_stage_pos<bf16_t>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(k_stage_route<float>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_stage_build<float>, dim3(1), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_stage_pos<float>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+  }
+  HIP_OK(hipGetLastError());
+  rc = copy_routing(d, p, routing, s);
+  if (rc) return rc;
+  if (d->flags & MOE_FLAG_CHECK) return moe_last_device_error(d, workspace, stream);
+  return MOE_OK;
+}
+
+int moe_last_device_error(const moe_desc* d, const void* workspace, void* stream) {
+  if (validate(d) != MOE_OK || !workspace) return MOE_ERR_ARG;
+  Layout L;
+  make_layout(d, &L);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_OK(hipStreamSynchronize(s));
+  int err = 0;
+  const char* base = static_cast<const char*>(workspace) + L.off_ctrl;
+  HIP_OK(hipMemcpy(&err, base + sizeof(int) * CW_ERROR * kCtrlStride, sizeof(int),
+                   hipMemcpyDeviceToHost));
+  return err;
+}
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape (d, f and f_shared must be multiples of 128)";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_TIMEOUT: return "device watchdog timeout";
+    case MOE_ERR_CAPACITY: return "device table capacity exceeded";
+    case MOE_ERR_NONFINITE: return "non-finite router logit";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

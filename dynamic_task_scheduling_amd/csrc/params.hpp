@@ -1,0 +1,123 @@
+// params.hpp -- the launch-parameter block (host and device) and the task /
+// queue / control-word encodings of the persistent scheduler.
+#pragma once
+#include <stdint.h>
+
+namespace moe {
+
+// Task kinds.  A task id packs the kind in bits [30:27] and a payload below.
+enum TaskKind : int {
+  TK_ROUTE = 1,  // payload rt: router logits + top-k for tokens [32 rt, 32 rt + 32)
+  TK_POS = 2,    // payload rt: stable positions of those tokens' slots
+  TK_PERM = 3,   // payload mt * pch + c: gather rows chunk c of row-tile mt
+  TK_UP = 4,     // payload mt * n_up_n + n: gate/up GEMM + SiLU-gate epilogue
+  TK_DOWN = 5,   // payload (mt * n_down_n + n) * splitk + ks: DOWN GEMM + combine
+  TK_SUP = 6,    // payload (s * n_smt + m) * n_s_up_n + n: shared-expert UP
+  TK_SDOWN = 7,  // payload (s * n_smt + m) * n_down_n + n: shared-expert DOWN
+  TK_BUILD = 8,  // (trace only) the post-routing task builder
+};
+constexpr int kKindShift = 27;
+constexpr int kPayloadMask = (1 << kKindShift) - 1;
+__host__ __device__ inline int make_task(int kind, int payload) {
+  return (kind << kKindShift) | payload;
+}
+__host__ __device__ inline int task_kind(int id) { return id >> kKindShift; }
+__host__ __device__ inline int task_payload(int id) { return id & kPayloadMask; }
+
+// Ready queues.
+enum Queue : int { QA = 0, QM = 1, QC = 2, kNumQueues = 3 };
+
+// Control words; each sits on its own 128-byte line (index * kCtrlStride).
+enum CtrlWord : int {
+  CW_HEAD = 0,         // + queue
+  CW_TAIL = 3,         // + queue
+  CW_TOTAL = 6,        // + queue: tasks that will ever enter the queue
+  CW_ROUTE_DONE = 9,
+  CW_POS_DONE = 10,
+  CW_SPLIT_READY = 11, // 1 once the task builder has published its tables
+  CW_WMEM = 12,        // memory-bound worker count chosen by the cost model
+  CW_ROLE = 13,        // role tickets handed out after the routing phase
+  CW_TICKET = 14,      // worker tickets (dynamic worker ids)
+  CW_ERROR = 15,       // first device error code
+  CW_NMT = 16,         // expert row tiles
+  CW_NPERM = 17,       // permute tasks
+  CW_BAR_COUNT = 18,   // grid barrier (static mode)
+  CW_BAR_GEN = 19,
+  CW_TRACE = 20,       // trace cursor
+  CW_COUNT = 21
+};
+constexpr int kCtrlStride = 32;
+
+struct MTile {
+  int e;     // local expert
+  int row0;  // first row in the expert-contiguous buffers
+  int rows;  // valid rows (<= bm)
+  int bm;    // tile height class: 32, 64 or 128
+};
+
+struct Params {
+  // shape
+  int T, d, E, k, f, e_begin, E_loc, n_shared, fs;
+  int dtype;
+  // derived geometry
+  int n_rt;        // router / position tiles of 32 tokens
+  int hist_ld;     // row stride of hist / rt_base (n_rt rounded up to 4)
+  int n_up_n;      // f / 128
+  int n_down_n;    // d / 128
+  int splitk;      // DOWN split-K slices
+  int n_s_up_n;    // fs / 128
+  int n_smt;       // shared-expert row tiles of 128 tokens
+  int perm_rows;   // rows per permute task (divides 128)
+  int pch;         // permute chunks per row tile = 128 / perm_rows
+  int max_mt;      // capacity of the row-tile table
+  int max_perm;    // capacity of the permute list
+  int n_sup, n_sdown;
+  int q_cap;       // slots per queue
+  // scheduling
+  int workers;
+  int mode, split_policy, fixed_mem;
+  unsigned flags;
+  long long timeout_ticks;
+  float cm_mfma_rate;   // cost model: sustained MFMA flop/s per CU
+  float cm_cu_bw;       // cost model: bytes/s one CU moves in a gather
+  float cm_hbm_bw;      // cost model: device bytes/s
+  float cm_slack;       // cost model: permute must finish within slack * compute
+  // inputs
+  const void* x;
+  const void* wr;
+  const float* bias;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const void* sg;
+  const void* su;
+  const void* sd;
+  float* y;
+  // workspace
+  int* ctrl;
+  int* slots;      // [kNumQueues][q_cap]
+  float* logits;   // [T][E]
+  int* idx;        // [T][k]
+  float* w;        // [T][k]
+  int* hist;       // [E_loc][hist_ld]
+  int* rt_base;    // [E_loc][hist_ld]
+  int* counts;     // [E_loc]
+  int* offsets;    // [E_loc + 1]
+  int* eorder;     // [E_loc] local experts by descending count
+  int* perm;       // [T*k]
+  float* rw;       // [T*k]
+  int* slot_pos;   // [T*k]
+  MTile* mtiles;   // [max_mt]
+  int* cnt_perm;   // [max_mt]
+  int* cnt_down;   // [max_mt * splitk]
+  int* cnt_sdown;  // [n_shared * n_smt]
+  int* perm_list;  // [max_perm]
+  void* Xp;        // [T*k][d]
+  void* H;         // [T*k][f]
+  void* Hs;        // [n_shared][T][fs]
+  uint64_t* trace; // [trace_cap][4]
+  int trace_cap;
+  int route_from_logits;  // 1: logits are an input, y untouched
+};
+
+}  // namespace moe

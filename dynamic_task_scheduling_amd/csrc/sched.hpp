@@ -1,0 +1,483 @@
+// sched.hpp -- the persistent scheduler.
+//
+// Dynamic mode (the method).  Workgroups stay resident and loop: claim a
+// ready task by an atomic increment of a queue head (xxqk.cn/news/665650
+// s2.1, fetch_task), run it, publish its results with an agent-scope
+// release, and decrement the dependency counters of its consumers; the
+// producer that brings a counter to zero pushes the consumers into a ready
+// queue (same page s2.3; m.xxqk.cn/news/657744 s2.3: readiness follows the
+// data, no global barrier).  A worker leaves a queue only when its claimed
+// slot is past that queue's published task total, never when the queue
+// merely looks empty -- the early-exit bug m.xxqk.cn/news/657744 s3.3
+// describes.  After routing the builder sizes a memory-bound worker group
+// from the per-expert counts (spatial scheduler, Weave abstract); its
+// members drain the permute queue and then join the compute queue, while the
+// rest start on expert GEMMs as soon as rows land (temporal interleaving).
+//
+// Queues: QA (router tiles, shared-expert UP tiles, position tiles: all
+// workers), QM (permute tasks: the memory group), QC (expert UP/DOWN and
+// shared DOWN tasks: everyone once their own queue is drained).
+//
+// Static mode (the baseline the pages argue against): identical tasks,
+// pre-assigned round-robin from a worker ticket, a grid barrier between
+// stages (or, with MOE_FLAG_REF_SYNC, a spin on each task's own counter and a
+// fixed worker split).
+#pragma once
+#include "stages.hpp"
+
+namespace moe {
+
+constexpr int kClaimExhausted = -1;
+constexpr int kClaimAbort = -2;
+constexpr int kFlagTrace = 0x2;
+constexpr int kFlagPhaseSync = 0x4;
+constexpr int kFlagRefSync = 0x8;
+
+DEV int* cw(const Params& p, int word) { return p.ctrl + word * kCtrlStride; }
+
+DEV bool timed_out(const Params& p, uint64_t t0) {
+  return (long long)(rtc() - t0) > p.timeout_ticks;
+}
+
+// Thread 0: claim the next slot of queue q and wait until it is filled.
+DEV int claim(const Params& p, int q) {
+  const int h = add_relaxed(cw(p, CW_HEAD + q), 1);
+  const uint64_t t0 = rtc();
+  for (;;) {
+    const int total = ld_relaxed(cw(p, CW_TOTAL + q));
+    if (h >= total) return kClaimExhausted;
+    if (h < p.q_cap) {
+      const int v = ld_relaxed(p.slots + (size_t)q * p.q_cap + h);
+      if (v != 0) return v - 1;
+    }
+    if (ld_relaxed(cw(p, CW_ERROR)) != 0) return kClaimAbort;
+    if (timed_out(p, t0)) {
+      set_error(p, 5 /* MOE_ERR_TIMEOUT */);
+      return kClaimAbort;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Thread 0: spin until *c reaches zero (static mode's per-task dependency).
+DEV bool wait_zero(const Params& p, const int* c) {
+  const uint64_t t0 = rtc();
+  while (ld_relaxed(c) != 0) {
+    if (ld_relaxed(cw(p, CW_ERROR)) != 0) return false;
+    if (timed_out(p, t0)) {
+      set_error(p, 5);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// All threads: push n task ids (id_of(i)) into queue q.  Callers have run a
+// release fence in every thread, so the slot stores publish the data.
+template <typename F>
+DEV void push_burst(const Params& p, int q, int n, int* s_tmp, F&& id_of) {
+  if (n <= 0) return;
+  // Data this workgroup acquired from other producers (through the counter
+  // it just decremented) must be visible before the consumer is.
+  fence_release_agent();
+  if (threadIdx.x == 0) s_tmp[0] = add_relaxed(cw(p, CW_TAIL + q), n);
+  __syncthreads();
+  const int base = s_tmp[0];
+  __syncthreads();
+  if (base + n > p.q_cap) {
+    if (threadIdx.x == 0) set_error(p, 6 /* MOE_ERR_CAPACITY */);
+    return;
+  }
+  int* slots = p.slots + (size_t)q * p.q_cap + base;
+  for (int i = threadIdx.x; i < n; i += kThreads) st_relaxed(slots + i, id_of(i) + 1);
+}
+
+// All threads: the last of `target` arrivals on counter c returns true.
+DEV bool arrive_last(int* c, int delta, int last_old, int* s_tmp) {
+  fence_release_agent();
+  __syncthreads();
+  if (threadIdx.x == 0) s_tmp[0] = (add_acqrel(c, delta) == last_old);
+  __syncthreads();
+  const bool last = s_tmp[0] != 0;
+  __syncthreads();
+  if (last) fence_acquire_agent();
+  return last;
+}
+
+// Grid barrier over all workers (static mode).  Returns false on abort.
+DEV bool grid_barrier(const Params& p, int& gen, int* s_tmp) {
+  fence_release_agent();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    const int arrived = add_acqrel(cw(p, CW_BAR_COUNT), 1);
+    if (arrived == p.workers - 1) {
+      st_relaxed(cw(p, CW_BAR_COUNT), 0);
+      st_release(cw(p, CW_BAR_GEN), gen + 1);
+    } else {
+      const uint64_t t0 = rtc();
+      while (ld_relaxed(cw(p, CW_BAR_GEN)) == gen) {
+        if (ld_relaxed(cw(p, CW_ERROR)) != 0) { ok = 0; break; }
+        if (timed_out(p, t0)) { set_error(p, 5); ok = 0; break; }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    s_tmp[0] = ok;
+  }
+  __syncthreads();
+  const bool ok = s_tmp[0] != 0;
+  __syncthreads();
+  ++gen;
+  fence_acquire_agent();
+  return ok;
+}
+
+DEV void trace_record(const Params& p, int task, int worker, uint64_t t_req,
+                      uint64_t t_start, uint64_t t_end) {
+  if (!(p.flags & kFlagTrace) || p.trace == nullptr || threadIdx.x != 0) return;
+  const int i = add_relaxed(cw(p, CW_TRACE), 1);
+  if (i < p.trace_cap) {
+    uint64_t* r = p.trace + (size_t)i * 4;
+    r[0] = t_req;
+    r[1] = t_start;
+    r[2] = t_end;
+    r[3] = (uint64_t)(uint32_t)task | ((uint64_t)(worker & 0xffff) << 32) |
+           ((uint64_t)xcc_id() << 48);
+  }
+}
+
+template <typename Elem>
+struct Sched {
+  using S = Stages<Elem>;
+
+  // Publish the builder's results and release the work that follows it.
+  static DEV void publish_build(const Params& p, int* s_tmp) {
+    const int n_mt = ld_relaxed(cw(p, CW_NMT));
+    const int n_perm = ld_relaxed(cw(p, CW_NPERM));
+    const bool split = p.split_policy != 2;
+    const int n_comp = n_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sdown;
+    fence_release_agent();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      st_relaxed(cw(p, CW_TOTAL + QM), split ? n_perm : 0);
+      st_relaxed(cw(p, CW_TOTAL + QC), n_comp + (split ? 0 : n_perm));
+      st_release(cw(p, CW_SPLIT_READY), 1);
+    }
+    // position tiles go to QA
+    push_burst(p, QA, p.n_rt, s_tmp, [&](int i) { return make_task(TK_POS, i); });
+    // shared-expert DOWN tiles waited for the routing phase (zeroed y rows)
+    const int nsm = p.n_shared * p.n_smt;
+    for (int i = threadIdx.x; i < nsm; i += kThreads) {
+      if (add_acqrel(p.cnt_sdown + i, -1) == 1) {
+        int* sl = nullptr;
+        const int base = add_relaxed(cw(p, CW_TAIL + QC), p.n_down_n);
+        if (base + p.n_down_n <= p.q_cap) sl = p.slots + (size_t)QC * p.q_cap + base;
+        else set_error(p, 6);
+        if (sl) {
+          fence_release_agent();
+          for (int n = 0; n < p.n_down_n; ++n)
+            st_relaxed(sl + n, make_task(TK_SDOWN, i * p.n_down_n + n) + 1);
+        }
+      }
+    }
+  }
+
+  // Run one task; in dynamic mode also publish it and push what it enables.
+  // *t_body receives the clock at the end of the task body, before any
+  // publication, so a trace can check producer-end <= consumer-start.
+  static DEV void run(const Params& p, int task, char* smem, int* s_tmp, bool dyn,
+                      uint64_t* t_body) {
+    const int kind = task_kind(task);
+    const int pl = task_payload(task);
+    *t_body = 0;
+    switch (kind) {
+      case TK_ROUTE: {
+        S::route(p, pl, smem);
+        *t_body = rtc();
+        if (arrive_last(cw(p, CW_ROUTE_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
+          S::build(p, smem);
+          __syncthreads();
+          publish_build(p, s_tmp);
+        }
+        break;
+      }
+      case TK_POS: {
+        S::position(p, pl, smem);
+        *t_body = rtc();
+        if (arrive_last(cw(p, CW_POS_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
+          const int n_perm = ld_relaxed(cw(p, CW_NPERM));
+          const int q = (p.split_policy != 2) ? QM : QC;
+          push_burst(p, q, n_perm, s_tmp, [&](int i) { return p.perm_list[i]; });
+        }
+        break;
+      }
+      case TK_PERM: {
+        const int mt = pl / p.pch, c = pl % p.pch;
+        S::permute(p, mt, c);
+        *t_body = rtc();
+        if (arrive_last(p.cnt_perm + mt, -1, 1, s_tmp) && dyn)
+          push_burst(p, QC, p.n_up_n, s_tmp,
+                     [&](int n) { return make_task(TK_UP, mt * p.n_up_n + n); });
+        break;
+      }
+      case TK_UP: {
+        const int mt = pl / p.n_up_n, n = pl % p.n_up_n;
+        S::up(p, mt, n, smem);
+        *t_body = rtc();
+        const int ks = slice_of(n, p.n_up_n, p.splitk);
+        if (arrive_last(p.cnt_down + mt * p.splitk + ks, -1, 1, s_tmp) && dyn)
+          push_burst(p, QC, p.n_down_n, s_tmp, [&](int nn) {
+            return make_task(TK_DOWN, (mt * p.n_down_n + nn) * p.splitk + ks);
+          });
+        break;
+      }
+      case TK_DOWN: {
+        const int ks = pl % p.splitk;
+        const int r = pl / p.splitk;
+        S::down(p, r / p.n_down_n, r % p.n_down_n, ks, smem);
+        *t_body = rtc();
+        break;
+      }
+      case TK_SUP: {
+        const int n = pl % p.n_s_up_n;
+        const int sm = pl / p.n_s_up_n;          // s * n_smt + m
+        S::shared_up(p, sm / p.n_smt, sm % p.n_smt, n, smem);
+        *t_body = rtc();
+        if (arrive_last(p.cnt_sdown + sm, -1, 1, s_tmp) && dyn)
+          push_burst(p, QC, p.n_down_n, s_tmp,
+                     [&](int nn) { return make_task(TK_SDOWN, sm * p.n_down_n + nn); });
+        break;
+      }
+      case TK_SDOWN: {
+        const int n = pl % p.n_down_n;
+        const int sm = pl / p.n_down_n;
+        S::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem);
+        *t_body = rtc();
+        break;
+      }
+      default:
+        if (threadIdx.x == 0) set_error(p, 1);
+    }
+    __syncthreads();
+  }
+};
+
+// ------------------------------------------------------------- dynamic
+template <typename Elem>
+__global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
+  __shared__ int s_tmp[4];
+  __shared__ int s_worker;
+  if (threadIdx.x == 0) s_worker = add_relaxed(cw(p, CW_TICKET), 1);
+  int q = QA;
+  for (;;) {
+    uint64_t t_req = rtc();
+    if (threadIdx.x == 0) s_tmp[1] = claim(p, q);
+    __syncthreads();
+    const int v = s_tmp[1];
+    __syncthreads();
+    if (v == kClaimAbort) break;
+    if (v == kClaimExhausted) {
+      if (q == QA) {
+        // routing phase over: wait for the split, then take a role ticket
+        if (threadIdx.x == 0) {
+          const uint64_t t0 = rtc();
+          int nq = QC;
+          while (ld_relaxed(cw(p, CW_SPLIT_READY)) == 0) {
+            if (ld_relaxed(cw(p, CW_ERROR)) != 0 || timed_out(p, t0)) {
+              if (ld_relaxed(cw(p, CW_ERROR)) == 0) set_error(p, 5);
+              nq = -1;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          if (nq >= 0 && p.split_policy != 2) {
+            const int wm = ld_relaxed(cw(p, CW_WMEM));
+            nq = (add_relaxed(cw(p, CW_ROLE), 1) < wm) ? QM : QC;
+          }
+          s_tmp[2] = nq;
+        }
+        __syncthreads();
+        q = s_tmp[2];
+        __syncthreads();
+        if (q < 0) break;
+        continue;
+      }
+      if (q == QM) {
+        q = QC;
+        continue;
+      }
+      break;
+    }
+    fence_acquire_agent();
+    const uint64_t t_start = rtc();
+    uint64_t t_body;
+    Sched<Elem>::run(p, v, smem, s_tmp, true, &t_body);
+    trace_record(p, v, s_worker, t_req, t_start, t_body);
+  }
+}
+
+// -------------------------------------------------------------- static
+template <typename Elem>
+__global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
+  __shared__ int s_tmp[4];
+  if (threadIdx.x == 0) s_tmp[3] = add_relaxed(cw(p, CW_TICKET), 1);
+  __syncthreads();
+  const int w = s_tmp[3];
+  const int W = p.workers;
+  int gen = 0;
+  using SC = Sched<Elem>;
+  auto exec = [&](int task) __attribute__((always_inline)) {
+    const uint64_t t0 = rtc();
+    uint64_t t_body;
+    SC::run(p, task, smem, s_tmp, false, &t_body);
+    trace_record(p, task, w, t0, t0, t_body);
+  };
+  // stage 1: router tiles and shared-expert UP tiles
+  const int nA = p.n_rt + p.n_sup;
+  for (int i = w; i < nA; i += W)
+    exec(i < p.n_rt ? make_task(TK_ROUTE, i) : make_task(TK_SUP, i - p.n_rt));
+  if (!grid_barrier(p, gen, s_tmp)) return;
+  if (w == 0) {
+    Stages<Elem>::build(p, smem);
+    __syncthreads();
+    // the routing stage (which zeroes y) is over: release the shared DOWN tiles
+    for (int i = threadIdx.x; i < p.n_shared * p.n_smt; i += kThreads)
+      add_relaxed(p.cnt_sdown + i, -1);
+  }
+  if (!grid_barrier(p, gen, s_tmp)) return;
+  for (int i = w; i < p.n_rt; i += W) exec(make_task(TK_POS, i));
+  if (!grid_barrier(p, gen, s_tmp)) return;
+  const int n_mt = ld_relaxed(cw(p, CW_NMT));
+  const int n_perm = ld_relaxed(cw(p, CW_NPERM));
+  const int n_up = n_mt * p.n_up_n;
+  const int n_down = n_mt * p.n_down_n * p.splitk;
+  if (!(p.flags & kFlagRefSync) || W < 2) {
+    for (int i = w; i < n_perm; i += W) exec(p.perm_list[i]);
+    if (!grid_barrier(p, gen, s_tmp)) return;
+    for (int i = w; i < n_up; i += W) exec(make_task(TK_UP, i));
+    if (!grid_barrier(p, gen, s_tmp)) return;
+    for (int i = w; i < n_down + p.n_sdown; i += W)
+      exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
+    return;
+  }
+  // fixed split, per-task counter waits, no barriers
+  const int wm = max(1, p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8);
+  if (w < wm) {
+    for (int i = w; i < n_perm; i += wm) exec(p.perm_list[i]);
+  } else {
+    for (int i = w - wm; i < n_up; i += W - wm) {
+      if (threadIdx.x == 0) s_tmp[1] = wait_zero(p, p.cnt_perm + i / p.n_up_n);
+      __syncthreads();
+      const bool ok = s_tmp[1];
+      __syncthreads();
+      if (!ok) return;
+      fence_acquire_agent();
+      exec(make_task(TK_UP, i));
+    }
+  }
+  for (int i = w; i < n_down + p.n_sdown; i += W) {
+    const int* c;
+    if (i < n_down) {
+      const int ks = i % p.splitk, mt = i / p.splitk / p.n_down_n;
+      c = p.cnt_down + mt * p.splitk + ks;
+    } else {
+      c = p.cnt_sdown + (i - n_down) / p.n_down_n;
+    }
+    if (threadIdx.x == 0) s_tmp[1] = wait_zero(p, c);
+    __syncthreads();
+    const bool ok = s_tmp[1];
+    __syncthreads();
+    if (!ok) return;
+    fence_acquire_agent();
+    exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
+  }
+}
+
+// ----------------------------------------------- one launch per stage
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void k_stage_route(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Tile<Elem, 32, 1>::LDS_BYTES + 32 * kMaxE * 4 + kMaxE * 4];
+  if (p.route_from_logits) Stages<Elem>::topk_from_logits(p, blockIdx.x, smem);
+  else Stages<Elem>::route(p, blockIdx.x, smem);
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void k_stage_build(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[16384];
+  Stages<Elem>::build(p, smem);
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void k_stage_pos(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[kTB * kMaxK * 8];
+  Stages<Elem>::position(p, blockIdx.x, smem);
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void k_stage_perm(Params p) {
+  const int n_perm = ld_relaxed(cw(p, CW_NPERM));
+  if ((int)blockIdx.x >= n_perm) return;
+  const int pl = task_payload(p.perm_list[blockIdx.x]);
+  Stages<Elem>::permute(p, pl / p.pch, pl % p.pch);
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads, 1) void k_stage_up(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
+  const int b = blockIdx.x;
+  const int routed = p.max_mt * p.n_up_n;
+  if (b < routed) {
+    const int n_mt = ld_relaxed(cw(p, CW_NMT));
+    if (b >= n_mt * p.n_up_n) return;
+    Stages<Elem>::up(p, b / p.n_up_n, b % p.n_up_n, smem);
+  } else {
+    const int pl = b - routed;
+    const int n = pl % p.n_s_up_n, sm = pl / p.n_s_up_n;
+    Stages<Elem>::shared_up(p, sm / p.n_smt, sm % p.n_smt, n, smem);
+  }
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads, 1) void k_stage_down(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Tile<Elem, 128, 1>::LDS_BYTES];
+  const int b = blockIdx.x;
+  const int routed = p.max_mt * p.n_down_n * p.splitk;
+  if (b < routed) {
+    const int n_mt = ld_relaxed(cw(p, CW_NMT));
+    if (b >= n_mt * p.n_down_n * p.splitk) return;
+    const int ks = b % p.splitk, r = b / p.splitk;
+    Stages<Elem>::down(p, r / p.n_down_n, r % p.n_down_n, ks, smem);
+  } else {
+    const int pl = b - routed;
+    const int n = pl % p.n_down_n, sm = pl / p.n_down_n;
+    Stages<Elem>::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem);
+  }
+}
+
+// Control block reset + queue seeding, launched before every call.
+__global__ __launch_bounds__(kThreads) void k_reset(Params p) {
+  const int gid = blockIdx.x * kThreads + threadIdx.x;
+  const int stride = gridDim.x * kThreads;
+  const int ncw = CW_COUNT * kCtrlStride;
+  for (int i = gid; i < ncw; i += stride) p.ctrl[i] = 0;
+  const size_t ns = (size_t)kNumQueues * p.q_cap;
+  for (size_t i = gid; i < ns; i += stride) {
+    int v = 0;
+    if (i < (size_t)p.n_rt) v = make_task(TK_ROUTE, (int)i) + 1;
+    else if (i < (size_t)(p.n_rt + p.n_sup)) v = make_task(TK_SUP, (int)i - p.n_rt) + 1;
+    p.slots[i] = v;
+  }
+  const int nsm = p.n_shared * p.n_smt;
+  for (int i = gid; i < nsm; i += stride) p.cnt_sdown[i] = p.n_s_up_n + 1;
+  if (gid == 0) {
+    p.ctrl[(CW_TAIL + QA) * kCtrlStride] = p.n_rt + p.n_sup;
+    p.ctrl[(CW_TOTAL + QA) * kCtrlStride] = 2 * p.n_rt + p.n_sup;
+    p.ctrl[(CW_TOTAL + QM) * kCtrlStride] = 0x7fffffff;
+    p.ctrl[(CW_TOTAL + QC) * kCtrlStride] = 0x7fffffff;
+  }
+}
+
+}  // namespace moe

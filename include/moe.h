@@ -1,0 +1,198 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts megakernel library.
+ *
+ * One call runs a whole MoE layer on one GPU:
+ *   router GEMM -> softmax top-k -> stable count/scan/permute into
+ *   expert-contiguous rows -> per-expert SwiGLU GEMM tasks (bf16 MFMA,
+ *   fused SiLU-gate epilogue) -> weighted scatter-add combine.
+ *
+ * The stages are those the Weave pages place inside one persistent MoE
+ * kernel (xxqk.cn/news/665650 section 1; m.xxqk.cn/news/657744 section 2.1).
+ * The default mode runs them as ONE persistent kernel whose workgroups claim
+ * ready tasks from atomic queues (xxqk.cn/news/665650 section 2.1, the
+ * TaskQueue / fetch_task scheme), with per-task dependency counters instead
+ * of global barriers (same page, section 2.3; m.xxqk.cn/news/657744 section
+ * 2.3), and a post-routing cost model that splits the workers into a
+ * memory-bound group (permute = the local stand-in for expert-parallel
+ * dispatch) and an MFMA-bound group (expert GEMMs), per the spatial and
+ * temporal schedulers of the Weave abstract (arxivdaily.com/papers/2609.21483).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *    The library allocates nothing and keeps no per-call state: everything
+ *    it needs lives in the caller's workspace (sized by moe_workspace_size),
+ *    so a call can be captured in a HIP graph.
+ *  - Calls are asynchronous on `hip_stream` (a hipStream_t, NULL = default
+ *    stream).  Argument errors are returned synchronously before anything is
+ *    launched.  Errors found on the device (watchdog timeout, non-finite
+ *    logit) are written to the workspace; read them with
+ *    moe_last_device_error after synchronising, or set MOE_FLAG_CHECK to
+ *    have moe_layer synchronise and return them.
+ *  - A workspace may be used by one call at a time.
+ */
+#ifndef DTS_MOE_H
+#define DTS_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of x, the expert weights, the router weights and the
+ * intermediate buffers.  Accumulation is always fp32; y is always fp32. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Scheduling mode.  Every mode runs the same device tile code and gives the
+ * same routing bit for bit; y differs only by fp32 summation order.
+ *  MOE_DYNAMIC           one persistent kernel, dependency-driven ready
+ *                        queues, count-sized worker split (the method).
+ *  MOE_STATIC_PARTITION  one persistent kernel, tasks pre-assigned to
+ *                        workers round-robin, fixed worker split, a grid
+ *                        barrier between stages (the static fused kernel the
+ *                        pages compare against, xxqk.cn/news/665650 s3.2).
+ *  MOE_MULTI_KERNEL      one ordinary launch per stage on the stream; each
+ *                        launch boundary is the only synchronisation
+ *                        (xxqk.cn/news/665650 section 1.2). */
+typedef enum {
+  MOE_DYNAMIC = 0,
+  MOE_STATIC_PARTITION = 1,
+  MOE_MULTI_KERNEL = 2
+} moe_mode;
+
+/* How the persistent kernel sizes the memory-bound worker group.
+ *  MOE_SPLIT_COST_MODEL  from the per-expert counts, after routing.
+ *  MOE_SPLIT_FIXED       desc.fixed_mem_workers (default: workers / 8).
+ *  MOE_SPLIT_NONE        one ready queue shared by every worker. */
+typedef enum {
+  MOE_SPLIT_COST_MODEL = 0,
+  MOE_SPLIT_FIXED = 1,
+  MOE_SPLIT_NONE = 2
+} moe_split_policy;
+
+/* Flags. */
+#define MOE_FLAG_CHECK 0x1u      /* synchronise and return device errors   */
+#define MOE_FLAG_TRACE 0x2u      /* record per-task timestamps in desc.trace */
+#define MOE_FLAG_PHASE_SYNC 0x4u /* static mode: barriers between stages (default on) */
+#define MOE_FLAG_REF_SYNC 0x8u   /* static mode: per-task counter waits instead of barriers */
+
+/* Return codes. */
+#define MOE_OK 0
+#define MOE_ERR_ARG 1         /* NULL pointer, bad shape, k > E, E > 256    */
+#define MOE_ERR_WORKSPACE 2   /* workspace NULL or smaller than required    */
+#define MOE_ERR_UNSUPPORTED 3 /* d or f not a multiple of 128, etc.         */
+#define MOE_ERR_HIP 4         /* a HIP runtime call failed                  */
+#define MOE_ERR_TIMEOUT 5     /* device watchdog: a wait exceeded its limit */
+#define MOE_ERR_CAPACITY 6    /* a device table overflowed its capacity     */
+#define MOE_ERR_NONFINITE 7   /* a router logit was NaN or infinite         */
+
+typedef struct moe_desc {
+  int T;              /* tokens (>= 0)                                      */
+  int d;              /* model dim, multiple of 128                         */
+  int E;              /* router width = global experts, 1..256              */
+  int k;              /* experts per token, 1..min(E, 8)                    */
+  int f;              /* expert FFN dim, multiple of 128                    */
+  int e_begin, e_end; /* local experts [e_begin, e_end); e_end=0 -> E       */
+  int n_shared;       /* always-on shared experts (weight 1), 0..4          */
+  int f_shared;       /* their FFN dim, multiple of 128                     */
+  int dtype;          /* moe_dtype                                          */
+  int mode;           /* moe_mode                                           */
+  int split_policy;   /* moe_split_policy                                   */
+  int fixed_mem_workers; /* for MOE_SPLIT_FIXED; 0 = workers / 8            */
+  int split_k;        /* DOWN split-K slices; 0 = automatic                 */
+  int max_workers;    /* cap on persistent workgroups; 0 = all resident     */
+  unsigned flags;     /* MOE_FLAG_*                                         */
+  uint64_t* trace;    /* device buffer for MOE_FLAG_TRACE, or NULL          */
+  int trace_cap;      /* records that fit in trace (3 x uint64 each)        */
+  int timeout_ms;     /* device watchdog per wait; 0 = 2000 ms              */
+} moe_desc;
+
+/* Weights.  E_loc = e_end - e_begin.  Element type = desc.dtype.
+ *   w_router [d, E]         (router_bias [E] fp32, may be NULL)
+ *   w_gate   [E_loc, d, f]  SiLU branch;   w_up [E_loc, d, f]  linear branch
+ *   w_down   [E_loc, f, d]
+ *   ws_gate, ws_up [n_shared, d, f_shared], ws_down [n_shared, f_shared, d]
+ *   (NULL when n_shared == 0). */
+typedef struct moe_weights {
+  const void* w_router;
+  const float* router_bias;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* ws_gate;
+  const void* ws_up;
+  const void* ws_down;
+} moe_weights;
+
+/* Routing results, for checking (every pointer may be NULL = not wanted).
+ *   logits        [T, E]      fp32 router logits (bias included)
+ *   topk_idx      [T, k]      chosen global expert ids, best first; equal
+ *                             logits break toward the lower id
+ *   topk_w        [T, k]      fp32 weights, softmax renormalised over the k
+ *   expert_counts [E_loc]     kept rows per local expert
+ *   offsets       [E_loc+1]   exclusive prefix of expert_counts
+ *   perm          [T*k]       token of each kept row, rows grouped by
+ *                             expert, tokens ascending inside an expert
+ *                             (first offsets[E_loc] entries valid)
+ *   slot_pos      [T, k]      row of each (token, slot), -1 if not local */
+typedef struct moe_routing {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* expert_counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* slot_pos;
+} moe_routing;
+
+/* Information about how a descriptor will run (filled by moe_query). */
+typedef struct moe_info {
+  int workers;          /* persistent workgroups launched                  */
+  int cus;              /* compute units on the device                     */
+  int blocks_per_cu;    /* resident workgroups per CU for the megakernel   */
+  int route_tiles;      /* router / position tiles (32 tokens each)        */
+  int up_ntiles;        /* f / 128                                         */
+  int down_ntiles;      /* d / 128                                         */
+  int split_k;          /* DOWN split-K actually used                      */
+  int permute_rows;     /* rows per permute task                           */
+  int max_mtiles;       /* capacity of the expert row-tile table           */
+  int max_tasks;        /* capacity of the ready queues                    */
+  size_t workspace_bytes;
+} moe_info;
+
+/* Bytes of workspace a call with this descriptor needs (0 on bad desc). */
+size_t moe_workspace_size(const moe_desc* desc);
+
+/* Fill `info` for this descriptor on the current device. */
+int moe_query(const moe_desc* desc, moe_info* info);
+
+/* Run one MoE layer: y[T,d] (fp32, overwritten) = sum over each token's kept
+ * top-k experts of w * SwiGLU_e(x[t]) + sum of the shared experts.
+ * `routing` may be NULL; otherwise the requested routing tables are written.
+ * The workspace must be at least moe_workspace_size(desc) bytes. */
+int moe_layer(const moe_desc* desc, const void* x, const moe_weights* weights,
+              float* y, const moe_routing* routing, void* workspace,
+              size_t workspace_bytes, void* hip_stream);
+
+/* Routing only, from caller-supplied fp32 logits [T, E]: top-k, weights,
+ * counts, offsets, perm and slot_pos, with the same device code the layer
+ * uses.  Lets a checker feed identical logits to this library and to a
+ * reference and compare the tables bit for bit. */
+int moe_route_from_logits(const moe_desc* desc, const float* logits,
+                          const moe_routing* routing, void* workspace,
+                          size_t workspace_bytes, void* hip_stream);
+
+/* Synchronise `hip_stream` and return the device error word of the last
+ * call that used `workspace` (MOE_OK if none). */
+int moe_last_device_error(const moe_desc* desc, const void* workspace,
+                          void* hip_stream);
+
+/* Human-readable text for a return code. */
+const char* moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DTS_MOE_H */

@@ -1,0 +1,71 @@
+"""Trace checks shared by GPU tests: every task ran exactly once, and every
+task started after all of its producers' bodies ended."""
+from collections import defaultdict
+
+import numpy as np
+
+from dynamic_task_scheduling_amd.analysis import decode_trace
+
+ROUTE, POS, PERM, UP, DOWN, SUP, SDOWN = 1, 2, 3, 4, 5, 6, 7
+
+
+def check_trace(raw, layer, routing):
+    tr = decode_trace(raw)
+    info = layer.info
+    s = layer.shape
+    n_rt = info["route_tiles"]
+    n_up = info["up_ntiles"]
+    n_down = info["down_ntiles"]
+    sk = info["split_k"]
+    pch = 128 // info["permute_rows"]
+    counts = routing.expert_counts.cpu().numpy()
+    n_mt = int(sum((c + 127) // 128 for c in counts))
+    ids, cnt = np.unique(tr["task"], return_counts=True)
+    assert np.all(cnt == 1), "a task ran more than once"
+    kinds = tr["kind"]
+    pl = tr["payload"]
+    n_smt = (s.T + 127) // 128
+    n_sup_n = (s.f_shared // 128) if s.n_shared else 0
+    expect = {ROUTE: n_rt, POS: n_rt, UP: n_mt * n_up, DOWN: n_mt * n_down * sk,
+              SUP: s.n_shared * n_smt * n_sup_n, SDOWN: s.n_shared * n_smt * n_down}
+    for k, n in expect.items():
+        assert int((kinds == k).sum()) == n, "kind %d ran %d times, expected %d" % (
+            k, int((kinds == k).sum()), n)
+    start = {int(t): int(v) for t, v in zip(tr["task"], tr["t_start"])}
+    end = {int(t): int(v) for t, v in zip(tr["task"], tr["t_end"])}
+    route_end = max(end[(ROUTE << 27) | i] for i in range(n_rt))
+    pos_end = max(end[(POS << 27) | i] for i in range(n_rt))
+    perm_end = defaultdict(int)
+    for t, k, p in zip(tr["task"], kinds, pl):
+        if k == PERM:
+            perm_end[int(p) // pch] = max(perm_end[int(p) // pch], end[int(t)])
+    up_end = defaultdict(int)   # (mt, ks) -> latest end
+    bounds = [ks * n_up // sk for ks in range(sk + 1)]
+    def slice_of(n):
+        ks = 0
+        while ks + 1 < sk and bounds[ks + 1] <= n:
+            ks += 1
+        return ks
+    sup_end = defaultdict(int)
+    for t, k, p in zip(tr["task"], kinds, pl):
+        t, p = int(t), int(p)
+        if k == UP:
+            up_end[(p // n_up, slice_of(p % n_up))] = max(up_end[(p // n_up, slice_of(p % n_up))], end[t])
+        if k == SUP:
+            sup_end[p // n_sup_n] = max(sup_end[p // n_sup_n], end[t])
+    for t, k, p in zip(tr["task"], kinds, pl):
+        t, p = int(t), int(p)
+        st = start[t]
+        if k == POS:
+            assert st >= route_end
+        elif k == PERM:
+            assert st >= pos_end
+        elif k == UP:
+            assert st >= perm_end[p // n_up]
+        elif k == DOWN:
+            ks = p % sk
+            mt = p // sk // n_down
+            assert st >= up_end[(mt, ks)], "DOWN before its UP slice"
+        elif k == SDOWN:
+            assert st >= sup_end[p // n_down] and st >= route_end
+    return tr

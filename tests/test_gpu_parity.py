@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Routing (top-k ids, counts, offsets, permutation, slot rows) must match bit
+for bit given the same fp32 logits; y within the stated tolerances.  Every
+scheduling mode runs the same tiles, so every mode is checked.
+"""
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import oracle
+from dynamic_task_scheduling_amd.configs import LayerShape, workload
+from dynamic_task_scheduling_amd.moe import MoELayer, route_from_logits
+from gpu_util import check_routing, gen_inputs, host_inputs, run_and_check
+
+MODES = [("dynamic", "cost_model"), ("dynamic", "none"), ("dynamic", "fixed"),
+         ("static", "fixed"), ("multi_kernel", "none")]
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = workload(1)
+    s = wl.layers[0]
+    g = gen_inputs(s, wl.name, 0)
+    return s, g, host_inputs(g)
+
+
+@pytest.mark.parametrize("mode,split", MODES)
+def test_tiny_fp32_all_modes(tiny, mode, split):
+    s, g, n = tiny
+    run_and_check(s, g, n, mode, split, label="tiny_fp32")
+
+
+MID = LayerShape(T=300, d=512, E=16, k=4, f=384, n_shared=1, f_shared=256, zipf_s=1.0)
+MID_LOCAL = LayerShape(T=211, d=256, E=32, k=6, f=256, e_begin=8, e_end=24, zipf_s=1.5)
+
+
+@pytest.fixture(scope="module")
+def mid():
+    g = gen_inputs(MID, "mid", 1)
+    return g, host_inputs(g)
+
+
+@pytest.mark.parametrize("mode,split", MODES)
+def test_mid_bf16_all_modes(mid, mode, split):
+    g, n = mid
+    run_and_check(MID, g, n, mode, split, label="mid_bf16")
+
+
+@pytest.mark.parametrize("mode,split", [("dynamic", "cost_model"), ("static", "fixed"),
+                                        ("multi_kernel", "none")])
+def test_local_expert_range(mode, split):
+    g = gen_inputs(MID_LOCAL, "mid_local", 2)
+    _, r, ro = run_and_check(MID_LOCAL, g, None, mode, split, label="mid_local")
+    assert (ro["slot_pos"] < 0).any()
+
+
+def test_split_k_uneven():
+    s = LayerShape(T=96, d=256, E=4, k=2, f=1024, zipf_s=0.5)
+    g = gen_inputs(s, "splitk", 3)
+    for sk in (3, 8):
+        run_and_check(s, g, None, "dynamic", "cost_model", split_k=sk, label="splitk%d" % sk)
+
+
+@pytest.mark.parametrize("T", [1, 33, 129])
+def test_ragged_and_tiny_T(T):
+    s = LayerShape(T=T, d=256, E=8, k=3, f=256, zipf_s=1.2)
+    g = gen_inputs(s, "ragged", T)
+    for mode, split in (("dynamic", "cost_model"), ("static", "fixed")):
+        run_and_check(s, g, None, mode, split, label="T%d" % T)
+
+
+def test_single_expert_k1():
+    s = LayerShape(T=70, d=128, E=1, k=1, f=128)
+    g = gen_inputs(s, "e1", 4)
+    _, r, _ = run_and_check(s, g, None, "dynamic", "cost_model", label="E1k1")
+    assert torch.all(r.topk_w == 1.0)
+
+
+def test_all_tokens_one_expert():
+    """A dominant bias sends every token to expert 5 first: one hot expert
+    with many row tiles and several empty experts."""
+    s = LayerShape(T=700, d=256, E=16, k=2, f=256)
+    g = gen_inputs(s, "hot", 5)
+    b = torch.zeros(16, dtype=torch.float32, device="cuda")
+    b[5] = 50.0
+    g["router_bias"] = b
+    _, r, ro = run_and_check(s, g, None, "dynamic", "cost_model", label="hot_expert")
+    assert int(ro["counts"][5]) == 700
+
+
+def test_few_workers():
+    """Correct with 1, 2 and 3 persistent workers (no co-residency needed)."""
+    g = gen_inputs(MID, "mid", 1)
+    n = host_inputs(g)
+    for w in (1, 2, 3):
+        run_and_check(MID, g, n, "dynamic", "cost_model", max_workers=w, label="W%d" % w)
+
+
+def test_route_from_logits_ties():
+    """Identical logits in, identical tables out: random, heavy ties, signed
+    zeros, and the 256-wide router."""
+    rng = np.random.default_rng(0)
+    cases = []
+    for E, k in ((8, 2), (64, 6), (256, 8), (128, 8)):
+        T = 257
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        cases.append((E, k, lg))
+        lt = np.round(rng.standard_normal((T, E)) * 2).astype(np.float32)   # many ties
+        lt[:, ::3] = 0.0
+        lt[:, 1::7] = -0.0
+        cases.append((E, k, lt))
+    cases.append((16, 4, np.zeros((40, 16), np.float32)))
+    for E, k, lg in cases:
+        s = LayerShape(T=lg.shape[0], d=128, E=E, k=k, f=128)
+        r = route_from_logits(s, torch.from_numpy(lg).cuda())
+        torch.cuda.synchronize()
+        ro = oracle.route(lg, k)
+        check_routing(r, ro, s)
+    # local range
+    lg = rng.standard_normal((100, 32)).astype(np.float32)
+    s = LayerShape(T=100, d=128, E=32, k=4, f=128, e_begin=4, e_end=20)
+    r = route_from_logits(s, torch.from_numpy(lg).cuda())
+    torch.cuda.synchronize()
+    check_routing(r, oracle.route(lg, 4, 4, 20), s)
+
+
+def test_cross_mode_agreement(mid):
+    g, n = mid
+    ys = {}
+    routes = {}
+    for mode, split in MODES:
+        layer = MoELayer(MID, g, mode=mode, split=split, timeout_ms=3000)
+        y, r = layer(g["x"], return_routing=True, check_errors=True)
+        ys[(mode, split)] = y.clone()
+        routes[(mode, split)] = r
+    torch.cuda.synchronize()
+    ref = ys[MODES[0]]
+    for key in MODES[1:]:
+        for f in ("topk_idx", "expert_counts", "offsets", "slot_pos"):
+            assert torch.equal(getattr(routes[key], f), getattr(routes[MODES[0]], f))
+        d = (ys[key] - ref).abs().max().item()
+        assert d <= 1e-5 * ref.abs().max().item(), "%s differs by %g" % (key, d)
+
+
+def test_repeat_and_poisoned_workspace(mid):
+    """Repeated calls on one workspace, and a workspace filled with NaN-like
+    bytes before a call, give the same result (no read before write)."""
+    g, n = mid
+    layer = MoELayer(MID, g, mode="dynamic", timeout_ms=3000)
+    y0 = layer(g["x"], check_errors=True).clone()
+    for _ in range(3):
+        y1 = layer(g["x"], check_errors=True)
+        assert (y1 - y0).abs().max().item() <= 1e-5 * y0.abs().max().item()
+    layer.workspace.fill_(0xFF)
+    y2 = layer(g["x"], check_errors=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y2).all()
+    assert (y2 - y0).abs().max().item() <= 1e-5 * y0.abs().max().item()
+
+
+def test_trace_happens_before(mid):
+    """Every task runs exactly once and starts after its producers ended."""
+    from analysis_util import check_trace
+    g, n = mid
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(MID, g, mode="dynamic", trace=trace, timeout_ms=3000)
+    y, r = layer(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+
+
+# ------------------------------------------------------------ full sizes
+def _full(cfg, sample, modes=(("dynamic", "cost_model"),), layers=(0,)):
+    wl = workload(cfg)
+    for li in layers:
+        s = wl.layers[li]
+        from dynamic_task_scheduling_amd.synth import make_layer
+        t = make_layer(s, wl.name, li, 0, "cuda")
+        n = host_inputs(t)
+        for mode, split in modes:
+            run_and_check(s, t, n, mode, split, sample=sample, label="%s[%d]" % (wl.name, li))
+        del t
+        torch.cuda.empty_cache()
+
+
+def test_full_decode():
+    _full(2, 12, modes=(("dynamic", "cost_model"), ("static", "fixed"), ("multi_kernel", "none")))
+
+
+def test_full_prefill():
+    _full(3, 12, modes=(("dynamic", "cost_model"), ("static", "fixed"), ("multi_kernel", "none")))
+
+
+def test_full_ep_share():
+    _full(4, 8)
+
+
+def test_full_stress_layers():
+    _full(5, 8, layers=(0, 1, 15))
