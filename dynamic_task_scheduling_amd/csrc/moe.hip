@@ -23,7 +23,7 @@ struct Layout {
   Params p;          // geometry only (pointers filled by carve)
   int esz;
   size_t off_ctrl, off_slots, off_logits, off_idx, off_w, off_hist, off_rtb, off_counts,
-      off_offsets, off_eorder, off_perm, off_rw, off_slotpos, off_mtiles, off_cnt_perm,
+      off_offsets, off_eorder, off_route_part, off_cnt_route, off_perm, off_rw, off_slotpos, off_mtiles, off_cnt_perm,
       off_cnt_down, off_cnt_sdown, off_perm_list, off_xp, off_h, off_hs, total;
 };
 
@@ -66,6 +66,15 @@ void make_layout(const moe_desc* d, Layout* L) {
   L->esz = d->dtype == MOE_BF16 ? 2 : 4;
   p.n_rt = (d->T + kTB - 1) / kTB;
   p.hist_ld = std::max(4, (p.n_rt + 3) / 4 * 4);
+  // router K slices: enough router tasks to occupy the device (~256), each
+  // slice at least 512 deep, slices a divisor of d/64
+  {
+    const int ksteps = d->d / 64;
+    const int want = std::max(1, (256 + std::max(p.n_rt, 1) - 1) / std::max(p.n_rt, 1));
+    p.rsk = 1;
+    for (int sl = 1; sl <= ksteps; ++sl)
+      if (ksteps % sl == 0 && sl <= want && d->d / sl >= 512) p.rsk = sl;
+  }
   p.n_up_n = d->f / kBN;
   p.n_down_n = d->d / kBN;
   int sk = d->split_k;
@@ -83,9 +92,9 @@ void make_layout(const moe_desc* d, Layout* L) {
   p.max_perm = (int)((R + pr - 1) / pr + p.max_mt);
   p.n_sup = p.n_shared * p.n_smt * p.n_s_up_n;
   p.n_sdown = p.n_shared * p.n_smt * p.n_down_n;
-  const long long qa = 2ll * p.n_rt + p.n_sup;
-  const long long qc = (long long)p.max_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sdown +
-                       p.max_perm;
+  const long long qa = (long long)p.n_rt * (p.rsk + 1);
+  const long long qc = (long long)p.max_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup +
+                       p.n_sdown + p.max_perm;
   p.q_cap = (int)(std::max(qa, qc) + kMaxWorkersBound);
 
   size_t o = 0;
@@ -98,6 +107,8 @@ void make_layout(const moe_desc* d, Layout* L) {
   L->off_ctrl = take(sizeof(int) * CW_COUNT * kCtrlStride);
   L->off_slots = take(sizeof(int) * (size_t)kNumQueues * p.q_cap);
   L->off_logits = take(sizeof(float) * (size_t)d->T * d->E);
+  L->off_route_part = take(p.rsk > 1 ? sizeof(float) * (size_t)p.rsk * d->T * d->E : 0);
+  L->off_cnt_route = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
   L->off_idx = take(sizeof(int) * Tk);
   L->off_w = take(sizeof(float) * Tk);
   L->off_hist = take(sizeof(int) * (size_t)p.E_loc * p.hist_ld);
@@ -125,6 +136,8 @@ void carve(Layout* L, void* ws) {
   p.ctrl = reinterpret_cast<int*>(b + L->off_ctrl);
   p.slots = reinterpret_cast<int*>(b + L->off_slots);
   p.logits = reinterpret_cast<float*>(b + L->off_logits);
+  p.route_part = reinterpret_cast<float*>(b + L->off_route_part);
+  p.cnt_route = reinterpret_cast<int*>(b + L->off_cnt_route);
   p.idx = reinterpret_cast<int*>(b + L->off_idx);
   p.w = reinterpret_cast<float*>(b + L->off_w);
   p.hist = reinterpret_cast<int*>(b + L->off_hist);
@@ -208,7 +221,7 @@ int launch_layer(const moe_desc* d, Params& p, hipStream_t s) {
   } else if (d->mode == MOE_STATIC_PARTITION) {
     hipLaunchKernelGGL(k_static<Elem>, dim3(p.workers), dim3(kThreads), 0, s, p);
   } else {
-    hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt * p.rsk), dim3(kThreads), 0, s, p);
     HIP_OK(hipGetLastError());
     hipLaunchKernelGGL(k_stage_build<Elem>, dim3(1), dim3(kThreads), 0, s, p);
     HIP_OK(hipGetLastError());
@@ -258,10 +271,11 @@ int fill_params(const moe_desc* d, Layout* L, void* ws, size_t ws_bytes) {
   if (!(p.flags & MOE_FLAG_REF_SYNC)) p.flags |= MOE_FLAG_PHASE_SYNC;
   const long long ms = d->timeout_ms > 0 ? d->timeout_ms : 2000;
   p.timeout_ticks = ms * 100000ll;  // 100 MHz constant clock
-  // cost model constants: per-CU bf16 MFMA rate at ~50% of peak, per-CU
-  // gather bandwidth, and device HBM bandwidth (measured on MI355X)
+  // cost model constants (measured on MI355X): sustained per-CU bf16 MFMA
+  // rate in expert tiles, the bytes/s one worker moves in a gather task, and
+  // the device HBM bandwidth a streaming tile sustains
   p.cm_mfma_rate = (d->dtype == MOE_BF16 ? 4.9e12f : 0.3e12f);
-  p.cm_cu_bw = 60e9f;
+  p.cm_cu_bw = 16e9f;
   p.cm_hbm_bw = 6.0e12f;
   p.cm_slack = 0.5f;
   p.trace = (d->flags & MOE_FLAG_TRACE) ? d->trace : nullptr;
@@ -296,6 +310,7 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->permute_rows = L.p.perm_rows;
   info->max_mtiles = L.p.max_mt;
   info->max_tasks = L.p.q_cap;
+  info->route_splits = L.p.rsk;
   info->workspace_bytes = L.total;
   return MOE_OK;
 }

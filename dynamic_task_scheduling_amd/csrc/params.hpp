@@ -7,7 +7,7 @@ namespace moe {
 
 // Task kinds.  A task id packs the kind in bits [30:27] and a payload below.
 enum TaskKind : int {
-  TK_ROUTE = 1,  // payload rt: router logits + top-k for tokens [32 rt, 32 rt + 32)
+  TK_ROUTE = 1,  // payload rt * rsk + ks: router K slice ks of tokens [32 rt, 32 rt + 32)
   TK_POS = 2,    // payload rt: stable positions of those tokens' slots
   TK_PERM = 3,   // payload mt * pch + c: gather rows chunk c of row-tile mt
   TK_UP = 4,     // payload mt * n_up_n + n: gate/up GEMM + SiLU-gate epilogue
@@ -61,6 +61,7 @@ struct Params {
   int dtype;
   // derived geometry
   int n_rt;        // router / position tiles of 32 tokens
+  int rsk;         // router K slices (divides d / 64)
   int hist_ld;     // row stride of hist / rt_base (n_rt rounded up to 4)
   int n_up_n;      // f / 128
   int n_down_n;    // d / 128
@@ -97,6 +98,8 @@ struct Params {
   int* ctrl;
   int* slots;      // [kNumQueues][q_cap]
   float* logits;   // [T][E]
+  float* route_part;  // [rsk][T][E] router partial sums (rsk > 1)
+  int* cnt_route;  // [n_rt] router slices still running
   int* idx;        // [T][k]
   float* w;        // [T][k]
   int* hist;       // [E_loc][hist_ld]

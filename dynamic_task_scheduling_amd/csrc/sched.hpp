@@ -14,9 +14,9 @@
 // members drain the permute queue and then join the compute queue, while the
 // rest start on expert GEMMs as soon as rows land (temporal interleaving).
 //
-// Queues: QA (router tiles, shared-expert UP tiles, position tiles: all
-// workers), QM (permute tasks: the memory group), QC (expert UP/DOWN and
-// shared DOWN tasks: everyone once their own queue is drained).
+// Queues: QA (router tiles and position tiles: all workers, first),
+// QM (permute tasks: the memory group), QC (shared-expert tiles, expert
+// UP/DOWN tiles: everyone once their own queue is drained).
 //
 // Static mode (the baseline the pages argue against): identical tasks,
 // pre-assigned round-robin from a worker ticket, a grid barrier between
@@ -73,14 +73,13 @@ DEV bool wait_zero(const Params& p, const int* c) {
   return true;
 }
 
-// All threads: push n task ids (id_of(i)) into queue q.  Callers have run a
-// release fence in every thread, so the slot stores publish the data.
+// All threads: push n task ids (id_of(i)) into queue q.  The slot stores are
+// agent-coherent; everything the new tasks read was written through and
+// drained by its producers before they published.
 template <typename F>
 DEV void push_burst(const Params& p, int q, int n, int* s_tmp, F&& id_of) {
   if (n <= 0) return;
-  // Data this workgroup acquired from other producers (through the counter
-  // it just decremented) must be visible before the consumer is.
-  fence_release_agent();
+  publish_fence();
   if (threadIdx.x == 0) s_tmp[0] = add_relaxed(cw(p, CW_TAIL + q), n);
   __syncthreads();
   const int base = s_tmp[0];
@@ -95,19 +94,19 @@ DEV void push_burst(const Params& p, int q, int n, int* s_tmp, F&& id_of) {
 
 // All threads: the last of `target` arrivals on counter c returns true.
 DEV bool arrive_last(int* c, int delta, int last_old, int* s_tmp) {
-  fence_release_agent();
+  publish_fence();
   __syncthreads();
   if (threadIdx.x == 0) s_tmp[0] = (add_acqrel(c, delta) == last_old);
   __syncthreads();
   const bool last = s_tmp[0] != 0;
   __syncthreads();
-  if (last) fence_acquire_agent();
+  if (last) consume_fence();
   return last;
 }
 
 // Grid barrier over all workers (static mode).  Returns false on abort.
 DEV bool grid_barrier(const Params& p, int& gen, int* s_tmp) {
-  fence_release_agent();
+  publish_fence();
   __syncthreads();
   if (threadIdx.x == 0) {
     int ok = 1;
@@ -129,7 +128,7 @@ DEV bool grid_barrier(const Params& p, int& gen, int* s_tmp) {
   const bool ok = s_tmp[0] != 0;
   __syncthreads();
   ++gen;
-  fence_acquire_agent();
+  consume_fence();
   return ok;
 }
 
@@ -156,8 +155,8 @@ struct Sched {
     const int n_mt = ld_relaxed(cw(p, CW_NMT));
     const int n_perm = ld_relaxed(cw(p, CW_NPERM));
     const bool split = p.split_policy != 2;
-    const int n_comp = n_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sdown;
-    fence_release_agent();
+    const int n_comp = n_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup + p.n_sdown;
+    publish_fence();
     __syncthreads();
     if (threadIdx.x == 0) {
       st_relaxed(cw(p, CW_TOTAL + QM), split ? n_perm : 0);
@@ -175,7 +174,7 @@ struct Sched {
         if (base + p.n_down_n <= p.q_cap) sl = p.slots + (size_t)QC * p.q_cap + base;
         else set_error(p, 6);
         if (sl) {
-          fence_release_agent();
+          publish_fence();
           for (int n = 0; n < p.n_down_n; ++n)
             st_relaxed(sl + n, make_task(TK_SDOWN, i * p.n_down_n + n) + 1);
         }
@@ -193,8 +192,14 @@ struct Sched {
     *t_body = 0;
     switch (kind) {
       case TK_ROUTE: {
-        S::route(p, pl, smem);
+        const int rt = pl / p.rsk;
+        S::route(p, rt, pl % p.rsk, smem);
         *t_body = rtc();
+        if (p.rsk > 1) {
+          // the last K slice of this tile reduces the partials and routes
+          if (!arrive_last(p.cnt_route + rt, -1, 1, s_tmp)) break;
+          S::route_finish(p, rt, smem);
+        }
         if (arrive_last(cw(p, CW_ROUTE_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
           S::build(p, smem);
           __syncthreads();
@@ -310,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
       }
       break;
     }
-    fence_acquire_agent();
+    consume_fence();
     const uint64_t t_start = rtc();
     uint64_t t_body;
     Sched<Elem>::run(p, v, smem, s_tmp, true, &t_body);
@@ -336,9 +341,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
     trace_record(p, task, w, t0, t0, t_body);
   };
   // stage 1: router tiles and shared-expert UP tiles
-  const int nA = p.n_rt + p.n_sup;
+  const int n_route = p.n_rt * p.rsk;
+  const int nA = n_route + p.n_sup;
   for (int i = w; i < nA; i += W)
-    exec(i < p.n_rt ? make_task(TK_ROUTE, i) : make_task(TK_SUP, i - p.n_rt));
+    exec(i < n_route ? make_task(TK_ROUTE, i) : make_task(TK_SUP, i - n_route));
   if (!grid_barrier(p, gen, s_tmp)) return;
   if (w == 0) {
     Stages<Elem>::build(p, smem);
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
       const bool ok = s_tmp[1];
       __syncthreads();
       if (!ok) return;
-      fence_acquire_agent();
+      consume_fence();
       exec(make_task(TK_UP, i));
     }
   }
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
     const bool ok = s_tmp[1];
     __syncthreads();
     if (!ok) return;
-    fence_acquire_agent();
+    consume_fence();
     exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
   }
 }
@@ -399,14 +405,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
 // ----------------------------------------------- one launch per stage
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void k_stage_route(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[Tile<Elem, 32, 1>::LDS_BYTES + 32 * kMaxE * 4 + kMaxE * 4];
-  if (p.route_from_logits) Stages<Elem>::topk_from_logits(p, blockIdx.x, smem);
-  else Stages<Elem>::route(p, blockIdx.x, smem);
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kRouteTile + 32 * kMaxE * 4 + kMaxE * 4];
+  if (p.route_from_logits) {
+    Stages<Elem>::topk_from_logits(p, blockIdx.x, smem);
+    return;
+  }
+  const int rt = blockIdx.x / p.rsk;
+  Stages<Elem>::route(p, rt, blockIdx.x % p.rsk, smem);
+  if (p.rsk > 1) {
+    __shared__ int s_tmp[4];
+    if (!arrive_last(p.cnt_route + rt, -1, 1, s_tmp)) return;
+    Stages<Elem>::route_finish(p, rt, smem);
+  }
 }
 
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void k_stage_build(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[16384];
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kBuildSmem];
   Stages<Elem>::build(p, smem);
 }
 
@@ -442,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stage_up(Params p) {
 
 template <typename Elem>
 __global__ __launch_bounds__(kThreads, 1) void k_stage_down(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[Tile<Elem, 128, 1>::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
   const int b = blockIdx.x;
   const int routed = p.max_mt * p.n_down_n * p.splitk;
   if (b < routed) {
@@ -464,17 +479,23 @@ __global__ __launch_bounds__(kThreads) void k_reset(Params p) {
   const int ncw = CW_COUNT * kCtrlStride;
   for (int i = gid; i < ncw; i += stride) p.ctrl[i] = 0;
   const size_t ns = (size_t)kNumQueues * p.q_cap;
+  const int n_route = p.n_rt * p.rsk;
+  // QA starts with the router tasks, QC with the shared-expert UP tiles
+  // (they need no routing, so they fill the routing phase's idle workers)
   for (size_t i = gid; i < ns; i += stride) {
+    const size_t q = i / p.q_cap, j = i % p.q_cap;
     int v = 0;
-    if (i < (size_t)p.n_rt) v = make_task(TK_ROUTE, (int)i) + 1;
-    else if (i < (size_t)(p.n_rt + p.n_sup)) v = make_task(TK_SUP, (int)i - p.n_rt) + 1;
+    if (q == QA && j < (size_t)n_route) v = make_task(TK_ROUTE, (int)j) + 1;
+    else if (q == QC && j < (size_t)p.n_sup) v = make_task(TK_SUP, (int)j) + 1;
     p.slots[i] = v;
   }
+  for (int i = gid; i < p.n_rt; i += stride) p.cnt_route[i] = p.rsk;
   const int nsm = p.n_shared * p.n_smt;
   for (int i = gid; i < nsm; i += stride) p.cnt_sdown[i] = p.n_s_up_n + 1;
   if (gid == 0) {
-    p.ctrl[(CW_TAIL + QA) * kCtrlStride] = p.n_rt + p.n_sup;
-    p.ctrl[(CW_TOTAL + QA) * kCtrlStride] = 2 * p.n_rt + p.n_sup;
+    p.ctrl[(CW_TAIL + QA) * kCtrlStride] = n_route;
+    p.ctrl[(CW_TOTAL + QA) * kCtrlStride] = n_route + p.n_rt;
+    p.ctrl[(CW_TAIL + QC) * kCtrlStride] = p.n_sup;
     p.ctrl[(CW_TOTAL + QM) * kCtrlStride] = 0x7fffffff;
     p.ctrl[(CW_TOTAL + QC) * kCtrlStride] = 0x7fffffff;
   }

@@ -11,6 +11,7 @@
 #include "common.hpp"
 #include "params.hpp"
 #include "tile.hpp"
+#include "tile2.hpp"
 
 namespace moe {
 
@@ -42,14 +43,63 @@ DEV int slice_of(int tile, int n, int s) {
   return ks;
 }
 
+// GEMM tile used for expert tasks: bf16 runs the multi-stage LDS ring
+// (tile2.hpp); fp32 runs the register-staged tile (tile.hpp).
+// Ring depth: as many 64-deep K stages as fit in 144 KB of LDS (bytes in
+// flight set a streaming task's rate), at most 7.
+constexpr int tile2_stages(int bm, int nb) {
+  return (147456 / (bm * 128 + nb * 16384)) > 7 ? 7 : (147456 / (bm * 128 + nb * 16384));
+}
+template <typename Elem, int BM, int NB>
+struct GemmSel {
+  using T = Tile<Elem, BM, NB>;
+};
+template <int BM, int NB>
+struct GemmSel<bf16_t, BM, NB> {
+  using T = Tile2<BM, NB, tile2_stages(BM, NB)>;
+};
+
+// Router tiles (32 tokens x 128 experts): a 4-stage ring for bf16 when the
+// router width is a multiple of 128, so the router scratch fits beside it.
+template <typename Elem>
+struct RouteSel {
+  using T = Tile<Elem, 32, 1>;
+};
+template <>
+struct RouteSel<bf16_t> {
+  using T = Tile2<32, 1, 4>;
+};
+
+template <typename T>
+struct requires_n_valid {
+  static constexpr bool value = false;
+};
+template <typename Elem, int BM, int NB>
+struct requires_n_valid<Tile<Elem, BM, NB>> {
+  static constexpr bool value = true;
+};
+
 template <typename Elem>
 struct Stages {
   using TR = ElemTraits<Elem>;
-  static constexpr int kSmemTile = Tile<Elem, 128, 2>::LDS_BYTES;
+  static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+  // LDS of the largest expert tile over every row class and B count
+  static constexpr int kSmemTile =
+      cmax(cmax(cmax(GemmSel<Elem, 32, 1>::T::LDS_BYTES, GemmSel<Elem, 64, 1>::T::LDS_BYTES),
+                cmax(GemmSel<Elem, 128, 1>::T::LDS_BYTES, GemmSel<Elem, 32, 2>::T::LDS_BYTES)),
+           cmax(GemmSel<Elem, 64, 2>::T::LDS_BYTES, GemmSel<Elem, 128, 2>::T::LDS_BYTES));
   // Router scratch after the router tile's own two stages.
-  static constexpr int kRouteTile = Tile<Elem, 32, 1>::LDS_BYTES;
+  static constexpr int kRouteTile =
+      Tile<Elem, 32, 1>::LDS_BYTES > RouteSel<Elem>::T::LDS_BYTES
+          ? Tile<Elem, 32, 1>::LDS_BYTES
+          : RouteSel<Elem>::T::LDS_BYTES;
   static constexpr int kSmem = kSmemTile;
   static_assert(kRouteTile + 32 * kMaxE * 4 + kMaxE * 4 <= kSmemTile, "route LDS");
+  // build(): small tables first, then a histogram staging area
+  static constexpr int kBuildScratch = 16384;
+  static constexpr int kBuildStage = 65536;
+  static constexpr int kBuildSmem = kBuildScratch + kBuildStage;
+  static_assert(kBuildSmem <= kSmemTile, "build LDS");
 
   // --------------------------------------------------------------- router
   // Top-k with renormalised softmax for `rows` tokens starting at t0, whose
@@ -104,8 +154,8 @@ struct Stages {
           s += a[j];
         }
         for (int j = 0; j < k; ++j) {
-          p.idx[(size_t)t * k + j] = sel_e[j];
-          p.w[(size_t)t * k + j] = a[j] / s;
+          st_wt(p.idx + (size_t)t * k + j, sel_e[j]);
+          st_wt(p.w + (size_t)t * k + j, a[j] / s);
           const int el = sel_e[j] - p.e_begin;
           if (el >= 0 && el < p.E_loc) atomicAdd(&hist_s[el], 1);
         }
@@ -115,25 +165,20 @@ struct Stages {
 
   static DEV void write_hist(const Params& p, int rt, const int* hist_s) {
     for (int e = threadIdx.x; e < p.E_loc; e += kThreads)
-      p.hist[(size_t)e * p.hist_ld + rt] = hist_s[e];
+      st_wt(p.hist + (size_t)e * p.hist_ld + rt, hist_s[e]);
   }
 
-  // ROUTE(rt): zero y rows, logits = x W_r + b (MFMA tile), top-k, tile histogram.
-  static TASKFN void route(const Params& p, int rt, char* smem) {
-    using RT = Tile<Elem, 32, 1>;
-    const int t0 = rt * kTB;
-    const int rows = min(kTB, p.T - t0);
-    float* Ls = reinterpret_cast<float*>(smem + kRouteTile);     // [32][E]
-    int* hist_s = reinterpret_cast<int*>(smem + kRouteTile + 32 * kMaxE * 4);
-    for (int e = threadIdx.x; e < p.E_loc; e += kThreads) hist_s[e] = 0;
-    // zero this tile's output rows (the combine accumulates into them)
-    {
-      float4* y4 = reinterpret_cast<float4*>(p.y + (size_t)t0 * p.d);
-      const int n4 = rows * p.d / 4;
-      for (int i = threadIdx.x; i < n4; i += kThreads) y4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const Elem* x = reinterpret_cast<const Elem*>(p.x) + (size_t)t0 * p.d;
-    const Elem* wr = reinterpret_cast<const Elem*>(p.wr);
+  // ROUTE(rt, ks): router logits of tokens [32 rt, 32 rt + 32) over K slice
+  // ks of rsk.  With rsk == 1 the task also adds the bias, picks the top-k
+  // and writes the tile histogram; with rsk > 1 it writes an fp32 partial
+  // and the last slice to finish runs route_finish (fixed-order sum, so the
+  // logits do not depend on which slice finished last).  Slice 0 zeroes the
+  // tile's y rows, which the combine later accumulates into.
+  template <typename RT>
+  static DEV void route_gemm(const Params& p, int t0, int rows, int k0, int K, float* Ls,
+                             float* part, char* smem) {
+    const Elem* x = reinterpret_cast<const Elem*>(p.x) + (size_t)t0 * p.d + k0;
+    const Elem* wr = reinterpret_cast<const Elem*>(p.wr) + (size_t)k0 * p.E;
     for (int n0 = 0; n0 < p.E; n0 += kBN) {
       typename RT::Args g;
       g.A = x;
@@ -141,24 +186,76 @@ struct Stages {
       g.a_rows = rows;
       g.B[0] = wr + n0;
       g.ldb = p.E;
-      g.n_valid = min(kBN, p.E - n0);
-      g.K = p.d;
+      if constexpr (requires_n_valid<RT>::value) g.n_valid = min(kBN, p.E - n0);
+      g.K = K;
       typename RT::Acc acc;
-      RT::run(g, reinterpret_cast<Elem*>(smem), acc);
+      if constexpr (requires_n_valid<RT>::value) RT::run(g, reinterpret_cast<Elem*>(smem), acc);
+      else RT::run(g, smem, acc);
       RT::for_each([&](int row, int col, int fm, int fn, int i) __attribute__((always_inline)) {
         const int e = n0 + col;
         if (e < p.E) {
-          float v = acc[0][fm][fn][i];
-          if (p.bias) v += p.bias[e];
-          Ls[row * p.E + e] = v;
-          if (row < rows) p.logits[(size_t)(t0 + row) * p.E + e] = v;
+          const float v = acc[0][fm][fn][i];
+          if (part) {
+            if (row < rows) st_wt(part + (size_t)(t0 + row) * p.E + e, v);
+          } else {
+            Ls[row * p.E + e] = v;
+          }
         }
       });
+    }
+  }
+
+  static TASKFN void route(const Params& p, int rt, int ks, char* smem) {
+    const int t0 = rt * kTB;
+    const int rows = min(kTB, p.T - t0);
+    if (ks == 0) {
+      for (int r = 0; r < rows; ++r) {
+        float* yr = p.y + (size_t)(t0 + r) * p.d;
+        for (int i = threadIdx.x; i < p.d / 4; i += kThreads) st_wt16(yr, i * 16, make_uint4(0, 0, 0, 0));
+      }
+    }
+    const int Ks = p.d / p.rsk;
+    float* Ls = reinterpret_cast<float*>(smem + kRouteTile);     // [32][E]
+    float* part = p.rsk > 1 ? p.route_part + (size_t)ks * p.T * p.E : nullptr;
+    if (ElemTraits<Elem>::kBf16 && (p.E % kBN) == 0)
+      route_gemm<typename RouteSel<Elem>::T>(p, t0, rows, ks * Ks, Ks, Ls, part, smem);
+    else
+      route_gemm<Tile<Elem, 32, 1>>(p, t0, rows, ks * Ks, Ks, Ls, part, smem);
+    if (p.rsk == 1) route_topk(p, rt, smem, false);
+  }
+
+  // Sum the K-slice partials of tile rt in slice order, then top-k.
+  static TASKFN void route_finish(const Params& p, int rt, char* smem) {
+    const int t0 = rt * kTB;
+    const int rows = min(kTB, p.T - t0);
+    float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
+    for (int i = threadIdx.x; i < rows * p.E; i += kThreads) {
+      float v = 0.f;
+      for (int ks = 0; ks < p.rsk; ++ks) v += p.route_part[((size_t)ks * p.T + t0) * p.E + i];
+      Ls[i] = v;
+    }
+    route_topk(p, rt, smem, true);
+  }
+
+  // Bias, exported logits, top-k and the tile histogram from Ls.
+  static DEV void route_topk(const Params& p, int rt, char* smem, bool synced) {
+    const int t0 = rt * kTB;
+    const int rows = min(kTB, p.T - t0);
+    float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
+    int* hist_s = reinterpret_cast<int*>(smem + kRouteTile + 32 * kMaxE * 4);
+    for (int e = threadIdx.x; e < p.E_loc; e += kThreads) hist_s[e] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < rows * p.E; i += kThreads) {
+      const int e = i % p.E;
+      const float v = Ls[i] + (p.bias ? p.bias[e] : 0.f);
+      Ls[i] = v;
+      p.logits[(size_t)t0 * p.E + i] = v;
     }
     __syncthreads();
     topk(p, t0, rows, Ls, p.E, hist_s);
     __syncthreads();
     write_hist(p, rt, hist_s);
+    (void)synced;
   }
 
   // Routing from given logits (checking path): top-k + histogram only.
@@ -194,22 +291,37 @@ struct Stages {
     int* s_wm = reinterpret_cast<int*>(s_red + kThreads); // [kThreads]
     const int tid = threadIdx.x;
     const int El = p.E_loc;
-    // 1. per-expert counts and per-tile exclusive bases
-    if (tid < El) {
-      const int* h = p.hist + (size_t)tid * p.hist_ld;
-      int* b = p.rt_base + (size_t)tid * p.hist_ld;
+    // 1. per-expert counts and per-tile exclusive bases.  The histogram is
+    //    staged through LDS in column chunks so its loads are all in flight
+    //    at once (one row per thread would be a chain of dependent loads).
+    {
+      int* s_h = reinterpret_cast<int*>(smem + kBuildScratch);
+      const int C = max(4, min(p.hist_ld, (kBuildStage / 4 / max(El, 1)) & ~3));
       int run = 0;
-      for (int r = 0; r < p.n_rt; r += 4) {
-        const int4 v = *reinterpret_cast<const int4*>(h + r);
-        int4 o;
-        o.x = run; run += v.x;
-        o.y = run; run += (r + 1 < p.n_rt) ? v.y : 0;
-        o.z = run; run += (r + 2 < p.n_rt) ? v.z : 0;
-        o.w = run; run += (r + 3 < p.n_rt) ? v.w : 0;
-        *reinterpret_cast<int4*>(b + r) = o;
+      for (int r0 = 0; r0 < p.n_rt; r0 += C) {
+        const int cw = min(C, p.hist_ld - r0);
+        const int q4 = cw / 4;
+        for (int i = tid; i < El * q4; i += kThreads) {
+          const int e = i / q4, q = i % q4;
+          *reinterpret_cast<int4*>(s_h + e * cw + q * 4) =
+              *reinterpret_cast<const int4*>(p.hist + (size_t)e * p.hist_ld + r0 + q * 4);
+        }
+        __syncthreads();
+        if (tid < El) {
+          int* b = p.rt_base + (size_t)tid * p.hist_ld + r0;
+          const int nr = min(cw, p.n_rt - r0);
+          for (int r = 0; r < nr; ++r) {
+            const int v = s_h[tid * cw + r];
+            st_wt(b + r, run);
+            run += v;
+          }
+        }
+        __syncthreads();
       }
-      s_cnt[tid] = run;
-      p.counts[tid] = run;
+      if (tid < El) {
+        s_cnt[tid] = run;
+        st_wt(p.counts + tid, run);
+      }
     }
     __syncthreads();
     // 2. offsets (exclusive scan) and expert order by descending count
@@ -229,13 +341,13 @@ struct Stages {
       s_ord[rank] = tid;
     }
     __syncthreads();
-    for (int e = tid; e <= El; e += kThreads) p.offsets[e] = s_off[e];
+    for (int e = tid; e <= El; e += kThreads) st_wt(p.offsets + e, s_off[e]);
     // 3. row tiles (128 rows; the last one of an expert takes the smallest
     //    class that holds it) and permute chunks, per rank
     const float esz = TR::kBf16 ? 2.f : 4.f;
     if (tid < El) {
       const int e = s_ord[tid];
-      p.eorder[tid] = e;
+      st_wt(p.eorder + tid, e);
       const int c = s_cnt[e];
       const int nt = (c + 127) / 128;
       int np = 0;
@@ -283,13 +395,17 @@ struct Stages {
         t.row0 = s_off[e] + 128 * m;
         t.rows = rows;
         t.bm = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
-        p.mtiles[mt] = t;
+        int* tw = reinterpret_cast<int*>(p.mtiles + mt);
+        st_wt(tw + 0, t.e);
+        st_wt(tw + 1, t.row0);
+        st_wt(tw + 2, t.rows);
+        st_wt(tw + 3, t.bm);
         const int np = (rows + p.perm_rows - 1) / p.perm_rows;
-        p.cnt_perm[mt] = np;
+        st_wt(p.cnt_perm + mt, np);
         for (int ks = 0; ks < p.splitk; ++ks)
-          p.cnt_down[mt * p.splitk + ks] =
-              slice_lo(ks + 1, p.n_up_n, p.splitk) - slice_lo(ks, p.n_up_n, p.splitk);
-        for (int c2 = 0; c2 < np; ++c2) p.perm_list[pb++] = make_task(TK_PERM, mt * p.pch + c2);
+          st_wt(p.cnt_down + mt * p.splitk + ks,
+                slice_lo(ks + 1, p.n_up_n, p.splitk) - slice_lo(ks, p.n_up_n, p.splitk));
+        for (int c2 = 0; c2 < np; ++c2) st_wt(p.perm_list + pb++, make_task(TK_PERM, mt * p.pch + c2));
       }
     }
     // 4. spatial split: smallest memory group whose gather finishes within
@@ -347,16 +463,16 @@ struct Stages {
       const int e = p.idx[(size_t)t0 * k + i];
       s_idx[i] = e - p.e_begin;
       s_w[i] = p.w[(size_t)t0 * k + i];
-      if (e < p.e_begin || e - p.e_begin >= p.E_loc) p.slot_pos[(size_t)t0 * k + i] = -1;
+      if (e < p.e_begin || e - p.e_begin >= p.E_loc) st_wt(p.slot_pos + (size_t)t0 * k + i, -1);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < p.E_loc; e += kThreads) {
       int pos = p.offsets[e] + p.rt_base[(size_t)e * p.hist_ld + rt];
       for (int i = 0; i < ns; ++i) {
         if (s_idx[i] == e) {
-          p.perm[pos] = t0 + i / k;
-          p.rw[pos] = s_w[i];
-          p.slot_pos[(size_t)t0 * k + i] = pos;
+          st_wt(p.perm + pos, t0 + i / k);
+          st_wt(p.rw + pos, s_w[i]);
+          st_wt(p.slot_pos + (size_t)t0 * k + i, pos);
           ++pos;
         }
       }
@@ -373,26 +489,30 @@ struct Stages {
     const int cpr = p.d * (int)sizeof(Elem) / 16;           // 16-byte chunks per row
     const int total = (r1 - r0) * cpr;
     const uint4* x = reinterpret_cast<const uint4*>(p.x);
-    uint4* xp = reinterpret_cast<uint4*>(p.Xp);
+    char* xp = reinterpret_cast<char*>(p.Xp);
+    const size_t row_bytes = (size_t)cpr * 16;
+    // 16 loads in flight per thread (64 KB per workgroup): a gather is a
+    // latency-bound copy, so bytes in flight set its rate.
+    constexpr int U = 16;
     int i = threadIdx.x;
-    for (; i + 3 * kThreads < total; i += 4 * kThreads) {
-      uint4 v[4];
+    for (; i + (U - 1) * kThreads < total; i += U * kThreads) {
+      uint4 v[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int ii = i + u * kThreads;
         const int r = r0 + ii / cpr, cc = ii % cpr;
         v[u] = x[(size_t)p.perm[r] * cpr + cc];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int ii = i + u * kThreads;
         const int r = r0 + ii / cpr, cc = ii % cpr;
-        xp[(size_t)r * cpr + cc] = v[u];
+        st_wt16(xp + (size_t)r * row_bytes, cc * 16, v[u]);
       }
     }
     for (; i < total; i += kThreads) {
       const int r = r0 + i / cpr, cc = i % cpr;
-      xp[(size_t)r * cpr + cc] = x[(size_t)p.perm[r] * cpr + cc];
+      st_wt16(xp + (size_t)r * row_bytes, cc * 16, x[(size_t)p.perm[r] * cpr + cc]);
     }
   }
 
@@ -401,7 +521,7 @@ struct Stages {
   template <int BM>
   static DEV void up_tile(const Elem* A, int lda, int rows, const Elem* wg, const Elem* wu,
                           int ldb, int K, Elem* Hout, int ldh, char* smem) {
-    using TL = Tile<Elem, BM, 2>;
+    using TL = typename GemmSel<Elem, BM, 2>::T;
     typename TL::Args g;
     g.A = A;
     g.lda = lda;
@@ -409,10 +529,11 @@ struct Stages {
     g.B[0] = wg;
     g.B[1] = wu;
     g.ldb = ldb;
-    g.n_valid = kBN;
     g.K = K;
+    if constexpr (!TR::kBf16) g.n_valid = kBN;
     typename TL::Acc acc;
-    TL::run(g, reinterpret_cast<Elem*>(smem), acc);
+    if constexpr (TR::kBf16) TL::run(g, smem, acc);
+    else TL::run(g, reinterpret_cast<Elem*>(smem), acc);
     // stage the tile in LDS, then write whole rows
     constexpr int SLD = kBN + 16 / (int)sizeof(Elem);
     Elem* st = reinterpret_cast<Elem*>(smem);
@@ -426,8 +547,8 @@ struct Stages {
     constexpr int CPR = kBN * (int)sizeof(Elem) / 16;
     for (int i = threadIdx.x; i < rows * CPR; i += kThreads) {
       const int r = i / CPR, c = i % CPR;
-      *reinterpret_cast<uint4*>(Hout + (size_t)r * ldh + c * (16 / (int)sizeof(Elem))) =
-          *reinterpret_cast<const uint4*>(st + r * SLD + c * (16 / (int)sizeof(Elem)));
+      st_wt16(Hout + (size_t)r * ldh, c * 16,
+              *reinterpret_cast<const uint4*>(st + r * SLD + c * (16 / (int)sizeof(Elem))));
     }
     __syncthreads();
   }
@@ -438,17 +559,18 @@ struct Stages {
   static DEV void down_tile(const Elem* A, int lda, int rows, const Elem* wd, int ldb, int K,
                             const int* tok, const float* wt, int row_tok0, float* y, int ldy,
                             char* smem) {
-    using TL = Tile<Elem, BM, 1>;
+    using TL = typename GemmSel<Elem, BM, 1>::T;
     typename TL::Args g;
     g.A = A;
     g.lda = lda;
     g.a_rows = rows;
     g.B[0] = wd;
     g.ldb = ldb;
-    g.n_valid = kBN;
     g.K = K;
+    if constexpr (!TR::kBf16) g.n_valid = kBN;
     typename TL::Acc acc;
-    TL::run(g, reinterpret_cast<Elem*>(smem), acc);
+    if constexpr (TR::kBf16) TL::run(g, smem, acc);
+    else TL::run(g, reinterpret_cast<Elem*>(smem), acc);
     TL::for_each([&](int row, int col, int fm, int fn, int i) __attribute__((always_inline)) {
       if (row < rows) {
         const float v = acc[0][fm][fn][i];

@@ -66,7 +66,7 @@ struct Tile {
   };
 
   static DEV void load(const Args& g, int kt, Regs& r) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     const int k0 = kt * BK;
 #pragma unroll
     for (int p = 0; p < A_CHUNKS; ++p) {
@@ -122,7 +122,7 @@ struct Tile {
   }
 
   static DEV void store(const Regs& r, Elem* stage) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
 #pragma unroll
     for (int p = 0; p < A_CHUNKS; ++p) {
       const int row = (tid >> 3) + 32 * p;
@@ -164,8 +164,9 @@ struct Tile {
   }
 
   static DEV void compute(const Elem* stage, Acc& acc) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid_ = opaque_tid();
+    const int lane = tid_ & 63;
+    const int wave = tid_ >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int l16 = lane & 15, lg = lane >> 4;
 #pragma unroll
@@ -242,8 +243,9 @@ struct Tile {
   // 4*(lane/16) .. +3 of its fragment.
   template <typename F>
   static DEV void for_each(F&& fn) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid_ = opaque_tid();
+    const int lane = tid_ & 63;
+    const int wave = tid_ >> 6;
     const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)

@@ -158,6 +158,7 @@ typedef struct moe_info {
   int permute_rows;     /* rows per permute task                           */
   int max_mtiles;       /* capacity of the expert row-tile table           */
   int max_tasks;        /* capacity of the ready queues                    */
+  int route_splits;     /* router K slices per router tile                 */
   size_t workspace_bytes;
 } moe_info;
 

@@ -26,14 +26,15 @@ def check_trace(raw, layer, routing):
     pl = tr["payload"]
     n_smt = (s.T + 127) // 128
     n_sup_n = (s.f_shared // 128) if s.n_shared else 0
-    expect = {ROUTE: n_rt, POS: n_rt, UP: n_mt * n_up, DOWN: n_mt * n_down * sk,
+    expect = {ROUTE: n_rt * info["route_splits"], POS: n_rt, UP: n_mt * n_up,
+              DOWN: n_mt * n_down * sk,
               SUP: s.n_shared * n_smt * n_sup_n, SDOWN: s.n_shared * n_smt * n_down}
     for k, n in expect.items():
         assert int((kinds == k).sum()) == n, "kind %d ran %d times, expected %d" % (
             k, int((kinds == k).sum()), n)
     start = {int(t): int(v) for t, v in zip(tr["task"], tr["t_start"])}
     end = {int(t): int(v) for t, v in zip(tr["task"], tr["t_end"])}
-    route_end = max(end[(ROUTE << 27) | i] for i in range(n_rt))
+    route_end = max(int(e) for e, k in zip(tr["t_end"], kinds) if k == ROUTE)
     pos_end = max(end[(POS << 27) | i] for i in range(n_rt))
     perm_end = defaultdict(int)
     for t, k, p in zip(tr["task"], kinds, pl):

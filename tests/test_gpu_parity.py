@@ -16,7 +16,7 @@ pytestmark = [pytest.mark.gpu,
 import oracle
 from dynamic_task_scheduling_amd.configs import LayerShape, workload
 from dynamic_task_scheduling_amd.moe import MoELayer, route_from_logits
-from gpu_util import check_routing, gen_inputs, host_inputs, run_and_check
+from gpu_util import check_routing, compare_y, gen_inputs, host_inputs, run_and_check
 
 MODES = [("dynamic", "cost_model"), ("dynamic", "none"), ("dynamic", "fixed"),
          ("static", "fixed"), ("multi_kernel", "none")]
@@ -162,6 +162,28 @@ def test_repeat_and_poisoned_workspace(mid):
     torch.cuda.synchronize()
     assert torch.isfinite(y2).all()
     assert (y2 - y0).abs().max().item() <= 1e-5 * y0.abs().max().item()
+
+
+@pytest.mark.parametrize("mode,split", [("dynamic", "cost_model"), ("dynamic", "none"),
+                                        ("static", "fixed")])
+def test_consecutive_calls_new_inputs(mode, split):
+    """One workspace, several calls with different token batches (so the
+    routing, the gathered rows and the hidden rows all change): every call
+    matches the oracle, so no call reads data left by an earlier one."""
+    g = gen_inputs(MID, "mid", 1)
+    n = host_inputs(g)
+    layer = MoELayer(MID, g, mode=mode, split=split, timeout_ms=3000)
+    for seed in (21, 22, 23):
+        xs = torch.randn((MID.T, MID.d), generator=torch.Generator().manual_seed(seed))
+        x = xs.to(torch.bfloat16).cuda()
+        y, r = layer(x, return_routing=True, check_errors=True)
+        torch.cuda.synchronize()
+        nx = dict(n, x=x.cpu().view(torch.int16).numpy().view(np.uint16))
+        ro = oracle.route(r.logits.cpu().numpy(), MID.k)
+        check_routing(r, ro, MID)
+        shared = (nx["ws_gate"], nx["ws_up"], nx["ws_down"])
+        yo = oracle.moe_layer(nx["x"], nx["w_gate"], nx["w_up"], nx["w_down"], ro, 0, shared)
+        compare_y(y.cpu().numpy(), yo, "bf16")
 
 
 def test_trace_happens_before(mid):
