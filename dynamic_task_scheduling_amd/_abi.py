@@ -11,7 +11,7 @@ c_int, c_uint, c_void_p, c_size_t = ctypes.c_int, ctypes.c_uint, ctypes.c_void_p
 MOE_F32, MOE_BF16 = 0, 1
 MODES = {"dynamic": 0, "static": 1, "multi_kernel": 2}
 SPLITS = {"cost_model": 0, "fixed": 1, "none": 2}
-FLAG_CHECK, FLAG_TRACE, FLAG_PHASE_SYNC, FLAG_REF_SYNC = 0x1, 0x2, 0x4, 0x8
+FLAG_CHECK, FLAG_TRACE, FLAG_PHASE_SYNC, FLAG_REF_SYNC, FLAG_NO_STEAL = 0x1, 0x2, 0x4, 0x8, 0x10
 
 ERRORS = {
     0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_WORKSPACE", 3: "MOE_ERR_UNSUPPORTED",

@@ -32,6 +32,7 @@ constexpr int kClaimAbort = -2;
 constexpr int kFlagTrace = 0x2;
 constexpr int kFlagPhaseSync = 0x4;
 constexpr int kFlagRefSync = 0x8;
+constexpr int kFlagNoSteal = 0x10;
 
 DEV int* cw(const Params& p, int word) { return p.ctrl + word * kCtrlStride; }
 
@@ -40,15 +41,46 @@ DEV bool timed_out(const Params& p, uint64_t t0) {
 }
 
 // Thread 0: claim the next slot of queue q and wait until it is filled.
-DEV int claim(const Params& p, int q) {
-  const int h = add_relaxed(cw(p, CW_HEAD + q), 1);
+// `pend` keeps the claimed slot across calls: with `steal` set, a worker whose
+// compute-queue slot is still empty takes an already-pushed permute task
+// (non-committal compare-and-swap on the permute queue head) and comes back
+// to its own slot afterwards, so gather work never waits while compute
+// workers idle (the steal variant of the spatial split).
+DEV int claim(const Params& p, int q, int& pend, bool steal) {
+  if (pend < 0) pend = add_relaxed(cw(p, CW_HEAD + q), 1);
+  const int h = pend;
   const uint64_t t0 = rtc();
   for (;;) {
     const int total = ld_relaxed(cw(p, CW_TOTAL + q));
-    if (h >= total) return kClaimExhausted;
+    if (h >= total) {
+      pend = -1;
+      return kClaimExhausted;
+    }
     if (h < p.q_cap) {
       const int v = ld_relaxed(p.slots + (size_t)q * p.q_cap + h);
-      if (v != 0) return v - 1;
+      if (v != 0) {
+        pend = -1;
+        return v - 1;
+      }
+    }
+    if (steal) {
+      int* mh = cw(p, CW_HEAD + QM);
+      const int hm = ld_relaxed(mh);
+      if (hm < ld_relaxed(cw(p, CW_TAIL + QM)) && hm < p.q_cap && cas_relaxed(mh, hm, hm + 1) == hm) {
+        // a pusher reserved this slot; its store is at most a few cycles away
+        const int* sl = p.slots + (size_t)QM * p.q_cap + hm;
+        int v;
+        const uint64_t ts = rtc();
+        while ((v = ld_relaxed(sl)) == 0) {
+          if (ld_relaxed(cw(p, CW_ERROR)) != 0) return kClaimAbort;
+          if (timed_out(p, ts)) {
+            set_error(p, 5);
+            return kClaimAbort;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        return v - 1;
+      }
     }
     if (ld_relaxed(cw(p, CW_ERROR)) != 0) return kClaimAbort;
     if (timed_out(p, t0)) {
@@ -276,9 +308,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
   __shared__ int s_worker;
   if (threadIdx.x == 0) s_worker = add_relaxed(cw(p, CW_TICKET), 1);
   int q = QA;
+  int pend = -1;   // thread 0: claimed but not yet filled slot of queue q
+  const bool steal = p.split_policy != 2 && !(p.flags & kFlagNoSteal);
   for (;;) {
     uint64_t t_req = rtc();
-    if (threadIdx.x == 0) s_tmp[1] = claim(p, q);
+    if (threadIdx.x == 0) s_tmp[1] = claim(p, q, pend, steal && q == QC);
     __syncthreads();
     const int v = s_tmp[1];
     __syncthreads();

@@ -76,6 +76,7 @@ typedef enum {
 #define MOE_FLAG_TRACE 0x2u      /* record per-task timestamps in desc.trace */
 #define MOE_FLAG_PHASE_SYNC 0x4u /* static mode: barriers between stages (default on) */
 #define MOE_FLAG_REF_SYNC 0x8u   /* static mode: per-task counter waits instead of barriers */
+#define MOE_FLAG_NO_STEAL 0x10u  /* dynamic split: compute workers never take permute tasks */
 
 /* Return codes. */
 #define MOE_OK 0
