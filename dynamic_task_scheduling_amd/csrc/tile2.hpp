@@ -21,6 +21,8 @@
 // A lane of a global_load_lds instruction writes its 16 bytes at
 // base + 16 * lane, so the swizzles are applied to the global addresses.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -61,7 +63,11 @@ DEV uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
 }
 
-template <int BM, int NB, int S>
+// MF selects the MFMA: 16 = v_mfma_f32_16x16x32_bf16, 32 =
+// v_mfma_f32_32x32x16_bf16.  The 32x32 form keeps the matrix pipe far busier
+// with one wave per SIMD (measured 2.1 vs 1.35 PFLOP/s on gfx950) and halves
+// LDS fragment traffic per flop.
+template <int BM, int NB, int S, int MF = 32>
 struct Tile2 {
   static constexpr int BN = kBN;
   static constexpr int BK = 64;
@@ -69,8 +75,10 @@ struct Tile2 {
   static constexpr int WN = 4 / WM;
   static constexpr int WTM = BM / WM;
   static constexpr int WTN = BN / WN;
-  static constexpr int FM = WTM / 16;
-  static constexpr int FN = WTN / 16;
+  static constexpr int FM = WTM / MF;
+  static constexpr int FN = WTN / MF;
+  static_assert(MF == 16 || MF == 32, "MFMA shape");
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
   static constexpr int A_BYTES = BM * 128;
   static constexpr int B_BYTES = BK * 256;
   static constexpr int STAGE = A_BYTES + NB * B_BYTES;
@@ -81,7 +89,10 @@ struct Tile2 {
   static_assert(S >= 2 && S <= 8, "stages");
   static_assert((S - 2) * LOADS < 64, "vmcnt range");
 
-  using Acc = f32x4_t[NB][FM][FN];
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  using Frag = typename std::conditional<MF == 32, f32x16_t, f32x4_t>::type;
+  static constexpr int FRAG = MF == 32 ? 16 : 4;   // accumulator values per lane
+  using Acc = Frag[NB][FM][FN];
 
   struct Args {
     const bf16_t* A;    // row 0 of the tile, K column 0
@@ -124,42 +135,83 @@ struct Tile2 {
     const int wave = tid_ >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int l16 = lane & 15, lg = lane >> 4;
+    if constexpr (MF == 16) {
+      // A lane: row lane%16, K 8*(lane/16)..+7; B lane: column lane%16, same K.
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t a[FM];
-      bf16x8_t b[NB][FN];
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t a[FM];
+        bf16x8_t b[NB][FN];
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int m = wm * WTM + fm * 16 + l16;
-        const int c = kk * 4 + lg;
-        a[fm] = *reinterpret_cast<const LDS_AS bf16x8_t*>(
-            (const LDS_AS char*)stage + m * 128 + ((c ^ (m & 7)) << 4));
-      }
-#pragma unroll
-      for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int n = wn * WTN + fn * 16 + 4 * (l16 & 3);
-          const int c = n >> 3, half = (n >> 2) & 1;
-          bf16x4_t v[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int k = kk * 32 + 8 * lg + 4 * h + (l16 >> 2);
-            const LDS_AS char* p = (const LDS_AS char*)stage + A_BYTES + mtx * B_BYTES + k * 256 +
-                                   ((c ^ (2 * (k & 3))) << 4) + half * 8;
-            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)p);
-          }
-          b[mtx][fn] = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int fm = 0; fm < FM; ++fm) {
+          const int m = wm * WTM + fm * 16 + l16;
+          const int c = kk * 4 + lg;
+          a[fm] = *reinterpret_cast<const LDS_AS bf16x8_t*>(
+              (const LDS_AS char*)stage + m * 128 + ((c ^ (m & 7)) << 4));
         }
 #pragma unroll
-      for (int mtx = 0; mtx < NB; ++mtx)
+        for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+          for (int fn = 0; fn < FN; ++fn) {
+            const int n = wn * WTN + fn * 16 + 4 * (l16 & 3);
+            b[mtx][fn] = read_b(stage, mtx, n, kk * 32 + 8 * lg + (l16 >> 2));
+          }
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[mtx][fm][fn] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[mtx][fn], acc[mtx][fm][fn], 0, 0, 0);
+        for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              acc[mtx][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[mtx][fn],
+                                                                         acc[mtx][fm][fn], 0, 0, 0);
+      }
+    } else {
+      // A lane: row lane%32, K 8*(lane/32)..+7.  B lane: column lane%32, same
+      // K; 16-lane group g reads columns 16*(g&1).., K rows 8*(g>>1)..
+      const int l32 = lane & 31, lh = lane >> 5;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8_t a[FM];
+        bf16x8_t b[NB][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int m = wm * WTM + fm * 32 + l32;
+          const int c = kk * 2 + lh;
+          a[fm] = *reinterpret_cast<const LDS_AS bf16x8_t*>(
+              (const LDS_AS char*)stage + m * 128 + ((c ^ (m & 7)) << 4));
+        }
+#pragma unroll
+        for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int n = wn * WTN + fn * 32 + 16 * (lg & 1) + 4 * (l16 & 3);
+            b[mtx][fn] = read_b(stage, mtx, n, kk * 16 + 8 * (lg >> 1) + (l16 >> 2));
+          }
+#pragma unroll
+        for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              acc[mtx][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fm], b[mtx][fn],
+                                                                         acc[mtx][fm][fn], 0, 0, 0);
+      }
     }
+  }
+
+  // Eight consecutive K (rows k0, k0+4's quads) of B column block starting at
+  // n for this lane, via two transposing LDS reads: rows k0..k0+3 and
+  // k0+4..k0+7 of the 4 x 16 block each 16-lane group addresses.
+  static DEV bf16x8_t read_b(const char* stage, int mtx, int n, int k0) {
+    const int c = n >> 3, half = (n >> 2) & 1;
+    bf16x4_t v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + 4 * h;
+      const LDS_AS char* p = (const LDS_AS char*)stage + A_BYTES + mtx * B_BYTES + k * 256 +
+                             ((c ^ (2 * (k & 3))) << 4) + half * 8;
+      v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)p);
+    }
+    return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
   }
 
   // Wait until at most `newer` stages of loads (those issued after the
@@ -182,7 +234,7 @@ struct Tile2 {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[m][fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int fn = 0; fn < FN; ++fn) acc[m][fm][fn] = Frag{};
     const int nk = g.K / BK;
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
@@ -202,6 +254,9 @@ struct Tile2 {
     __syncthreads();
   }
 
+  // Visit every accumulator position: fn(row, col, fm, fn, i).  16x16
+  // result: lane holds column lane%16, rows 4*(lane/16)+i.  32x32 result:
+  // column lane%32, rows 8*(i/4) + 4*(lane/32) + i%4.
   template <typename F>
   static DEV void for_each(F&& fn) {
     const int tid_ = opaque_tid();
@@ -213,9 +268,15 @@ struct Tile2 {
 #pragma unroll
       for (int fnn = 0; fnn < FN; ++fnn)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
-          const int col = wn * WTN + fnn * 16 + (lane & 15);
+        for (int i = 0; i < FRAG; ++i) {
+          int row, col;
+          if constexpr (MF == 16) {
+            row = wm * WTM + fm * 16 + (lane >> 4) * 4 + i;
+            col = wn * WTN + fnn * 16 + (lane & 15);
+          } else {
+            row = wm * WTM + fm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+            col = wn * WTN + fnn * 32 + (lane & 31);
+          }
           fn(row, col, fm, fnn, i);
         }
   }
