@@ -58,6 +58,11 @@ template <> struct ElemTraits<float> {
 // Producers therefore store that data with agent-coherent (sc1, write-
 // through) stores and drain them (vmcnt(0)) before the atomic that
 // publishes; consumers read with plain loads and need no invalidation.
+// The dependency counters and queue words themselves are relaxed atomics.
+// This holds at cache-line granularity too: every region one task writes
+// and another reads (a row block of Xp, H or y, a token tile of the routing
+// tables, a router partial tile) starts and ends on a 128-byte boundary, so
+// a reader never caches a line that a later writer still changes.
 DEV void publish_fence() {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));   // vmcnt(0): stores done
   asm volatile("" ::: "memory");
@@ -79,23 +84,14 @@ DEV void st_wt16(void* base, uint32_t byte_off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(d, r, byte_off, 0, 16 /* sc1 */);
 }
 
-DEV int ld_acquire(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
 DEV int ld_relaxed(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 DEV void st_relaxed(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-DEV void st_release(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
 DEV int add_relaxed(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-DEV int add_acqrel(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 DEV int cas_relaxed(int* p, int expected, int desired) {
   __hip_atomic_compare_exchange_strong(p, &expected, desired, __ATOMIC_RELAXED,

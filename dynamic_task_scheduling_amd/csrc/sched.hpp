@@ -2,8 +2,9 @@
 //
 // Dynamic mode (the method).  Workgroups stay resident and loop: claim a
 // ready task by an atomic increment of a queue head (xxqk.cn/news/665650
-// s2.1, fetch_task), run it, publish its results with an agent-scope
-// release, and decrement the dependency counters of its consumers; the
+// s2.1, fetch_task), run it, publish its results (write-through stores,
+// drained before the counter update; see common.hpp), and decrement the
+// dependency counters of its consumers; the
 // producer that brings a counter to zero pushes the consumers into a ready
 // queue (same page s2.3; m.xxqk.cn/news/657744 s2.3: readiness follows the
 // data, no global barrier).  A worker leaves a queue only when its claimed
@@ -128,7 +129,7 @@ DEV void push_burst(const Params& p, int q, int n, int* s_tmp, F&& id_of) {
 DEV bool arrive_last(int* c, int delta, int last_old, int* s_tmp) {
   publish_fence();
   __syncthreads();
-  if (threadIdx.x == 0) s_tmp[0] = (add_acqrel(c, delta) == last_old);
+  if (threadIdx.x == 0) s_tmp[0] = (add_relaxed(c, delta) == last_old);
   __syncthreads();
   const bool last = s_tmp[0] != 0;
   __syncthreads();
@@ -142,10 +143,10 @@ DEV bool grid_barrier(const Params& p, int& gen, int* s_tmp) {
   __syncthreads();
   if (threadIdx.x == 0) {
     int ok = 1;
-    const int arrived = add_acqrel(cw(p, CW_BAR_COUNT), 1);
+    const int arrived = add_relaxed(cw(p, CW_BAR_COUNT), 1);
     if (arrived == p.workers - 1) {
       st_relaxed(cw(p, CW_BAR_COUNT), 0);
-      st_release(cw(p, CW_BAR_GEN), gen + 1);
+      st_relaxed(cw(p, CW_BAR_GEN), gen + 1);
     } else {
       const uint64_t t0 = rtc();
       while (ld_relaxed(cw(p, CW_BAR_GEN)) == gen) {
@@ -193,14 +194,14 @@ struct Sched {
     if (threadIdx.x == 0) {
       st_relaxed(cw(p, CW_TOTAL + QM), split ? n_perm : 0);
       st_relaxed(cw(p, CW_TOTAL + QC), n_comp + (split ? 0 : n_perm));
-      st_release(cw(p, CW_SPLIT_READY), 1);
+      st_relaxed(cw(p, CW_SPLIT_READY), 1);
     }
     // position tiles go to QA
     push_burst(p, QA, p.n_rt, s_tmp, [&](int i) { return make_task(TK_POS, i); });
     // shared-expert DOWN tiles waited for the routing phase (zeroed y rows)
     const int nsm = p.n_shared * p.n_smt;
     for (int i = threadIdx.x; i < nsm; i += kThreads) {
-      if (add_acqrel(p.cnt_sdown + i, -1) == 1) {
+      if (add_relaxed(p.cnt_sdown + i, -1) == 1) {
         int* sl = nullptr;
         const int base = add_relaxed(cw(p, CW_TAIL + QC), p.n_down_n);
         if (base + p.n_down_n <= p.q_cap) sl = p.slots + (size_t)QC * p.q_cap + base;
