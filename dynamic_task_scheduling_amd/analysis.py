@@ -10,7 +10,8 @@ from typing import Dict
 import numpy as np
 
 KIND_SHIFT = 27
-KINDS = {1: "ROUTE", 2: "POS", 3: "PERM", 4: "UP", 5: "DOWN", 6: "SUP", 7: "SDOWN"}
+KINDS = {1: "ROUTE", 2: "POS", 3: "PERM", 4: "UP", 5: "DOWN", 6: "SUP", 7: "SDOWN",
+         8: "PHASE"}   # PHASE: scheduler phases (builder steps, router reduction)
 CLOCK_HZ = 100e6   # s_memrealtime rate
 
 
@@ -74,6 +75,9 @@ def schedule_stats(tr: Dict[str, np.ndarray], workers: int) -> Dict[str, float]:
     the kernel end, summed over workers."""
     if tr["t_end"].size == 0:
         return {}
+    # builder sub-step records nest inside the builder's own record
+    keep = ~((tr["kind"] == 8) & (tr["payload"] >= 2) & (tr["payload"] < 0x100))
+    tr = {k: v[keep] for k, v in tr.items()}
     t0 = int(tr["t_req"].min())
     t1 = int(tr["t_end"].max())
     span = max(1, t1 - t0)

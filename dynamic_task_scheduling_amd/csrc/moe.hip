@@ -46,6 +46,7 @@ int validate(const moe_desc* d) {
   const long long rows = (long long)d->T * d->k;
   const long long mt = rows / 128 + (e_end - d->e_begin);
   if (mt * (d->d / kBN) * 8 >= (1ll << kKindShift)) return MOE_ERR_UNSUPPORTED;
+  if (mt * 64 >= (1ll << kKindShift)) return MOE_ERR_UNSUPPORTED;  // permute payloads
   return MOE_OK;
 }
 
@@ -67,13 +68,16 @@ void make_layout(const moe_desc* d, Layout* L) {
   p.n_rt = (d->T + kTB - 1) / kTB;
   p.hist_ld = std::max(4, (p.n_rt + 3) / 4 * 4);
   // router K slices: enough router tasks to occupy the device (~256), each
-  // slice at least 512 deep, slices a divisor of d/64
+  // slice at least 256 deep, slices a divisor of d/64, and one tile's
+  // partials small enough to be staged in LDS at once by its reduction
   {
     const int ksteps = d->d / 64;
     const int want = std::max(1, (256 + std::max(p.n_rt, 1) - 1) / std::max(p.n_rt, 1));
+    const int stage = d->dtype == MOE_BF16 ? Stages<bf16_t>::kRouteStage : Stages<float>::kRouteStage;
+    const int max_rsk = std::max(1, stage / (kTB * d->E * 4));
     p.rsk = 1;
     for (int sl = 1; sl <= ksteps; ++sl)
-      if (ksteps % sl == 0 && sl <= want && d->d / sl >= 512) p.rsk = sl;
+      if (ksteps % sl == 0 && sl <= want && sl <= max_rsk && d->d / sl >= 256) p.rsk = sl;
   }
   p.n_up_n = d->f / kBN;
   p.n_down_n = d->d / kBN;
@@ -82,9 +86,16 @@ void make_layout(const moe_desc* d, Layout* L) {
   p.splitk = std::min(sk, p.n_up_n);
   p.n_s_up_n = p.fs / kBN;
   p.n_smt = (d->T + 127) / 128;
-  // rows per permute task: about 256 KB moved, a power of two in [8, 128]
+  // rows per permute task: a power of two in [2, 128] moving at most 256 KB,
+  // and small enough that a small layer's gather spreads over about two
+  // tasks per CU (32 KB minimum per task)
   int pr = 128;
-  while (pr > 8 && (long long)pr * d->d * L->esz > 262144) pr >>= 1;
+  {
+    const long long row_bytes = (long long)d->d * L->esz;
+    const long long total = (long long)d->T * d->k * row_bytes;
+    const long long target = std::max(32768ll, std::min(262144ll, total / 512));
+    while (pr > 2 && (long long)pr * row_bytes > target) pr >>= 1;
+  }
   p.perm_rows = pr;
   p.pch = 128 / pr;
   const long long R = (long long)d->T * d->k;
@@ -107,7 +118,7 @@ void make_layout(const moe_desc* d, Layout* L) {
   L->off_ctrl = take(sizeof(int) * CW_COUNT * kCtrlStride);
   L->off_slots = take(sizeof(int) * (size_t)kNumQueues * p.q_cap);
   L->off_logits = take(sizeof(float) * (size_t)d->T * d->E);
-  L->off_route_part = take(p.rsk > 1 ? sizeof(float) * (size_t)p.rsk * d->T * d->E : 0);
+  L->off_route_part = take(p.rsk > 1 ? sizeof(float) * (size_t)p.rsk * p.n_rt * kTB * d->E : 0);
   L->off_cnt_route = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
   L->off_idx = take(sizeof(int) * Tk);
   L->off_w = take(sizeof(float) * Tk);

@@ -14,8 +14,13 @@ enum TaskKind : int {
   TK_DOWN = 5,   // payload (mt * n_down_n + n) * splitk + ks: DOWN GEMM + combine
   TK_SUP = 6,    // payload (s * n_smt + m) * n_s_up_n + n: shared-expert UP
   TK_SDOWN = 7,  // payload (s * n_smt + m) * n_down_n + n: shared-expert DOWN
-  TK_BUILD = 8,  // (trace only) the post-routing task builder
+  TK_BUILD = 8,  // (trace only) scheduler phases: payload = kPhase* id
 };
+// Trace phase ids (payload of TK_BUILD records).
+constexpr int kPhaseBuild = 0;          // the whole post-routing builder
+constexpr int kPhasePublish = 1;        // publishing its tables, seeding queues
+constexpr int kPhaseBuildStep = 2;      // + s: builder step s (1..4)
+constexpr int kPhaseRouteFinish = 0x100;  // + rt: router partial reduction of tile rt
 constexpr int kKindShift = 27;
 constexpr int kPayloadMask = (1 << kKindShift) - 1;
 __host__ __device__ inline int make_task(int kind, int payload) {

@@ -43,47 +43,57 @@ DEV bool timed_out(const Params& p, uint64_t t0) {
 
 // Thread 0: claim the next slot of queue q and wait until it is filled.
 // `pend` keeps the claimed slot across calls: with `steal` set, a worker whose
-// compute-queue slot is still empty takes an already-pushed permute task
-// (non-committal compare-and-swap on the permute queue head) and comes back
-// to its own slot afterwards, so gather work never waits while compute
-// workers idle (the steal variant of the spatial split).
+// compute-queue slot is still empty takes an already-pushed permute task and
+// comes back to its own slot afterwards, so gather work never waits while
+// compute workers idle (the steal variant of the spatial split).  Steals take
+// permute slots by atomic increment, so any number of idle workers start
+// permute tasks within one memory round trip.  Every poll issues its loads
+// together (one round trip per poll, not one per load).
+DEV int wait_slot(const Params& p, const int* sl) {
+  const uint64_t t0 = rtc();
+  for (;;) {
+    const int v = ld_relaxed(sl);
+    const int err = ld_relaxed(cw(p, CW_ERROR));
+    if (v != 0) return v - 1;
+    if (err != 0) return kClaimAbort;
+    if (timed_out(p, t0)) {
+      set_error(p, 5);
+      return kClaimAbort;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 DEV int claim(const Params& p, int q, int& pend, bool steal) {
   if (pend < 0) pend = add_relaxed(cw(p, CW_HEAD + q), 1);
   const int h = pend;
+  const int* sl = p.slots + (size_t)q * p.q_cap + (h < p.q_cap ? h : 0);
   const uint64_t t0 = rtc();
   for (;;) {
+    const int v = h < p.q_cap ? ld_relaxed(sl) : 0;
     const int total = ld_relaxed(cw(p, CW_TOTAL + q));
+    const int err = ld_relaxed(cw(p, CW_ERROR));
+    int mh = 0, mt = 0;
+    if (steal) {
+      mh = ld_relaxed(cw(p, CW_HEAD + QM));
+      mt = ld_relaxed(cw(p, CW_TAIL + QM));
+    }
+    if (v != 0) {            // a filled slot is always below the total
+      pend = -1;
+      return v - 1;
+    }
     if (h >= total) {
       pend = -1;
       return kClaimExhausted;
     }
-    if (h < p.q_cap) {
-      const int v = ld_relaxed(p.slots + (size_t)q * p.q_cap + h);
-      if (v != 0) {
-        pend = -1;
-        return v - 1;
-      }
+    if (err != 0) return kClaimAbort;
+    if (steal && mh < mt) {
+      // pushed permute tasks are waiting: take one (the push is one burst,
+      // so a slot below the published total is filled now or very soon)
+      const int hm = add_relaxed(cw(p, CW_HEAD + QM), 1);
+      if (hm < ld_relaxed(cw(p, CW_TOTAL + QM)) && hm < p.q_cap)
+        return wait_slot(p, p.slots + (size_t)QM * p.q_cap + hm);
     }
-    if (steal) {
-      int* mh = cw(p, CW_HEAD + QM);
-      const int hm = ld_relaxed(mh);
-      if (hm < ld_relaxed(cw(p, CW_TAIL + QM)) && hm < p.q_cap && cas_relaxed(mh, hm, hm + 1) == hm) {
-        // a pusher reserved this slot; its store is at most a few cycles away
-        const int* sl = p.slots + (size_t)QM * p.q_cap + hm;
-        int v;
-        const uint64_t ts = rtc();
-        while ((v = ld_relaxed(sl)) == 0) {
-          if (ld_relaxed(cw(p, CW_ERROR)) != 0) return kClaimAbort;
-          if (timed_out(p, ts)) {
-            set_error(p, 5);
-            return kClaimAbort;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        return v - 1;
-      }
-    }
-    if (ld_relaxed(cw(p, CW_ERROR)) != 0) return kClaimAbort;
     if (timed_out(p, t0)) {
       set_error(p, 5 /* MOE_ERR_TIMEOUT */);
       return kClaimAbort;
@@ -179,6 +189,13 @@ DEV void trace_record(const Params& p, int task, int worker, uint64_t t_req,
   }
 }
 
+// Trace record of a scheduler phase that is not a queued task: the
+// post-routing builder and its steps, the router reduction (TK_BUILD,
+// payload = phase id).
+DEV void trace_mark(const Params& p, int phase, int worker, uint64_t t0, uint64_t t1) {
+  trace_record(p, make_task(TK_BUILD, phase), worker, t0, t0, t1);
+}
+
 template <typename Elem>
 struct Sched {
   using S = Stages<Elem>;
@@ -219,7 +236,7 @@ struct Sched {
   // *t_body receives the clock at the end of the task body, before any
   // publication, so a trace can check producer-end <= consumer-start.
   static DEV void run(const Params& p, int task, char* smem, int* s_tmp, bool dyn,
-                      uint64_t* t_body) {
+                      uint64_t* t_body, int worker) {
     const int kind = task_kind(task);
     const int pl = task_payload(task);
     *t_body = 0;
@@ -231,12 +248,18 @@ struct Sched {
         if (p.rsk > 1) {
           // the last K slice of this tile reduces the partials and routes
           if (!arrive_last(p.cnt_route + rt, -1, 1, s_tmp)) break;
+          const uint64_t tf = rtc();
           S::route_finish(p, rt, smem);
+          trace_mark(p, kPhaseRouteFinish + rt, worker, tf, rtc());
         }
         if (arrive_last(cw(p, CW_ROUTE_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
-          S::build(p, smem);
+          const uint64_t tb = rtc();
+          S::build(p, smem, worker);
           __syncthreads();
+          const uint64_t tp = rtc();
           publish_build(p, s_tmp);
+          trace_mark(p, kPhaseBuild, worker, tb, tp);
+          trace_mark(p, kPhasePublish, worker, tp, rtc());
         }
         break;
       }
@@ -353,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
     consume_fence();
     const uint64_t t_start = rtc();
     uint64_t t_body;
-    Sched<Elem>::run(p, v, smem, s_tmp, true, &t_body);
+    Sched<Elem>::run(p, v, smem, s_tmp, true, &t_body, s_worker);
     trace_record(p, v, s_worker, t_req, t_start, t_body);
   }
 }
@@ -372,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
   auto exec = [&](int task) __attribute__((always_inline)) {
     const uint64_t t0 = rtc();
     uint64_t t_body;
-    SC::run(p, task, smem, s_tmp, false, &t_body);
+    SC::run(p, task, smem, s_tmp, false, &t_body, w);
     trace_record(p, task, w, t0, t0, t_body);
   };
   // stage 1: router tiles and shared-expert UP tiles
@@ -440,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
 // ----------------------------------------------- one launch per stage
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void k_stage_route(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kRouteTile + 32 * kMaxE * 4 + kMaxE * 4];
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kRouteSmem];
   if (p.route_from_logits) {
     Stages<Elem>::topk_from_logits(p, blockIdx.x, smem);
     return;

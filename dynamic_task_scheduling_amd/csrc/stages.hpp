@@ -34,6 +34,20 @@ DEV void set_error(const Params& p, int code) {
   cas_relaxed(p.ctrl + CW_ERROR * kCtrlStride, 0, code);
 }
 
+// Thread 0 appends one trace record for a scheduler phase (see trace_mark).
+DEV void trace_step(const Params& p, int phase, int worker, uint64_t t0, uint64_t t1) {
+  if (p.trace == nullptr || threadIdx.x != 0) return;
+  const int i = add_relaxed(p.ctrl + 20 /* CW_TRACE */ * kCtrlStride, 1);
+  if (i < p.trace_cap) {
+    uint64_t* r = p.trace + (size_t)i * 4;
+    r[0] = t0;
+    r[1] = t0;
+    r[2] = t1;
+    r[3] = (uint64_t)(uint32_t)make_task(TK_BUILD, phase) | ((uint64_t)(worker & 0xffff) << 32) |
+           ((uint64_t)xcc_id() << 48);
+  }
+}
+
 // Slices of the DOWN split-K: slice ks covers UP column tiles
 // [ks*n/s, (ks+1)*n/s).
 DEV int slice_lo(int ks, int n, int s) { return ks * n / s; }
@@ -60,14 +74,15 @@ struct GemmSel<bf16_t, BM, NB> {
 };
 
 // Router tiles (32 tokens x 128 experts): a 4-stage ring for bf16 when the
-// router width is a multiple of 128, so the router scratch fits beside it.
+// router width is a multiple of 8 (columns past E are padding), so the router
+// scratch fits beside it.
 template <typename Elem>
 struct RouteSel {
   using T = Tile<Elem, 32, 1>;
 };
 template <>
 struct RouteSel<bf16_t> {
-  using T = Tile2<32, 1, 4>;
+  using T = Tile2<32, 1, 4, 32, true>;   // E may be narrower than 128
 };
 
 template <typename T>
@@ -94,7 +109,11 @@ struct Stages {
           ? Tile<Elem, 32, 1>::LDS_BYTES
           : RouteSel<Elem>::T::LDS_BYTES;
   static constexpr int kSmem = kSmemTile;
-  static_assert(kRouteTile + 32 * kMaxE * 4 + kMaxE * 4 <= kSmemTile, "route LDS");
+  // Router LDS: the tile ring, then logits [32][E], histogram [E], bias [E].
+  // route_finish stages a tile's K-slice partials over the (idle) ring.
+  static constexpr int kRouteSmem = kRouteTile + 32 * kMaxE * 4 + 2 * kMaxE * 4;
+  static constexpr int kRouteStage = kRouteTile;
+  static_assert(kRouteSmem <= kSmemTile, "route LDS");
   // build(): small tables first, then a histogram staging area
   static constexpr int kBuildScratch = 16384;
   static constexpr int kBuildStage = 65536;
@@ -102,64 +121,92 @@ struct Stages {
   static_assert(kBuildSmem <= kSmemTile, "build LDS");
 
   // --------------------------------------------------------------- router
-  // Top-k with renormalised softmax for `rows` tokens starting at t0, whose
-  // fp32 logits sit at L[row * ldl + e] (LDS or global).  One wave per token;
-  // each lane holds experts lane, lane+64, lane+128, lane+192.  Selection
+  // Top-k with renormalised softmax for `rows` (<= 32) tokens starting at t0,
+  // whose fp32 logits sit at L[row * ldl + e] (LDS or global).
+  //
+  // Token-parallel: a wave takes 8 tokens, 8 lanes per token.  Lane g of a
+  // token keeps, in registers, the 8 largest keys among experts g, g+8,
+  // g+16, ... (an insertion network, so every lane works on its own token at
+  // once); then k merge rounds each take the largest head among the token's
+  // 8 lanes (three DPP steps inside the 8-lane group) and pop it.  Selection
   // key = (order-preserving logit image, inverted index): the maximum is the
-  // largest logit, and among equal logits the lowest index.
+  // largest logit and, among equal logits, the lowest index.  Round j's
+  // winner is kept by lane j of the group, so the weights, the table stores
+  // and the histogram update are one instruction per wave.
+  static DEV uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+  template <int CTRL>
+  static DEV uint64_t dpp_u64(uint64_t x) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(x >> 32), CTRL, 0xf, 0xf, false);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+  }
+  template <int CTRL>
+  static DEV float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+  }
+  // 0xb1: quad_perm [1,0,3,2]; 0x4e: quad_perm [2,3,0,1]; 0x141: row_half_mirror
+  // (lane i <-> 7-i inside each 8-lane half row).  Together: every lane of an
+  // aligned 8-lane group sees the whole group.
+  static DEV uint64_t group8_max(uint64_t x) {
+    x = max_u64(x, dpp_u64<0xb1>(x));
+    x = max_u64(x, dpp_u64<0x4e>(x));
+    return max_u64(x, dpp_u64<0x141>(x));
+  }
+  static DEV float group8_sum(float x) {
+    x += dpp_f32<0xb1>(x);
+    x += dpp_f32<0x4e>(x);
+    return x + dpp_f32<0x141>(x);
+  }
+
   static DEV void topk(const Params& p, int t0, int rows, const float* L, int ldl,
                        int* hist_s) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    static_assert(kTB == 32 && kThreads == 256 && kMaxK <= 8, "8 lanes per token");
+    const int tid = threadIdx.x;
+    const int g = tid & 7;                  // lane within the token's group
+    const int r = tid >> 3;                 // token row in the tile (0..31)
     const int E = p.E, k = p.k;
-    for (int r = wave; r < rows; r += 4) {
-      uint64_t key[4];
-      bool bad = false;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q;
-        if (e < E) {
-          const float v = L[r * ldl + e];
-          if (!__builtin_isfinite(v)) bad = true;
-          const uint32_t m = __builtin_isfinite(v) ? mono_key(v) : 1u;
-          key[q] = ((uint64_t)m << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
-        } else {
-          key[q] = 0;
-        }
+    const bool live = r < rows;
+    // 1. per lane: the 8 largest keys of its experts, sorted descending
+    uint64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, s4 = 0, s5 = 0, s6 = 0, s7 = 0;
+    bool bad = false;
+    if (live) {
+      for (int e = g; e < E; e += 8) {
+        const float v = L[r * ldl + e];
+        if (!__builtin_isfinite(v)) bad = true;
+        const uint32_t m = __builtin_isfinite(v) ? mono_key(v) : 1u;
+        uint64_t x = ((uint64_t)m << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+        auto cs = [&](uint64_t& s) __attribute__((always_inline)) {
+          const uint64_t hi = max_u64(s, x);
+          x = (s > x) ? x : s;
+          s = hi;
+        };
+        cs(s0); cs(s1); cs(s2); cs(s3); cs(s4); cs(s5); cs(s6); cs(s7);
       }
-      if (__any(bad) && lane == 0) set_error(p, 7 /* MOE_ERR_NONFINITE */);
-      int sel_e[kMaxK];
-      float sel_v[kMaxK];
-      for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          const uint32_t hi = __shfl_xor((int)(best >> 32), off);
-          const uint32_t lo = __shfl_xor((int)(uint32_t)best, off);
-          const uint64_t o = ((uint64_t)hi << 32) | lo;
-          best = o > best ? o : best;
-        }
-        const int e = (int)(0xffffffffu - (uint32_t)best);
-        sel_e[j] = e;
-        sel_v[j] = mono_value((uint32_t)(best >> 32));
-        if ((e & 63) == lane) key[e >> 6] = 0;
+    }
+    if (__any(bad) && (tid & 63) == 0) set_error(p, 7 /* MOE_ERR_NONFINITE */);
+    // 2. k merge rounds over the group's heads
+    uint64_t mine = 0;       // winner of round g (lanes g < k)
+    uint64_t first = 0;      // winner of round 0 (largest logit)
+    for (int j = 0; j < k; ++j) {
+      const uint64_t w = group8_max(s0);
+      if (j == 0) first = w;
+      if (g == j) mine = w;
+      if (s0 == w) {         // keys are unique: exactly one lane pops
+        s0 = s1; s1 = s2; s2 = s3; s3 = s4; s4 = s5; s5 = s6; s6 = s7; s7 = 0;
       }
-      if (lane == 0) {
-        const int t = t0 + r;
-        float a[kMaxK];
-        float s = 0.f;
-        for (int j = 0; j < k; ++j) {
-          a[j] = expf(sel_v[j] - sel_v[0]);
-          s += a[j];
-        }
-        for (int j = 0; j < k; ++j) {
-          st_wt(p.idx + (size_t)t * k + j, sel_e[j]);
-          st_wt(p.w + (size_t)t * k + j, a[j] / s);
-          const int el = sel_e[j] - p.e_begin;
-          if (el >= 0 && el < p.E_loc) atomicAdd(&hist_s[el], 1);
-        }
-      }
+    }
+    // 3. w_j = exp(L_j - L_0) / sum_j' exp(L_j' - L_0)
+    const int my_e = (int)(0xffffffffu - (uint32_t)mine);
+    const float my_v = mono_value((uint32_t)(mine >> 32));
+    const float v0 = mono_value((uint32_t)(first >> 32));
+    const float a = (g < k) ? expf(my_v - v0) : 0.f;
+    const float s = group8_sum(a);
+    if (live && g < k) {
+      const int t = t0 + r;
+      st_wt(p.idx + (size_t)t * k + g, my_e);
+      st_wt(p.w + (size_t)t * k + g, a / s);
+      const int el = my_e - p.e_begin;
+      if (el >= 0 && el < p.E_loc) atomicAdd(&hist_s[el], 1);
     }
   }
 
@@ -187,6 +234,7 @@ struct Stages {
       g.B[0] = wr + n0;
       g.ldb = p.E;
       if constexpr (requires_n_valid<RT>::value) g.n_valid = min(kBN, p.E - n0);
+      else g.b_cols = min(kBN, p.E - n0);
       g.K = K;
       typename RT::Acc acc;
       if constexpr (requires_n_valid<RT>::value) RT::run(g, reinterpret_cast<Elem*>(smem), acc);
@@ -196,7 +244,7 @@ struct Stages {
         if (e < p.E) {
           const float v = acc[0][fm][fn][i];
           if (part) {
-            if (row < rows) st_wt(part + (size_t)(t0 + row) * p.E + e, v);
+            if (row < rows) st_wt(part + row * p.E + e, v);
           } else {
             Ls[row * p.E + e] = v;
           }
@@ -205,9 +253,18 @@ struct Stages {
     }
   }
 
+  // Router partials: slice ks of tile rt is a contiguous [32][E] fp32 block
+  // at ((rt * rsk + ks) * 32) * E, so one tile's slices form one contiguous
+  // range that route_finish pulls into LDS with a single burst of loads.
+  static DEV float* route_part_block(const Params& p, int rt, int ks) {
+    return p.route_part + ((size_t)rt * p.rsk + ks) * kTB * p.E;
+  }
+
   static TASKFN void route(const Params& p, int rt, int ks, char* smem) {
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
+    // the bias load is issued first, so its latency hides under the GEMM
+    const float bias_v = (p.rsk == 1 && p.bias && (int)threadIdx.x < p.E) ? p.bias[threadIdx.x] : 0.f;
     if (ks == 0) {
       for (int r = 0; r < rows; ++r) {
         float* yr = p.y + (size_t)(t0 + r) * p.d;
@@ -216,38 +273,64 @@ struct Stages {
     }
     const int Ks = p.d / p.rsk;
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);     // [32][E]
-    float* part = p.rsk > 1 ? p.route_part + (size_t)ks * p.T * p.E : nullptr;
-    if (ElemTraits<Elem>::kBf16 && (p.E % kBN) == 0)
+    float* part = p.rsk > 1 ? route_part_block(p, rt, ks) : nullptr;
+    if (ElemTraits<Elem>::kBf16 && (p.E % 8) == 0)
       route_gemm<typename RouteSel<Elem>::T>(p, t0, rows, ks * Ks, Ks, Ls, part, smem);
     else
       route_gemm<Tile<Elem, 32, 1>>(p, t0, rows, ks * Ks, Ks, Ls, part, smem);
-    if (p.rsk == 1) route_topk(p, rt, smem, false);
+    if (p.rsk == 1) {
+      float* bias_s = reinterpret_cast<float*>(smem + kRouteTile + 32 * kMaxE * 4 + kMaxE * 4);
+      if ((int)threadIdx.x < p.E) bias_s[threadIdx.x] = bias_v;
+      route_topk(p, rt, smem);
+    }
   }
 
-  // Sum the K-slice partials of tile rt in slice order, then top-k.
+  // Sum the K-slice partials of tile rt in slice order, then top-k.  Every
+  // partial of the tile is loaded into LDS by one burst of direct
+  // global->LDS loads (one memory round trip), and the bias with them.
   static TASKFN void route_finish(const Params& p, int rt, char* smem) {
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
-    for (int i = threadIdx.x; i < rows * p.E; i += kThreads) {
+    float* bias_s = reinterpret_cast<float*>(smem + kRouteTile + 32 * kMaxE * 4 + kMaxE * 4);
+    const float bias_v = (p.bias && (int)threadIdx.x < p.E) ? p.bias[threadIdx.x] : 0.f;
+    const int tid = opaque_tid();
+    const int wave = tid >> 6, lane = tid & 63;
+    const int bytes = p.rsk * kTB * p.E * 4;            // <= kRouteStage (host-checked)
+    const char* src = reinterpret_cast<const char*>(route_part_block(p, rt, 0));
+    const int n_inst = (bytes + 1023) / 1024;
+    for (int j = wave; j < n_inst; j += 4) {
+      int off = j * 1024 + lane * 16;
+      if (off >= bytes) off = 0;                        // tail lanes: stay inside the block
+      dma16(src + off, __builtin_amdgcn_readfirstlane(lds_addr(smem + j * 1024)));
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    const float* st = reinterpret_cast<const float*>(smem);
+    const int n = rows * p.E;
+    const int blk = kTB * p.E;
+    for (int i = threadIdx.x; i < n; i += kThreads) {
       float v = 0.f;
-      for (int ks = 0; ks < p.rsk; ++ks) v += p.route_part[((size_t)ks * p.T + t0) * p.E + i];
+      for (int ks = 0; ks < p.rsk; ++ks) v += st[ks * blk + i];
       Ls[i] = v;
     }
-    route_topk(p, rt, smem, true);
+    if ((int)threadIdx.x < p.E) bias_s[threadIdx.x] = bias_v;
+    __syncthreads();
+    route_topk(p, rt, smem);
   }
 
-  // Bias, exported logits, top-k and the tile histogram from Ls.
-  static DEV void route_topk(const Params& p, int rt, char* smem, bool synced) {
+  // Bias, exported logits, top-k and the tile histogram from Ls (the bias
+  // already staged in LDS).
+  static DEV void route_topk(const Params& p, int rt, char* smem) {
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
     int* hist_s = reinterpret_cast<int*>(smem + kRouteTile + 32 * kMaxE * 4);
+    const float* bias_s = reinterpret_cast<const float*>(hist_s + kMaxE);
     for (int e = threadIdx.x; e < p.E_loc; e += kThreads) hist_s[e] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < rows * p.E; i += kThreads) {
-      const int e = i % p.E;
-      const float v = Ls[i] + (p.bias ? p.bias[e] : 0.f);
+      const float v = Ls[i] + bias_s[i % p.E];
       Ls[i] = v;
       p.logits[(size_t)t0 * p.E + i] = v;
     }
@@ -255,7 +338,6 @@ struct Stages {
     topk(p, t0, rows, Ls, p.E, hist_s);
     __syncthreads();
     write_hist(p, rt, hist_s);
-    (void)synced;
   }
 
   // Routing from given logits (checking path): top-k + histogram only.
@@ -271,210 +353,285 @@ struct Stages {
   }
 
   // ---------------------------------------------------------------- build
+  // Workgroup-wide exclusive prefix sum of one int per thread; returns the
+  // thread's exclusive prefix, *total receives the sum.  s_w: 4 ints of LDS.
+  static DEV int block_exscan(int v, int* s_w, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o);
+      if (lane >= o) inc += u;
+    }
+    if (lane == 63) s_w[wave] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int s = s_w[w];
+      base += (w < wave) ? s : 0;
+      tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + inc - v;
+  }
+
+  // Workgroup-wide float sum in a fixed order (deterministic).
+  static DEV float block_sum(float v, float* s_w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) s_w[wave] = v;
+    __syncthreads();
+    const float t = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+    __syncthreads();
+    return t;
+  }
+
   // Runs once, after every ROUTE tile: counts, offsets, per-tile position
   // bases, expert order (most loaded first), the row-tile table, dependency
   // counters, the permute list and -- the cost model -- the worker split.
   // The pages run this "once routing completes", when every layer's
   // communication and computation volumes are known (Weave abstract).
-  // Returns nothing; writes tables and control words (not yet published).
-  static TASKFN void build(const Params& p, char* smem) {
-    int* s_cnt = reinterpret_cast<int*>(smem);            // [256]
-    int* s_off = s_cnt + 256;                             // [257]
-    int* s_rank = s_off + 257;                            // [256] rank of expert e
-    int* s_ord = s_rank + 256;                            // [256] expert of rank r
-    int* s_nt = s_ord + 256;                              // [256] tiles of rank r
-    int* s_np = s_nt + 256;                               // [256] permute tasks of rank r
-    int* s_mtb = s_np + 256;                              // [257] tile base of rank r
+  // Global memory costs about a microsecond per round trip, so every step
+  // issues its loads together and spreads its stores over all threads; the
+  // scans and reductions run in LDS and registers.
+  // Writes tables and control words (not yet published).
+  static TASKFN void build(const Params& p, char* smem, int worker = 0) {
+    uint64_t t_step = rtc();
+    auto mark = [&](int step) __attribute__((always_inline)) {
+      if (p.flags & 0x2 /* trace */) {
+        const uint64_t t = rtc();
+        trace_step(p, kPhaseBuildStep + step, worker, t_step, t);
+        t_step = t;
+      }
+    };
+    int* s_cnt = reinterpret_cast<int*>(smem);            // [256] count of expert e
+    int* s_off = s_cnt + 256;                             // [257] offset of expert e
+    int* s_ord = s_off + 257;                             // [256] expert of rank r
+    int* s_mtb = s_ord + 256;                             // [257] tile base of rank r
     int* s_pb = s_mtb + 257;                              // [257] permute base of rank r
-    float* s_cost = reinterpret_cast<float*>(s_pb + 257); // [256] compute seconds of rank r
-    float* s_red = s_cost + 256;                          // [kThreads] reduction
-    int* s_wm = reinterpret_cast<int*>(s_red + kThreads); // [kThreads]
+    int* s_w = s_pb + 257;                                // [8] scan / reduction scratch
+    float* s_wf = reinterpret_cast<float*>(s_w + 4);
+    int* s_h = reinterpret_cast<int*>(smem + kBuildScratch);   // histogram staging
     const int tid = threadIdx.x;
     const int El = p.E_loc;
-    // 1. per-expert counts and per-tile exclusive bases.  The histogram is
-    //    staged through LDS in column chunks so its loads are all in flight
-    //    at once (one row per thread would be a chain of dependent loads).
+    // 1. per-expert counts and per-tile exclusive bases, in column chunks of
+    //    the [El][n_rt] histogram (row stride cwp = cw + 1: the per-expert
+    //    scan reads a column per wave without bank conflicts).
+    int run = 0;
     {
-      int* s_h = reinterpret_cast<int*>(smem + kBuildScratch);
-      const int C = max(4, min(p.hist_ld, (kBuildStage / 4 / max(El, 1)) & ~3));
-      int run = 0;
+      const int C = max(4, min(p.hist_ld, ((kBuildStage / 4) / max(El, 1) - 1) & ~3));
       for (int r0 = 0; r0 < p.n_rt; r0 += C) {
         const int cw = min(C, p.hist_ld - r0);
+        const int cwp = cw + 1;
         const int q4 = cw / 4;
-        for (int i = tid; i < El * q4; i += kThreads) {
-          const int e = i / q4, q = i % q4;
-          *reinterpret_cast<int4*>(s_h + e * cw + q * 4) =
-              *reinterpret_cast<const int4*>(p.hist + (size_t)e * p.hist_ld + r0 + q * 4);
-        }
-        __syncthreads();
-        if (tid < El) {
-          int* b = p.rt_base + (size_t)tid * p.hist_ld + r0;
-          const int nr = min(cw, p.n_rt - r0);
-          for (int r = 0; r < nr; ++r) {
-            const int v = s_h[tid * cw + r];
-            st_wt(b + r, run);
-            run += v;
+        const int nq = El * q4;
+        // all loads of the chunk in flight, then into LDS
+        for (int i0 = tid; i0 < nq; i0 += 8 * kThreads) {
+          int4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kThreads;
+            if (i < nq)
+              v[u] = *reinterpret_cast<const int4*>(p.hist + (size_t)(i / q4) * p.hist_ld + r0 +
+                                                   (i % q4) * 4);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kThreads;
+            if (i < nq) {
+              int* d = s_h + (i / q4) * cwp + (i % q4) * 4;
+              d[0] = v[u].x; d[1] = v[u].y; d[2] = v[u].z; d[3] = v[u].w;
+            }
           }
         }
         __syncthreads();
+        const int nr = min(cw, p.n_rt - r0);
+        if (tid < El) {
+          int* row = s_h + tid * cwp;
+          for (int r = 0; r < nr; r += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = (r + u < nr) ? row[r + u] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              if (r + u < nr) row[r + u] = run;
+              run += v[u];
+            }
+          }
+        }
+        __syncthreads();
+        // exclusive bases out, spread over every thread
+        const int n = El * nr;
+        for (int i = tid; i < n; i += kThreads) {
+          const int e = i / nr, r = i % nr;
+          st_wt(p.rt_base + (size_t)e * p.hist_ld + r0 + r, s_h[e * cwp + r]);
+        }
+        __syncthreads();
       }
-      if (tid < El) {
-        s_cnt[tid] = run;
-        st_wt(p.counts + tid, run);
-      }
+    }
+    // 2. offsets (exclusive scan) and expert order by descending count
+    if (tid < El) s_cnt[tid] = run;
+    int total = 0;
+    const int off = block_exscan(tid < El ? run : 0, s_w, &total);
+    if (tid < El) {
+      s_off[tid] = off;
+      st_wt(p.counts + tid, run);
+      st_wt(p.offsets + tid, off);
+    }
+    if (tid == 0) {
+      s_off[El] = total;
+      st_wt(p.offsets + El, total);
     }
     __syncthreads();
-    // 2. offsets (exclusive scan) and expert order by descending count
-    if (tid == 0) {
-      int run = 0;
-      for (int e = 0; e < El; ++e) { s_off[e] = run; run += s_cnt[e]; }
-      s_off[El] = run;
-    }
     if (tid < El) {
-      const int c = s_cnt[tid];
+      const int c = run;
       int rank = 0;
       for (int e = 0; e < El; ++e) {
         const int ce = s_cnt[e];
         rank += (ce > c) || (ce == c && e < tid);
       }
-      s_rank[tid] = rank;
       s_ord[rank] = tid;
+      st_wt(p.eorder + rank, tid);
     }
     __syncthreads();
-    for (int e = tid; e <= El; e += kThreads) st_wt(p.offsets + e, s_off[e]);
+    mark(1);
     // 3. row tiles (128 rows; the last one of an expert takes the smallest
-    //    class that holds it) and permute chunks, per rank
+    //    class that holds it) and permute chunks, per rank; then the table,
+    //    filled by every thread in parallel (one tile per thread per pass)
     const float esz = TR::kBf16 ? 2.f : 4.f;
+    int nt = 0, np = 0;
+    float cost = 0.f;
     if (tid < El) {
-      const int e = s_ord[tid];
-      st_wt(p.eorder + tid, e);
-      const int c = s_cnt[e];
-      const int nt = (c + 127) / 128;
-      int np = 0;
-      float cost = 0.f;
-      for (int m = 0; m < nt; ++m) {
-        const int rows = min(128, c - 128 * m);
-        np += (rows + p.perm_rows - 1) / p.perm_rows;
-        const int bm = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
-        // padded MFMA flops vs streamed weight bytes of this tile's GEMMs
-        const float fl = 6.f * bm * (float)p.d * (float)p.f;
+      const int c = s_cnt[s_ord[tid]];
+      nt = (c + 127) / 128;
+      if (nt > 0) {
+        const int last = c - 128 * (nt - 1);
+        np = (nt - 1) * p.pch + (last + p.perm_rows - 1) / p.perm_rows;
+        // one worker's time for a tile: its MFMA work (padded rows), or its
+        // share of HBM bandwidth for the tile's weights
         const float by = 3.f * esz * (float)p.d * (float)p.f;
-        // one worker's time: its MFMA work, or its share of HBM bandwidth
-        cost += fmaxf(fl / p.cm_mfma_rate, by * (float)p.workers / p.cm_hbm_bw);
+        auto tile_cost = [&](int bm) {
+          const float fl = 6.f * bm * (float)p.d * (float)p.f;
+          return fmaxf(fl / p.cm_mfma_rate, by * (float)p.workers / p.cm_hbm_bw);
+        };
+        const int bml = last <= 32 ? 32 : last <= 64 ? 64 : 128;
+        cost = (float)(nt - 1) * tile_cost(128) + tile_cost(bml);
       }
-      s_nt[tid] = nt;
-      s_np[tid] = np;
-      s_cost[tid] = cost;
     }
-    __syncthreads();
+    int n_mt = 0, n_perm = 0;
+    const int mtb = block_exscan(nt, s_w, &n_mt);
+    const int pb = block_exscan(np, s_w, &n_perm);
+    if (tid < El) {
+      s_mtb[tid] = mtb;
+      s_pb[tid] = pb;
+    }
     if (tid == 0) {
-      int a = 0, b = 0;
-      for (int r = 0; r < El; ++r) {
-        s_mtb[r] = a; a += s_nt[r];
-        s_pb[r] = b; b += s_np[r];
-      }
-      s_mtb[El] = a;
-      s_pb[El] = b;
+      s_mtb[El] = n_mt;
+      s_pb[El] = n_perm;
     }
-    __syncthreads();
-    const int n_mt = s_mtb[El];
-    const int n_perm = s_pb[El];
+    const float tot_cost = block_sum(cost, s_wf);
     if (n_mt > p.max_mt || n_perm > p.max_perm) {
       if (tid == 0) set_error(p, 6 /* MOE_ERR_CAPACITY */);
       return;
     }
-    if (tid < El) {
-      const int e = s_ord[tid];
-      const int c = s_cnt[e];
-      int mt = s_mtb[tid];
-      int pb = s_pb[tid];
-      for (int m = 0; m < s_nt[tid]; ++m, ++mt) {
-        const int rows = min(128, c - 128 * m);
-        MTile t;
-        t.e = e;
-        t.row0 = s_off[e] + 128 * m;
-        t.rows = rows;
-        t.bm = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
-        int* tw = reinterpret_cast<int*>(p.mtiles + mt);
-        st_wt(tw + 0, t.e);
-        st_wt(tw + 1, t.row0);
-        st_wt(tw + 2, t.rows);
-        st_wt(tw + 3, t.bm);
-        const int np = (rows + p.perm_rows - 1) / p.perm_rows;
-        st_wt(p.cnt_perm + mt, np);
-        for (int ks = 0; ks < p.splitk; ++ks)
-          st_wt(p.cnt_down + mt * p.splitk + ks,
-                slice_lo(ks + 1, p.n_up_n, p.splitk) - slice_lo(ks, p.n_up_n, p.splitk));
-        for (int c2 = 0; c2 < np; ++c2) st_wt(p.perm_list + pb++, make_task(TK_PERM, mt * p.pch + c2));
+    for (int mt = tid; mt < n_mt; mt += kThreads) {
+      // rank of this tile: the last rank whose tile base is <= mt (ranks
+      // with no rows sort last, so they never match a real tile)
+      int lo = 0, hi = El - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_mtb[mid] <= mt) lo = mid;
+        else hi = mid - 1;
       }
+      const int r = lo;
+      const int e = s_ord[r];
+      const int m = mt - s_mtb[r];
+      const int rows = min(128, s_cnt[e] - 128 * m);
+      const int bm = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
+      static_assert(sizeof(MTile) == 16, "MTile is one 16-byte store");
+      st_wt16(p.mtiles, (uint32_t)mt * 16u,
+              make_uint4((unsigned)e, (unsigned)(s_off[e] + 128 * m), (unsigned)rows, (unsigned)bm));
+      const int npt = (rows + p.perm_rows - 1) / p.perm_rows;
+      st_wt(p.cnt_perm + mt, npt);
+      for (int ks = 0; ks < p.splitk; ++ks)
+        st_wt(p.cnt_down + mt * p.splitk + ks,
+              slice_lo(ks + 1, p.n_up_n, p.splitk) - slice_lo(ks, p.n_up_n, p.splitk));
+      const int pbase = s_pb[r] + m * p.pch;
+      for (int c2 = 0; c2 < npt; ++c2) st_wt(p.perm_list + pbase + c2, make_task(TK_PERM, mt * p.pch + c2));
     }
-    // 4. spatial split: smallest memory group whose gather finishes within
-    //    `slack` x the compute group's time (cost model, per layer).
-    float tot_cost = 0.f;
-    if (tid == 0)
-      for (int r = 0; r < El; ++r) tot_cost += s_cost[r];
-    if (tid == 0) s_red[0] = tot_cost;
-    __syncthreads();
-    tot_cost = s_red[0];
-    __syncthreads();
-    const int W = p.workers;
-    int wm_choice = 0;
-    if (p.split_policy == 0 /* cost model */ && W >= 2) {
-      const float R = (float)s_off[El];
-      const float bytes = 2.f * R * (float)p.d * esz;
-      int best = W - 1;
-      for (int wm = 1 + tid; wm < W; wm += kThreads) {
-        const float tm = bytes / fminf((float)wm * p.cm_cu_bw, p.cm_hbm_bw);
-        const float tc = tot_cost / (float)(W - wm);
-        if (tm <= p.cm_slack * tc) { best = wm; break; }
-      }
-      s_wm[tid] = best;
-      __syncthreads();
-      if (tid == 0) {
-        int b = W - 1;
-        for (int i = 0; i < kThreads; ++i) b = min(b, s_wm[i]);
-        s_wm[0] = b;
-      }
-      __syncthreads();
-      wm_choice = s_wm[0];
-    } else if (p.split_policy == 1 /* fixed */) {
-      wm_choice = p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8;
-    }
-    // with a split, at least one worker drains the permute queue
-    if (p.split_policy != 2) wm_choice = max(1, wm_choice);
+    mark(3);
+    // 4. spatial split: the smallest memory group whose gather finishes
+    //    within `slack` x the compute group's time (cost model, per layer).
+    //    The gather time falls and the compute time rises with the memory
+    //    group's size, so the first size that passes is found by bisection.
     if (tid == 0) {
+      const int W = p.workers;
+      int wm_choice = 0;
+      if (p.split_policy == 0 /* cost model */ && W >= 2) {
+        const float bytes = 2.f * (float)total * (float)p.d * esz;
+        auto ok = [&](int wm) {
+          const float tm = bytes / fminf((float)wm * p.cm_cu_bw, p.cm_hbm_bw);
+          const float tc = tot_cost / (float)(W - wm);
+          return tm <= p.cm_slack * tc;
+        };
+        int lo = 1, hi = W - 1;        // answer in [lo, hi]; hi if none passes
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (ok(mid)) hi = mid;
+          else lo = mid + 1;
+        }
+        wm_choice = lo;
+      } else if (p.split_policy == 1 /* fixed */) {
+        wm_choice = p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8;
+      }
+      // with a split, at least one worker drains the permute queue
+      if (p.split_policy != 2) wm_choice = max(1, wm_choice);
       int* cw = p.ctrl;
       st_relaxed(cw + CW_NMT * kCtrlStride, n_mt);
       st_relaxed(cw + CW_NPERM * kCtrlStride, n_perm);
       st_relaxed(cw + CW_WMEM * kCtrlStride, wm_choice);
     }
+    mark(4);
   }
 
   // POS(rt): rows of this tile's kept slots, ascending (token, slot) order
   // inside every expert: row = offsets[e] + rt_base[e][rt] + rank in tile.
+  // One thread per slot (32 tokens x k <= 256 slots): its rank is the number
+  // of earlier slots of the tile with the same expert.
   static TASKFN void position(const Params& p, int rt, char* smem) {
+    static_assert(kTB * kMaxK <= kThreads, "one thread per slot");
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     const int k = p.k;
-    int* s_idx = reinterpret_cast<int*>(smem);             // [32*k]
-    float* s_w = reinterpret_cast<float*>(s_idx + kTB * kMaxK);
     const int ns = rows * k;
-    for (int i = threadIdx.x; i < ns; i += kThreads) {
-      const int e = p.idx[(size_t)t0 * k + i];
-      s_idx[i] = e - p.e_begin;
-      s_w[i] = p.w[(size_t)t0 * k + i];
-      if (e < p.e_begin || e - p.e_begin >= p.E_loc) st_wt(p.slot_pos + (size_t)t0 * k + i, -1);
+    int* s_e = reinterpret_cast<int*>(smem);             // [256]
+    const int i = threadIdx.x;
+    int e = -1;
+    float w = 0.f;
+    if (i < ns) {
+      e = p.idx[(size_t)t0 * k + i] - p.e_begin;
+      w = p.w[(size_t)t0 * k + i];
+      if (e >= p.E_loc) e = -1;
+      if (e < 0) e = -1;
     }
+    s_e[i] = e;
+    // this slot's segment base, loaded while the ranks are counted
+    int base = 0;
+    if (e >= 0) base = p.offsets[e] + p.rt_base[(size_t)e * p.hist_ld + rt];
     __syncthreads();
-    for (int e = threadIdx.x; e < p.E_loc; e += kThreads) {
-      int pos = p.offsets[e] + p.rt_base[(size_t)e * p.hist_ld + rt];
-      for (int i = 0; i < ns; ++i) {
-        if (s_idx[i] == e) {
-          st_wt(p.perm + pos, t0 + i / k);
-          st_wt(p.rw + pos, s_w[i]);
-          st_wt(p.slot_pos + (size_t)t0 * k + i, pos);
-          ++pos;
-        }
+    if (i < ns) {
+      if (e < 0) {
+        st_wt(p.slot_pos + (size_t)t0 * k + i, -1);
+      } else {
+        int rank = 0;
+        for (int j = 0; j < i; ++j) rank += (s_e[j] == e);
+        const int pos = base + rank;
+        st_wt(p.perm + pos, t0 + i / k);
+        st_wt(p.rw + pos, w);
+        st_wt(p.slot_pos + (size_t)t0 * k + i, pos);
       }
     }
     __syncthreads();
@@ -482,10 +639,15 @@ struct Stages {
 
   // PERM(mt, c): Xp[r] = x[perm[r]] for rows chunk c of tile mt (16-byte
   // coalesced copies; the local stand-in for expert-parallel dispatch).
+  // The chunk's token ids go to LDS first, so every row load of a batch is
+  // issued together (one round trip per 64 KB batch).
   static TASKFN void permute(const Params& p, int mt, int c) {
+    __shared__ int s_tok[128];
     const MTile t = p.mtiles[mt];
     const int r0 = t.row0 + c * p.perm_rows;
     const int r1 = min(t.row0 + t.rows, r0 + p.perm_rows);
+    if ((int)threadIdx.x < r1 - r0) s_tok[threadIdx.x] = p.perm[r0 + threadIdx.x];
+    __syncthreads();
     const int cpr = p.d * (int)sizeof(Elem) / 16;           // 16-byte chunks per row
     const int total = (r1 - r0) * cpr;
     const uint4* x = reinterpret_cast<const uint4*>(p.x);
@@ -494,26 +656,20 @@ struct Stages {
     // 16 loads in flight per thread (64 KB per workgroup): a gather is a
     // latency-bound copy, so bytes in flight set its rate.
     constexpr int U = 16;
-    int i = threadIdx.x;
-    for (; i + (U - 1) * kThreads < total; i += U * kThreads) {
+    for (int i0 = threadIdx.x; i0 < total; i0 += U * kThreads) {
       uint4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int ii = i + u * kThreads;
-        const int r = r0 + ii / cpr, cc = ii % cpr;
-        v[u] = x[(size_t)p.perm[r] * cpr + cc];
+        const int ii = i0 + u * kThreads;
+        if (ii < total) v[u] = x[(size_t)s_tok[ii / cpr] * cpr + ii % cpr];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int ii = i + u * kThreads;
-        const int r = r0 + ii / cpr, cc = ii % cpr;
-        st_wt16(xp + (size_t)r * row_bytes, cc * 16, v[u]);
+        const int ii = i0 + u * kThreads;
+        if (ii < total) st_wt16(xp + (size_t)(r0 + ii / cpr) * row_bytes, (ii % cpr) * 16, v[u]);
       }
     }
-    for (; i < total; i += kThreads) {
-      const int r = r0 + i / cpr, cc = i % cpr;
-      st_wt16(xp + (size_t)r * row_bytes, cc * 16, x[(size_t)p.perm[r] * cpr + cc]);
-    }
+    __syncthreads();
   }
 
   // ------------------------------------------------------------- GEMM tasks

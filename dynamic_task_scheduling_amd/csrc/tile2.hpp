@@ -67,7 +67,11 @@ DEV uint32_t lds_addr(const void* p) {
 // v_mfma_f32_32x32x16_bf16.  The 32x32 form keeps the matrix pipe far busier
 // with one wave per SIMD (measured 2.1 vs 1.35 PFLOP/s on gfx950) and halves
 // LDS fragment traffic per flop.
-template <int BM, int NB, int S, int MF = 32>
+// CLAMP_B: B has only `b_cols` valid columns (a multiple of 8, row stride
+// ldb >= b_cols); 16-byte chunks past them reload chunk 0 of the same row, so
+// every load stays inside B and only the (discarded) padded output columns
+// see duplicated values.  Used by the router, whose width E may be < 128.
+template <int BM, int NB, int S, int MF = 32, bool CLAMP_B = false>
 struct Tile2 {
   static constexpr int BN = kBN;
   static constexpr int BK = 64;
@@ -101,6 +105,7 @@ struct Tile2 {
     const bf16_t* B[NB];  // K row 0, column n0 of the tile
     int ldb;
     int K;              // multiple of 64
+    int b_cols;         // CLAMP_B only: valid columns of B (multiple of 8)
   };
 
   static DEV void issue(const Args& g, int kt, char* stage) {
@@ -122,7 +127,8 @@ struct Tile2 {
       for (int ii = 0; ii < B_INST; ++ii) {
         const int i = wave * B_INST + ii;          // K rows 4i .. 4i+3
         const int k = 4 * i + (lane >> 4);
-        const int c = (lane & 15) ^ (2 * (k & 3));
+        int c = (lane & 15) ^ (2 * (k & 3));
+        if constexpr (CLAMP_B) c = (c * 8 < g.b_cols) ? c : 0;
         const bf16_t* src = g.B[mtx] + (size_t)(k0 + k) * g.ldb + c * 8;
         dma16(src, __builtin_amdgcn_readfirstlane(
                        lds_addr(stage + A_BYTES + mtx * B_BYTES + i * 1024)));
