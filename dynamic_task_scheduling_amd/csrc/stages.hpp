@@ -219,8 +219,8 @@ struct Stages {
   // ks of rsk.  With rsk == 1 the task also adds the bias, picks the top-k
   // and writes the tile histogram; with rsk > 1 it writes an fp32 partial
   // and the last slice to finish runs route_finish (fixed-order sum, so the
-  // logits do not depend on which slice finished last).  Slice 0 zeroes the
-  // tile's y rows, which the combine later accumulates into.
+  // logits do not depend on which slice finished last).  The slices share the
+  // zeroing of the tile's y rows, which the combine later accumulates into.
   template <typename RT>
   static DEV void route_gemm(const Params& p, int t0, int rows, int k0, int K, float* Ls,
                              float* part, char* smem) {
@@ -265,11 +265,10 @@ struct Stages {
     const int rows = min(kTB, p.T - t0);
     // the bias load is issued first, so its latency hides under the GEMM
     const float bias_v = (p.rsk == 1 && p.bias && (int)threadIdx.x < p.E) ? p.bias[threadIdx.x] : 0.f;
-    if (ks == 0) {
-      for (int r = 0; r < rows; ++r) {
-        float* yr = p.y + (size_t)(t0 + r) * p.d;
-        for (int i = threadIdx.x; i < p.d / 4; i += kThreads) st_wt16(yr, i * 16, make_uint4(0, 0, 0, 0));
-      }
+    // this slice zeroes its share of the tile's y rows (rows ks, ks + rsk, ...)
+    for (int r = ks; r < rows; r += p.rsk) {
+      float* yr = p.y + (size_t)(t0 + r) * p.d;
+      for (int i = threadIdx.x; i < p.d / 4; i += kThreads) st_wt16(yr, i * 16, make_uint4(0, 0, 0, 0));
     }
     const int Ks = p.d / p.rsk;
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);     // [32][E]
