@@ -47,7 +47,8 @@ class Info(ctypes.Structure):
     _fields_ = [("workers", c_int), ("cus", c_int), ("blocks_per_cu", c_int),
                 ("route_tiles", c_int), ("up_ntiles", c_int), ("down_ntiles", c_int),
                 ("split_k", c_int), ("permute_rows", c_int), ("max_mtiles", c_int),
-                ("max_tasks", c_int), ("route_splits", c_int), ("workspace_bytes", c_size_t)]
+                ("max_tasks", c_int), ("route_splits", c_int), ("combine_chunks", c_int),
+                ("workspace_bytes", c_size_t)]
 
 
 class MoEError(RuntimeError):

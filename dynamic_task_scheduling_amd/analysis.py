@@ -11,7 +11,7 @@ import numpy as np
 
 KIND_SHIFT = 27
 KINDS = {1: "ROUTE", 2: "POS", 3: "PERM", 4: "UP", 5: "DOWN", 6: "SUP", 7: "SDOWN",
-         8: "PHASE"}   # PHASE: scheduler phases (builder steps, router reduction)
+         8: "PHASE", 9: "COMB"}   # PHASE: scheduler phases (builder steps, router reduction)
 CLOCK_HZ = 100e6   # s_memrealtime rate
 
 

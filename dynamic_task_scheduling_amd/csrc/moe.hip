@@ -24,7 +24,8 @@ struct Layout {
   int esz;
   size_t off_ctrl, off_slots, off_logits, off_idx, off_w, off_hist, off_rtb, off_counts,
       off_offsets, off_eorder, off_route_part, off_cnt_route, off_perm, off_rw, off_slotpos, off_mtiles, off_cnt_perm,
-      off_cnt_down, off_cnt_sdown, off_perm_list, off_xp, off_h, off_hs, total;
+      off_cnt_down, off_cnt_sdown, off_perm_list, off_mt_base, off_cnt_comb, off_xp, off_h, off_hs,
+      off_o, off_ys, total;
 };
 
 int validate(const moe_desc* d) {
@@ -105,9 +106,13 @@ void make_layout(const moe_desc* d, Layout* L) {
   p.max_perm = (int)((R + pr - 1) / pr + p.max_mt);
   p.n_sup = p.n_shared * p.n_smt * p.n_s_up_n;
   p.n_sdown = p.n_shared * p.n_smt * p.n_down_n;
+  // combine chunks: 512 columns (128 float4, two tokens per pass of the
+  // workgroup) when d allows, else 256 or 128
+  p.comb_cols = d->d % 512 == 0 ? 512 : d->d % 256 == 0 ? 256 : 128;
+  p.n_cc = d->d / p.comb_cols;
   const long long qa = (long long)p.n_rt * (p.rsk + 1);
   const long long qc = (long long)p.max_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup +
-                       p.n_sdown + p.max_perm;
+                       p.n_sdown + p.max_perm + (long long)p.n_rt * p.n_cc;
   p.q_cap = (int)(std::max(qa, qc) + kMaxWorkersBound);
 
   size_t o = 0;
@@ -137,9 +142,13 @@ void make_layout(const moe_desc* d, Layout* L) {
   L->off_cnt_down = take(sizeof(int) * (size_t)p.max_mt * p.splitk);
   L->off_cnt_sdown = take(sizeof(int) * (size_t)std::max(1, p.n_shared * p.n_smt));
   L->off_perm_list = take(sizeof(int) * p.max_perm);
+  L->off_mt_base = take(sizeof(int) * p.E_loc);
+  L->off_cnt_comb = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
   L->off_xp = take((size_t)L->esz * Tk * d->d);
   L->off_h = take((size_t)L->esz * Tk * d->f);
   L->off_hs = take((size_t)L->esz * d->n_shared * d->T * (d->n_shared ? d->f_shared : 0));
+  L->off_o = take(sizeof(float) * (size_t)p.splitk * Tk * d->d);
+  L->off_ys = take(sizeof(float) * (size_t)d->n_shared * d->T * d->d);
   L->total = o;
 }
 
@@ -166,6 +175,10 @@ void carve(Layout* L, void* ws) {
   p.cnt_down = reinterpret_cast<int*>(b + L->off_cnt_down);
   p.cnt_sdown = reinterpret_cast<int*>(b + L->off_cnt_sdown);
   p.perm_list = reinterpret_cast<int*>(b + L->off_perm_list);
+  p.mt_base = reinterpret_cast<int*>(b + L->off_mt_base);
+  p.cnt_comb = reinterpret_cast<int*>(b + L->off_cnt_comb);
+  p.O = reinterpret_cast<float*>(b + L->off_o);
+  p.Ys = reinterpret_cast<float*>(b + L->off_ys);
   p.Xp = b + L->off_xp;
   p.H = b + L->off_h;
   p.Hs = b + L->off_hs;
@@ -246,6 +259,8 @@ int launch_layer(const moe_desc* d, Params& p, hipStream_t s) {
     HIP_OK(hipGetLastError());
     hipLaunchKernelGGL(k_stage_down<Elem>, dim3(p.max_mt * p.n_down_n * p.splitk + p.n_sdown),
                        dim3(kThreads), 0, s, p);
+    HIP_OK(hipGetLastError());
+    hipLaunchKernelGGL(k_stage_comb<Elem>, dim3(p.n_rt * p.n_cc), dim3(kThreads), 0, s, p);
   }
   HIP_OK(hipGetLastError());
   return MOE_OK;
@@ -324,6 +339,7 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->max_mtiles = L.p.max_mt;
   info->max_tasks = L.p.q_cap;
   info->route_splits = L.p.rsk;
+  info->combine_chunks = L.p.n_cc;
   info->workspace_bytes = L.total;
   return MOE_OK;
 }

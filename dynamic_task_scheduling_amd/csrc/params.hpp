@@ -11,10 +11,11 @@ enum TaskKind : int {
   TK_POS = 2,    // payload rt: stable positions of those tokens' slots
   TK_PERM = 3,   // payload mt * pch + c: gather rows chunk c of row-tile mt
   TK_UP = 4,     // payload mt * n_up_n + n: gate/up GEMM + SiLU-gate epilogue
-  TK_DOWN = 5,   // payload (mt * n_down_n + n) * splitk + ks: DOWN GEMM + combine
+  TK_DOWN = 5,   // payload (mt * n_down_n + n) * splitk + ks: DOWN GEMM -> O rows
   TK_SUP = 6,    // payload (s * n_smt + m) * n_s_up_n + n: shared-expert UP
-  TK_SDOWN = 7,  // payload (s * n_smt + m) * n_down_n + n: shared-expert DOWN
+  TK_SDOWN = 7,  // payload (s * n_smt + m) * n_down_n + n: shared-expert DOWN -> Ys rows
   TK_BUILD = 8,  // (trace only) scheduler phases: payload = kPhase* id
+  TK_COMB = 9,   // payload rt * n_cc + cc: y rows of tokens [32 rt, 32 rt + 32), column chunk cc
 };
 // Trace phase ids (payload of TK_BUILD records).
 constexpr int kPhaseBuild = 0;          // the whole post-routing builder
@@ -78,6 +79,8 @@ struct Params {
   int max_mt;      // capacity of the row-tile table
   int max_perm;    // capacity of the permute list
   int n_sup, n_sdown;
+  int comb_cols;   // y columns per combine task (divides d)
+  int n_cc;        // combine chunks per token tile = d / comb_cols
   int q_cap;       // slots per queue
   // scheduling
   int workers;
@@ -120,9 +123,13 @@ struct Params {
   int* cnt_down;   // [max_mt * splitk]
   int* cnt_sdown;  // [n_shared * n_smt]
   int* perm_list;  // [max_perm]
+  int* mt_base;    // [E_loc] first row tile of each local expert
+  int* cnt_comb;   // [n_rt] DOWN / shared-DOWN tiles a combine tile still waits for
   void* Xp;        // [T*k][d]
   void* H;         // [T*k][f]
   void* Hs;        // [n_shared][T][fs]
+  float* O;        // [splitk][T*k][d] fp32 DOWN output rows (per K slice)
+  float* Ys;       // [n_shared][T][d] fp32 shared-expert DOWN output
   uint64_t* trace; // [trace_cap][4]
   int trace_cap;
   int route_from_logits;  // 1: logits are an input, y untouched

@@ -196,6 +196,46 @@ DEV void trace_mark(const Params& p, int phase, int worker, uint64_t t0, uint64_
   trace_record(p, make_task(TK_BUILD, phase), worker, t0, t0, t1);
 }
 
+// One thread: push the combine tasks of token tile rt (all column chunks).
+DEV void push_combine(const Params& p, int rt) {
+  const int base = add_relaxed(cw(p, CW_TAIL + QC), p.n_cc);
+  if (base + p.n_cc > p.q_cap) {
+    set_error(p, 6 /* MOE_ERR_CAPACITY */);
+    return;
+  }
+  int* sl = p.slots + (size_t)QC * p.q_cap + base;
+  for (int c = 0; c < p.n_cc; ++c) st_relaxed(sl + c, make_task(TK_COMB, rt * p.n_cc + c) + 1);
+}
+
+// All threads, after a DOWN tile of rows [row0, row0 + rows): its results
+// are published, then each token tile those rows belong to loses one
+// pending tile; the arrival that empties a counter releases that tile's
+// combine tasks (dynamic mode).  An expert's rows are sorted by token, so
+// the tile's token tiles are the runs of perm[r] / 32.
+DEV void combine_arrive_rows(const Params& p, int row0, int rows, bool dyn) {
+  publish_fence();
+  __syncthreads();
+  const int r = threadIdx.x;
+  if (r < rows) {
+    const int blk = p.perm[row0 + r] / kTB;
+    const int prev = r > 0 ? p.perm[row0 + r - 1] / kTB : -1;
+    if (blk != prev && add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn) push_combine(p, blk);
+  }
+  __syncthreads();
+}
+
+// Same for a shared-expert DOWN tile of the 128 tokens [128 m, 128 m + 128).
+DEV void combine_arrive_shared(const Params& p, int m, bool dyn) {
+  static_assert(128 % kTB == 0, "shared row tiles hold whole token tiles");
+  publish_fence();
+  __syncthreads();
+  const int blk = m * (128 / kTB) + (int)threadIdx.x;
+  if ((int)threadIdx.x < 128 / kTB && blk < p.n_rt &&
+      add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn)
+    push_combine(p, blk);
+  __syncthreads();
+}
+
 template <typename Elem>
 struct Sched {
   using S = Stages<Elem>;
@@ -205,7 +245,8 @@ struct Sched {
     const int n_mt = ld_relaxed(cw(p, CW_NMT));
     const int n_perm = ld_relaxed(cw(p, CW_NPERM));
     const bool split = p.split_policy != 2;
-    const int n_comp = n_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup + p.n_sdown;
+    const int n_comp = n_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup + p.n_sdown +
+                       p.n_rt * p.n_cc;
     publish_fence();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -264,8 +305,20 @@ struct Sched {
         break;
       }
       case TK_POS: {
-        S::position(p, pl, smem);
+        const int nd = S::position(p, pl, smem);
         *t_body = rtc();
+        // the combine of these tokens waits for the DOWN tiles of the nd row
+        // tiles holding their rows; this replaces the counter's initial
+        // "positions pending" unit (k_reset) by that many tiles
+        if (threadIdx.x == 0) {
+          const int delta = nd * p.n_down_n * p.splitk - 1;
+          s_tmp[0] = (add_relaxed(p.cnt_comb + pl, delta) + delta == 0);
+        }
+        __syncthreads();
+        const bool comb_ready = s_tmp[0] != 0;
+        __syncthreads();
+        if (comb_ready && dyn)
+          push_burst(p, QC, p.n_cc, s_tmp, [&](int c) { return make_task(TK_COMB, pl * p.n_cc + c); });
         if (arrive_last(cw(p, CW_POS_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
           const int n_perm = ld_relaxed(cw(p, CW_NPERM));
           const int q = (p.split_policy != 2) ? QM : QC;
@@ -296,8 +349,11 @@ struct Sched {
       case TK_DOWN: {
         const int ks = pl % p.splitk;
         const int r = pl / p.splitk;
-        S::down(p, r / p.n_down_n, r % p.n_down_n, ks, smem);
+        const int mt = r / p.n_down_n;
+        S::down(p, mt, r % p.n_down_n, ks, smem);
         *t_body = rtc();
+        const MTile t = p.mtiles[mt];
+        combine_arrive_rows(p, t.row0, t.rows, dyn);
         break;
       }
       case TK_SUP: {
@@ -314,6 +370,12 @@ struct Sched {
         const int n = pl % p.n_down_n;
         const int sm = pl / p.n_down_n;
         S::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem);
+        *t_body = rtc();
+        combine_arrive_shared(p, sm % p.n_smt, dyn);
+        break;
+      }
+      case TK_COMB: {
+        S::combine(p, pl / p.n_cc, pl % p.n_cc, smem);
         *t_body = rtc();
         break;
       }
@@ -425,6 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
     if (!grid_barrier(p, gen, s_tmp)) return;
     for (int i = w; i < n_down + p.n_sdown; i += W)
       exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
+    if (!grid_barrier(p, gen, s_tmp)) return;
+    for (int i = w; i < p.n_rt * p.n_cc; i += W) exec(make_task(TK_COMB, i));
     return;
   }
   // fixed split, per-task counter waits, no barriers
@@ -458,6 +522,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
     consume_fence();
     exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
   }
+  for (int i = w; i < p.n_rt * p.n_cc; i += W) {
+    if (threadIdx.x == 0) s_tmp[1] = wait_zero(p, p.cnt_comb + i / p.n_cc);
+    __syncthreads();
+    const bool ok = s_tmp[1];
+    __syncthreads();
+    if (!ok) return;
+    consume_fence();
+    exec(make_task(TK_COMB, i));
+  }
 }
 
 // ----------------------------------------------- one launch per stage
@@ -485,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_build(Params p) {
 
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void k_stage_pos(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[kTB * kMaxK * 8];
+  __shared__ __attribute__((aligned(16))) char smem[(2 * kThreads + 4) * 4];
   Stages<Elem>::position(p, blockIdx.x, smem);
 }
 
@@ -530,6 +603,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_stage_down(Params p) {
   }
 }
 
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void k_stage_comb(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[kTB * kMaxK * 8];
+  Stages<Elem>::combine(p, blockIdx.x / p.n_cc, blockIdx.x % p.n_cc, smem);
+}
+
 // Control block reset + queue seeding, launched before every call.
 __global__ __launch_bounds__(kThreads) void k_reset(Params p) {
   const int gid = blockIdx.x * kThreads + threadIdx.x;
@@ -550,6 +629,9 @@ __global__ __launch_bounds__(kThreads) void k_reset(Params p) {
   for (int i = gid; i < p.n_rt; i += stride) p.cnt_route[i] = p.rsk;
   const int nsm = p.n_shared * p.n_smt;
   for (int i = gid; i < nsm; i += stride) p.cnt_sdown[i] = p.n_s_up_n + 1;
+  // combine tiles: the shared DOWN tiles over their tokens, plus one unit
+  // that the tile's POS task replaces by its routed DOWN tiles
+  for (int i = gid; i < p.n_rt; i += stride) p.cnt_comb[i] = 1 + p.n_shared * p.n_down_n;
   if (gid == 0) {
     p.ctrl[(CW_TAIL + QA) * kCtrlStride] = n_route;
     p.ctrl[(CW_TOTAL + QA) * kCtrlStride] = n_route + p.n_rt;

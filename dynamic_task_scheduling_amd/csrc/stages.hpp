@@ -219,8 +219,7 @@ struct Stages {
   // ks of rsk.  With rsk == 1 the task also adds the bias, picks the top-k
   // and writes the tile histogram; with rsk > 1 it writes an fp32 partial
   // and the last slice to finish runs route_finish (fixed-order sum, so the
-  // logits do not depend on which slice finished last).  The slices share the
-  // zeroing of the tile's y rows, which the combine later accumulates into.
+  // logits do not depend on which slice finished last).
   template <typename RT>
   static DEV void route_gemm(const Params& p, int t0, int rows, int k0, int K, float* Ls,
                              float* part, char* smem) {
@@ -265,11 +264,6 @@ struct Stages {
     const int rows = min(kTB, p.T - t0);
     // the bias load is issued first, so its latency hides under the GEMM
     const float bias_v = (p.rsk == 1 && p.bias && (int)threadIdx.x < p.E) ? p.bias[threadIdx.x] : 0.f;
-    // this slice zeroes its share of the tile's y rows (rows ks, ks + rsk, ...)
-    for (int r = ks; r < rows; r += p.rsk) {
-      float* yr = p.y + (size_t)(t0 + r) * p.d;
-      for (int i = threadIdx.x; i < p.d / 4; i += kThreads) st_wt16(yr, i * 16, make_uint4(0, 0, 0, 0));
-    }
     const int Ks = p.d / p.rsk;
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);     // [32][E]
     float* part = p.rsk > 1 ? route_part_block(p, rt, ks) : nullptr;
@@ -526,6 +520,7 @@ struct Stages {
     if (tid < El) {
       s_mtb[tid] = mtb;
       s_pb[tid] = pb;
+      st_wt(p.mt_base + s_ord[tid], mtb);
     }
     if (tid == 0) {
       s_mtb[El] = n_mt;
@@ -600,14 +595,20 @@ struct Stages {
   // inside every expert: row = offsets[e] + rt_base[e][rt] + rank in tile.
   // One thread per slot (32 tokens x k <= 256 slots): its rank is the number
   // of earlier slots of the tile with the same expert.
-  static TASKFN void position(const Params& p, int rt, char* smem) {
+  // Returns (to every thread) how many distinct expert row tiles hold the
+  // tile's kept slots: the combine of these tokens waits for exactly those
+  // tiles' DOWN tasks.
+  static TASKFN int position(const Params& p, int rt, char* smem) {
     static_assert(kTB * kMaxK <= kThreads, "one thread per slot");
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     const int k = p.k;
     const int ns = rows * k;
     int* s_e = reinterpret_cast<int*>(smem);             // [256]
+    int* s_mt = s_e + kThreads;                          // [256] row tile of each slot
+    int* s_nd = s_mt + kThreads;                         // distinct row tiles
     const int i = threadIdx.x;
+    if (i == 0) *s_nd = 0;
     int e = -1;
     float w = 0.f;
     if (i < ns) {
@@ -618,9 +619,14 @@ struct Stages {
     }
     s_e[i] = e;
     // this slot's segment base, loaded while the ranks are counted
-    int base = 0;
-    if (e >= 0) base = p.offsets[e] + p.rt_base[(size_t)e * p.hist_ld + rt];
+    int base = 0, eoff = 0, mtb = 0;
+    if (e >= 0) {
+      eoff = p.offsets[e];
+      base = eoff + p.rt_base[(size_t)e * p.hist_ld + rt];
+      mtb = p.mt_base[e];
+    }
     __syncthreads();
+    int mt = -1;
     if (i < ns) {
       if (e < 0) {
         st_wt(p.slot_pos + (size_t)t0 * k + i, -1);
@@ -631,9 +637,20 @@ struct Stages {
         st_wt(p.perm + pos, t0 + i / k);
         st_wt(p.rw + pos, w);
         st_wt(p.slot_pos + (size_t)t0 * k + i, pos);
+        mt = mtb + (pos - eoff) / 128;
       }
     }
+    s_mt[i] = mt;
     __syncthreads();
+    if (mt >= 0) {
+      bool first = true;
+      for (int j = 0; j < i; ++j) first = first && (s_mt[j] != mt);
+      if (first) atomicAdd(s_nd, 1);
+    }
+    __syncthreads();
+    const int nd = *s_nd;
+    __syncthreads();
+    return nd;
   }
 
   // PERM(mt, c): Xp[r] = x[perm[r]] for rows chunk c of tile mt (16-byte
@@ -708,12 +725,14 @@ struct Stages {
     __syncthreads();
   }
 
-  // DOWN tile: y[tok(r), n0:n0+128] += wt(r) * (A Wd)[r, :]  (fp32 atomics).
-  // tok == nullptr: rows map to tokens row_tok0 + r with weight 1 (shared).
+  // DOWN tile: Out[r, 0:128] = (A Wd)[r, :] for the valid rows r < rows,
+  // fp32, staged through LDS and written as whole 16-byte row chunks
+  // (write-through: a combine task on another XCD reads them).  The weighted
+  // sum over a token's experts is the combine task's job, so no output
+  // element is ever written twice and no atomics are needed.
   template <int BM>
   static DEV void down_tile(const Elem* A, int lda, int rows, const Elem* wd, int ldb, int K,
-                            const int* tok, const float* wt, int row_tok0, float* y, int ldy,
-                            char* smem) {
+                            float* out, int ldo, char* smem) {
     using TL = typename GemmSel<Elem, BM, 1>::T;
     typename TL::Args g;
     g.A = A;
@@ -726,16 +745,20 @@ struct Stages {
     typename TL::Acc acc;
     if constexpr (TR::kBf16) TL::run(g, smem, acc);
     else TL::run(g, reinterpret_cast<Elem*>(smem), acc);
+    // stage [BM][128] fp32 (rows padded by 4 floats against bank conflicts)
+    constexpr int SLD = kBN + 4;
+    static_assert(BM * SLD * 4 <= TL::LDS_BYTES, "DOWN staging fits the ring");
+    float* st = reinterpret_cast<float*>(smem);
     TL::for_each([&](int row, int col, int fm, int fn, int i) __attribute__((always_inline)) {
-      if (row < rows) {
-        const float v = acc[0][fm][fn][i];
-        if (tok) {
-          unsafeAtomicAdd(y + (size_t)tok[row] * ldy + col, wt[row] * v);
-        } else {
-          unsafeAtomicAdd(y + (size_t)(row_tok0 + row) * ldy + col, v);
-        }
-      }
+      st[row * SLD + col] = acc[0][fm][fn][i];
     });
+    __syncthreads();
+    constexpr int CPR = kBN * 4 / 16;
+    for (int i = threadIdx.x; i < rows * CPR; i += kThreads) {
+      const int r = i / CPR, c = i % CPR;
+      st_wt16(out + (size_t)r * ldo, c * 16, *reinterpret_cast<const uint4*>(st + r * SLD + c * 4));
+    }
+    __syncthreads();
   }
 
   static TASKFN void up(const Params& p, int mt, int n, char* smem) {
@@ -757,12 +780,15 @@ struct Stages {
     const Elem* A = reinterpret_cast<const Elem*>(p.H) + (size_t)t.row0 * p.f + k_lo;
     const Elem* wd = reinterpret_cast<const Elem*>(p.wd) + (size_t)t.e * p.f * p.d +
                      (size_t)k_lo * p.d + (size_t)n * kBN;
-    const int* tok = p.perm + t.row0;
-    const float* wt = p.rw + t.row0;
-    float* y = p.y + (size_t)n * kBN;
-    if (t.bm == 32) down_tile<32>(A, p.f, t.rows, wd, p.d, K, tok, wt, 0, y, p.d, smem);
-    else if (t.bm == 64) down_tile<64>(A, p.f, t.rows, wd, p.d, K, tok, wt, 0, y, p.d, smem);
-    else down_tile<128>(A, p.f, t.rows, wd, p.d, K, tok, wt, 0, y, p.d, smem);
+    float* out = o_slice(p, ks) + (size_t)t.row0 * p.d + (size_t)n * kBN;
+    if (t.bm == 32) down_tile<32>(A, p.f, t.rows, wd, p.d, K, out, p.d, smem);
+    else if (t.bm == 64) down_tile<64>(A, p.f, t.rows, wd, p.d, K, out, p.d, smem);
+    else down_tile<128>(A, p.f, t.rows, wd, p.d, K, out, p.d, smem);
+  }
+
+  // DOWN output rows of K slice ks: [T*k][d] fp32.
+  static DEV float* o_slice(const Params& p, int ks) {
+    return p.O + (size_t)ks * p.T * p.k * p.d;
   }
 
   // Shared (always-on) experts: every token, weight 1, input x directly.
@@ -784,10 +810,94 @@ struct Stages {
     const int rows = min(128, p.T - r0);
     const Elem* A = reinterpret_cast<const Elem*>(p.Hs) + ((size_t)s * p.T + r0) * p.fs;
     const Elem* wd = reinterpret_cast<const Elem*>(p.sd) + (size_t)s * p.fs * p.d + (size_t)n * kBN;
-    float* y = p.y + (size_t)n * kBN;
-    if (rows <= 32) down_tile<32>(A, p.fs, rows, wd, p.d, p.fs, nullptr, nullptr, r0, y, p.d, smem);
-    else if (rows <= 64) down_tile<64>(A, p.fs, rows, wd, p.d, p.fs, nullptr, nullptr, r0, y, p.d, smem);
-    else down_tile<128>(A, p.fs, rows, wd, p.d, p.fs, nullptr, nullptr, r0, y, p.d, smem);
+    float* out = p.Ys + ((size_t)s * p.T + r0) * p.d + (size_t)n * kBN;
+    if (rows <= 32) down_tile<32>(A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem);
+    else if (rows <= 64) down_tile<64>(A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem);
+    else down_tile<128>(A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem);
+  }
+
+  // ------------------------------------------------------------- combine
+  // COMB(rt, cc): y[t, cols] = sum_j w[t,j] * (sum_ks O_ks[slot_pos[t,j], cols])
+  // over the token's kept slots in slot order, then + sum_s Ys[s][t, cols]
+  // over the shared experts, for the 32 tokens of tile rt and the column
+  // chunk cc.  The weighted combine of the MoE layer (xxqk.cn/news/665650
+  // s1, last stage; it stands in for expert-parallel combine, Weave
+  // abstract): a token's output needs every one of its experts, so the task
+  // becomes ready only when all DOWN tiles holding its rows have finished.
+  // Fixed summation order: y does not depend on the schedule.
+  static TASKFN void combine(const Params& p, int rt, int cc, char* smem) {
+    const int t0 = rt * kTB;
+    const int rows = min(kTB, p.T - t0);
+    const int k = p.k;
+    int* s_pos = reinterpret_cast<int*>(smem);               // [32 * k]
+    float* s_w = reinterpret_cast<float*>(s_pos + kTB * kMaxK);
+    for (int i = threadIdx.x; i < rows * k; i += kThreads) {
+      s_pos[i] = p.slot_pos[(size_t)t0 * k + i];
+      s_w[i] = p.w[(size_t)t0 * k + i];
+    }
+    __syncthreads();
+    const int c4 = p.comb_cols / 4;                      // float4 per row chunk
+    const int col0 = cc * p.comb_cols;
+    const size_t slice = (size_t)p.T * k * p.d;
+    const int n = rows * c4;
+    // two (token, float4) items per thread per pass, every load of both
+    // issued before any sum (a combine task is a latency-bound gather)
+    for (int i0 = threadIdx.x; i0 < n; i0 += 2 * kThreads) {
+      float4 v[2][kMaxK];
+      float4 sh[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * kThreads;
+        const int r = i / c4, col = col0 + (i % c4) * 4;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+          v[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (i < n && j < k) {
+            const int pos = s_pos[r * k + j];
+            if (pos >= 0) {
+              const float* o = p.O + (size_t)pos * p.d + col;
+              float4 a = *reinterpret_cast<const float4*>(o);
+              for (int ks = 1; ks < p.splitk; ++ks) {
+                const float4 b = *reinterpret_cast<const float4*>(o + ks * slice);
+                a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+              }
+              v[u][j] = a;
+            }
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          sh[u][s] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (i < n && s < p.n_shared)
+            sh[u][s] = *reinterpret_cast<const float4*>(p.Ys + ((size_t)s * p.T + t0 + r) * p.d + col);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * kThreads;
+        if (i >= n) continue;
+        const int r = i / c4, col = col0 + (i % c4) * 4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+          if (j < k && s_pos[r * k + j] >= 0) {
+            const float wj = s_w[r * k + j];
+            acc.x += wj * v[u][j].x;
+            acc.y += wj * v[u][j].y;
+            acc.z += wj * v[u][j].z;
+            acc.w += wj * v[u][j].w;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s < p.n_shared) {
+            acc.x += sh[u][s].x; acc.y += sh[u][s].y; acc.z += sh[u][s].z; acc.w += sh[u][s].w;
+          }
+        }
+        *reinterpret_cast<float4*>(p.y + (size_t)(t0 + r) * p.d + col) = acc;
+      }
+    }
+    __syncthreads();
   }
 };
 

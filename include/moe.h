@@ -4,7 +4,8 @@
  * One call runs a whole MoE layer on one GPU:
  *   router GEMM -> softmax top-k -> stable count/scan/permute into
  *   expert-contiguous rows -> per-expert SwiGLU GEMM tasks (bf16 MFMA,
- *   fused SiLU-gate epilogue) -> weighted scatter-add combine.
+ *   fused SiLU-gate epilogue) -> weighted per-token combine of the experts'
+ *   output rows (fixed order, no atomics).
  *
  * The stages are those the Weave pages place inside one persistent MoE
  * kernel (xxqk.cn/news/665650 section 1; m.xxqk.cn/news/657744 section 2.1).
@@ -44,8 +45,10 @@ extern "C" {
  * intermediate buffers.  Accumulation is always fp32; y is always fp32. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-/* Scheduling mode.  Every mode runs the same device tile code and gives the
- * same routing bit for bit; y differs only by fp32 summation order.
+/* Scheduling mode.  Every mode runs the same device tile code in the same
+ * arithmetic order (each output row is summed over its experts by one
+ * combine task, in slot order), so every mode gives the same routing and
+ * the same y, bit for bit.
  *  MOE_DYNAMIC           one persistent kernel, dependency-driven ready
  *                        queues, count-sized worker split (the method).
  *  MOE_STATIC_PARTITION  one persistent kernel, tasks pre-assigned to
@@ -160,6 +163,7 @@ typedef struct moe_info {
   int max_mtiles;       /* capacity of the expert row-tile table           */
   int max_tasks;        /* capacity of the ready queues                    */
   int route_splits;     /* router K slices per router tile                 */
+  int combine_chunks;   /* combine tasks per 32-token tile (d / columns)   */
   size_t workspace_bytes;
 } moe_info;
 

@@ -144,24 +144,26 @@ def test_cross_mode_agreement(mid):
     for key in MODES[1:]:
         for f in ("topk_idx", "expert_counts", "offsets", "slot_pos"):
             assert torch.equal(getattr(routes[key], f), getattr(routes[MODES[0]], f))
-        d = (ys[key] - ref).abs().max().item()
-        assert d <= 1e-5 * ref.abs().max().item(), "%s differs by %g" % (key, d)
+        # same tiles, same fixed-order combine: bit-identical across modes
+        assert torch.equal(ys[key], ref), "%s differs by %g" % (
+            key, (ys[key] - ref).abs().max().item())
 
 
 def test_repeat_and_poisoned_workspace(mid):
     """Repeated calls on one workspace, and a workspace filled with NaN-like
-    bytes before a call, give the same result (no read before write)."""
+    bytes before a call, give the same y bit for bit (no read before write;
+    the result does not depend on the schedule)."""
     g, n = mid
     layer = MoELayer(MID, g, mode="dynamic", timeout_ms=3000)
     y0 = layer(g["x"], check_errors=True).clone()
     for _ in range(3):
         y1 = layer(g["x"], check_errors=True)
-        assert (y1 - y0).abs().max().item() <= 1e-5 * y0.abs().max().item()
+        assert torch.equal(y1, y0), "repeat call differs"
     layer.workspace.fill_(0xFF)
     y2 = layer(g["x"], check_errors=True)
     torch.cuda.synchronize()
     assert torch.isfinite(y2).all()
-    assert (y2 - y0).abs().max().item() <= 1e-5 * y0.abs().max().item()
+    assert torch.equal(y2, y0), "call on a poisoned workspace differs"
 
 
 @pytest.mark.parametrize("mode,split", [("dynamic", "cost_model"), ("dynamic", "none"),
