@@ -30,6 +30,7 @@ class Desc(ctypes.Structure):
         ("dtype", c_int), ("mode", c_int), ("split_policy", c_int),
         ("fixed_mem_workers", c_int), ("split_k", c_int), ("max_workers", c_int),
         ("flags", c_uint), ("trace", c_void_p), ("trace_cap", c_int), ("timeout_ms", c_int),
+        ("row_tile", c_int),
     ]
 
 
@@ -47,7 +48,7 @@ class Info(ctypes.Structure):
     _fields_ = [("workers", c_int), ("cus", c_int), ("blocks_per_cu", c_int),
                 ("route_tiles", c_int), ("up_ntiles", c_int), ("down_ntiles", c_int),
                 ("split_k", c_int), ("permute_rows", c_int), ("max_mtiles", c_int),
-                ("max_tasks", c_int), ("route_splits", c_int), ("combine_chunks", c_int),
+                ("max_tasks", c_int), ("route_splits", c_int), ("combine_chunks", c_int), ("row_tile", c_int),
                 ("workspace_bytes", c_size_t)]
 
 

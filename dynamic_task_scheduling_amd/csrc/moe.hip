@@ -47,7 +47,9 @@ int validate(const moe_desc* d) {
   const long long rows = (long long)d->T * d->k;
   const long long mt = rows / 128 + (e_end - d->e_begin);
   if (mt * (d->d / kBN) * 8 >= (1ll << kKindShift)) return MOE_ERR_UNSUPPORTED;
-  if (mt * 64 >= (1ll << kKindShift)) return MOE_ERR_UNSUPPORTED;  // permute payloads
+  if (mt * 128 >= (1ll << kKindShift)) return MOE_ERR_UNSUPPORTED;  // permute payloads
+  if (d->row_tile != 0 && d->row_tile != 128 && d->row_tile != 256) return MOE_ERR_ARG;
+  if (d->row_tile == 256 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -80,15 +82,22 @@ void make_layout(const moe_desc* d, Layout* L) {
     for (int sl = 1; sl <= ksteps; ++sl)
       if (ksteps % sl == 0 && sl <= want && sl <= max_rsk && d->d / sl >= 256) p.rsk = sl;
   }
+  // Expert row tiles: 256 rows for large bf16 layers (the 256 x 256 task
+  // reads half the LDS bytes per MFMA flop of a 128-row one), 128 otherwise
+  // (small layers need many tasks, and their experts hold few rows).
+  // DOWN tasks then cover 256 columns when d allows.
+  p.th = d->row_tile ? d->row_tile
+                     : (d->dtype == MOE_BF16 && (long long)d->T * d->k > 8192 ? 256 : 128);
+  p.down_nb = (p.th == 256 && d->d % 256 == 0) ? 2 : 1;
   p.n_up_n = d->f / kBN;
-  p.n_down_n = d->d / kBN;
+  p.n_down_n = d->d / (kBN * p.down_nb);
   int sk = d->split_k;
   // automatic DOWN split-K: one slice per 7168 of f (measured: decode-shaped
   // f = 14336 is fastest with 2; every slice adds fp32 atomics to y)
   if (sk == 0) sk = std::max(1, std::min(8, d->f / 7168));
   p.splitk = std::min(sk, p.n_up_n);
   p.n_s_up_n = p.fs / kBN;
-  p.n_smt = (d->T + 127) / 128;
+  p.n_smt = (d->T + p.th - 1) / p.th;
   // rows per permute task: a power of two in [2, 128] moving at most 256 KB,
   // and small enough that a small layer's gather spreads over about two
   // tasks per CU (32 KB minimum per task)
@@ -100,15 +109,22 @@ void make_layout(const moe_desc* d, Layout* L) {
     while (pr > 2 && (long long)pr * row_bytes > target) pr >>= 1;
   }
   p.perm_rows = pr;
-  p.pch = 128 / pr;
+  p.pch = p.th / pr;
   const long long R = (long long)d->T * d->k;
   p.max_mt = (int)(R / 128 + p.E_loc + 1);
   p.max_perm = (int)((R + pr - 1) / pr + p.max_mt);
   p.n_sup = p.n_shared * p.n_smt * p.n_s_up_n;
   p.n_sdown = p.n_shared * p.n_smt * p.n_down_n;
-  // combine chunks: 512 columns (128 float4, two tokens per pass of the
-  // workgroup) when d allows, else 256 or 128
-  p.comb_cols = d->d % 512 == 0 ? 512 : d->d % 256 == 0 ? 256 : 128;
+  // combine chunks: the widest of 512 / 256 / 128 columns that divides d
+  // and still gives about two combine tasks per CU; small-T layers get
+  // narrow chunks, so the combine that follows the last DOWN tile spreads
+  // over the whole device
+  p.comb_cols = 128;
+  for (int cols = 512; cols > 128; cols >>= 1)
+    if (d->d % cols == 0 && (long long)p.n_rt * (d->d / cols) >= 512) {
+      p.comb_cols = cols;
+      break;
+    }
   p.n_cc = d->d / p.comb_cols;
   const long long qa = (long long)p.n_rt * (p.rsk + 1);
   const long long qc = (long long)p.max_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup +
@@ -340,6 +356,7 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->max_tasks = L.p.q_cap;
   info->route_splits = L.p.rsk;
   info->combine_chunks = L.p.n_cc;
+  info->row_tile = L.p.th;
   info->workspace_bytes = L.total;
   return MOE_OK;
 }

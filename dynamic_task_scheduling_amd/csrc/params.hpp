@@ -58,7 +58,7 @@ struct MTile {
   int e;     // local expert
   int row0;  // first row in the expert-contiguous buffers
   int rows;  // valid rows (<= bm)
-  int bm;    // tile height class: 32, 64 or 128
+  int bm;    // tile height class: 32, 64, 128 or 256
 };
 
 struct Params {
@@ -69,13 +69,15 @@ struct Params {
   int n_rt;        // router / position tiles of 32 tokens
   int rsk;         // router K slices (divides d / 64)
   int hist_ld;     // row stride of hist / rt_base (n_rt rounded up to 4)
+  int th;          // expert row-tile height: 128 or 256 rows
   int n_up_n;      // f / 128
-  int n_down_n;    // d / 128
+  int down_nb;     // 128-column blocks per DOWN task: 1 or 2
+  int n_down_n;    // DOWN column tasks = d / (128 * down_nb)
   int splitk;      // DOWN split-K slices
   int n_s_up_n;    // fs / 128
-  int n_smt;       // shared-expert row tiles of 128 tokens
+  int n_smt;       // shared-expert row tiles of th tokens
   int perm_rows;   // rows per permute task (divides 128)
-  int pch;         // permute chunks per row tile = 128 / perm_rows
+  int pch;         // permute chunks per row tile = th / perm_rows
   int max_mt;      // capacity of the row-tile table
   int max_perm;    // capacity of the permute list
   int n_sup, n_sdown;

@@ -224,13 +224,14 @@ DEV void combine_arrive_rows(const Params& p, int row0, int rows, bool dyn) {
   __syncthreads();
 }
 
-// Same for a shared-expert DOWN tile of the 128 tokens [128 m, 128 m + 128).
+// Same for a shared-expert DOWN tile of the th tokens [th m, th m + th)
+// (th = 128 or 256: whole token tiles).
 DEV void combine_arrive_shared(const Params& p, int m, bool dyn) {
-  static_assert(128 % kTB == 0, "shared row tiles hold whole token tiles");
   publish_fence();
   __syncthreads();
-  const int blk = m * (128 / kTB) + (int)threadIdx.x;
-  if ((int)threadIdx.x < 128 / kTB && blk < p.n_rt &&
+  const int per = p.th / kTB;
+  const int blk = m * per + (int)threadIdx.x;
+  if ((int)threadIdx.x < per && blk < p.n_rt &&
       add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn)
     push_combine(p, blk);
   __syncthreads();

@@ -491,17 +491,18 @@ struct Stages {
     }
     __syncthreads();
     mark(1);
-    // 3. row tiles (128 rows; the last one of an expert takes the smallest
-    //    class that holds it) and permute chunks, per rank; then the table,
-    //    filled by every thread in parallel (one tile per thread per pass)
+    // 3. row tiles (th = 128 or 256 rows; the last one of an expert takes
+    //    the smallest class that holds it) and permute chunks, per rank; then
+    //    the table, filled by every thread in parallel (one tile per thread
+    //    per pass)
     const float esz = TR::kBf16 ? 2.f : 4.f;
     int nt = 0, np = 0;
     float cost = 0.f;
     if (tid < El) {
       const int c = s_cnt[s_ord[tid]];
-      nt = (c + 127) / 128;
+      nt = (c + p.th - 1) / p.th;
       if (nt > 0) {
-        const int last = c - 128 * (nt - 1);
+        const int last = c - p.th * (nt - 1);
         np = (nt - 1) * p.pch + (last + p.perm_rows - 1) / p.perm_rows;
         // one worker's time for a tile: its MFMA work (padded rows), or its
         // share of HBM bandwidth for the tile's weights
@@ -510,8 +511,7 @@ struct Stages {
           const float fl = 6.f * bm * (float)p.d * (float)p.f;
           return fmaxf(fl / p.cm_mfma_rate, by * (float)p.workers / p.cm_hbm_bw);
         };
-        const int bml = last <= 32 ? 32 : last <= 64 ? 64 : 128;
-        cost = (float)(nt - 1) * tile_cost(128) + tile_cost(bml);
+        cost = (float)(nt - 1) * tile_cost(p.th) + tile_cost(row_class(last));
       }
     }
     int n_mt = 0, n_perm = 0;
@@ -543,11 +543,11 @@ struct Stages {
       const int r = lo;
       const int e = s_ord[r];
       const int m = mt - s_mtb[r];
-      const int rows = min(128, s_cnt[e] - 128 * m);
-      const int bm = rows <= 32 ? 32 : rows <= 64 ? 64 : 128;
+      const int rows = min(p.th, s_cnt[e] - p.th * m);
+      const int bm = row_class(rows);
       static_assert(sizeof(MTile) == 16, "MTile is one 16-byte store");
       st_wt16(p.mtiles, (uint32_t)mt * 16u,
-              make_uint4((unsigned)e, (unsigned)(s_off[e] + 128 * m), (unsigned)rows, (unsigned)bm));
+              make_uint4((unsigned)e, (unsigned)(s_off[e] + p.th * m), (unsigned)rows, (unsigned)bm));
       const int npt = (rows + p.perm_rows - 1) / p.perm_rows;
       st_wt(p.cnt_perm + mt, npt);
       for (int ks = 0; ks < p.splitk; ++ks)
@@ -637,7 +637,7 @@ struct Stages {
         st_wt(p.perm + pos, t0 + i / k);
         st_wt(p.rw + pos, w);
         st_wt(p.slot_pos + (size_t)t0 * k + i, pos);
-        mt = mtb + (pos - eoff) / 128;
+        mt = mtb + (pos - eoff) / p.th;
       }
     }
     s_mt[i] = mt;
@@ -689,6 +689,11 @@ struct Stages {
   }
 
   // ------------------------------------------------------------- GEMM tasks
+  // Height class of an expert row tile holding `rows` rows.
+  static DEV int row_class(int rows) {
+    return rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : 256;
+  }
+
   // UP tile: H[rows, n0:n0+128] = silu(A Wg) * (A Wu), rounded to Elem.
   template <int BM>
   static DEV void up_tile(const Elem* A, int lda, int rows, const Elem* wg, const Elem* wu,
@@ -730,35 +735,72 @@ struct Stages {
   // (write-through: a combine task on another XCD reads them).  The weighted
   // sum over a token's experts is the combine task's job, so no output
   // element is ever written twice and no atomics are needed.
-  template <int BM>
+  // NB = 2: two adjacent 128-column blocks of Wd share the A tile (a
+  // 256-column task), written as two consecutive column blocks of Out.
+  template <int BM, int NB>
   static DEV void down_tile(const Elem* A, int lda, int rows, const Elem* wd, int ldb, int K,
                             float* out, int ldo, char* smem) {
-    using TL = typename GemmSel<Elem, BM, 1>::T;
+    using TL = typename GemmSel<Elem, BM, NB>::T;
     typename TL::Args g;
     g.A = A;
     g.lda = lda;
     g.a_rows = rows;
-    g.B[0] = wd;
+#pragma unroll
+    for (int m = 0; m < NB; ++m) g.B[m] = wd + m * kBN;
     g.ldb = ldb;
     g.K = K;
     if constexpr (!TR::kBf16) g.n_valid = kBN;
     typename TL::Acc acc;
     if constexpr (TR::kBf16) TL::run(g, smem, acc);
     else TL::run(g, reinterpret_cast<Elem*>(smem), acc);
-    // stage [BM][128] fp32 (rows padded by 4 floats against bank conflicts)
+    // stage one [BM][128] fp32 block at a time (rows padded by 4 floats
+    // against bank conflicts)
     constexpr int SLD = kBN + 4;
-    static_assert(BM * SLD * 4 <= TL::LDS_BYTES, "DOWN staging fits the ring");
+    static_assert(BM * SLD * 4 <= kSmemTile, "DOWN staging fits the tile LDS");
     float* st = reinterpret_cast<float*>(smem);
-    TL::for_each([&](int row, int col, int fm, int fn, int i) __attribute__((always_inline)) {
-      st[row * SLD + col] = acc[0][fm][fn][i];
-    });
-    __syncthreads();
     constexpr int CPR = kBN * 4 / 16;
-    for (int i = threadIdx.x; i < rows * CPR; i += kThreads) {
-      const int r = i / CPR, c = i % CPR;
-      st_wt16(out + (size_t)r * ldo, c * 16, *reinterpret_cast<const uint4*>(st + r * SLD + c * 4));
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      TL::for_each([&](int row, int col, int fm, int fn, int i) __attribute__((always_inline)) {
+        st[row * SLD + col] = acc[m][fm][fn][i];
+      });
+      __syncthreads();
+      for (int i = threadIdx.x; i < rows * CPR; i += kThreads) {
+        const int r = i / CPR, c = i % CPR;
+        st_wt16(out + (size_t)r * ldo + m * kBN, c * 16,
+                *reinterpret_cast<const uint4*>(st + r * SLD + c * 4));
+      }
+      __syncthreads();
     }
-    __syncthreads();
+  }
+
+  // Dispatch on the row class (and, for bf16, the 256-row class and the
+  // 256-column DOWN task).
+  template <typename F>
+  static DEV void by_class(int bm, F&& f) {
+    if (bm == 32) f(std::integral_constant<int, 32>{});
+    else if (bm == 64) f(std::integral_constant<int, 64>{});
+    else if (bm == 128 || !TR::kBf16) f(std::integral_constant<int, 128>{});
+    else if constexpr (TR::kBf16) f(std::integral_constant<int, 256>{});
+  }
+  static DEV void down_any(int bm, int nb, const Elem* A, int lda, int rows, const Elem* wd,
+                           int ldb, int K, float* out, int ldo, char* smem) {
+    by_class(bm, [&](auto c) __attribute__((always_inline)) {
+      constexpr int BM = decltype(c)::value;
+      if constexpr (TR::kBf16) {
+        if (nb == 2) {
+          down_tile<BM, 2>(A, lda, rows, wd, ldb, K, out, ldo, smem);
+          return;
+        }
+      }
+      down_tile<BM, 1>(A, lda, rows, wd, ldb, K, out, ldo, smem);
+    });
+  }
+  static DEV void up_any(int bm, const Elem* A, int lda, int rows, const Elem* wg, const Elem* wu,
+                         int ldb, int K, Elem* Hout, int ldh, char* smem) {
+    by_class(bm, [&](auto c) __attribute__((always_inline)) {
+      up_tile<decltype(c)::value>(A, lda, rows, wg, wu, ldb, K, Hout, ldh, smem);
+    });
   }
 
   static TASKFN void up(const Params& p, int mt, int n, char* smem) {
@@ -768,9 +810,7 @@ struct Stages {
     const Elem* wg = reinterpret_cast<const Elem*>(p.wg) + eo;
     const Elem* wu = reinterpret_cast<const Elem*>(p.wu) + eo;
     Elem* H = reinterpret_cast<Elem*>(p.H) + (size_t)t.row0 * p.f + (size_t)n * kBN;
-    if (t.bm == 32) up_tile<32>(A, p.d, t.rows, wg, wu, p.f, p.d, H, p.f, smem);
-    else if (t.bm == 64) up_tile<64>(A, p.d, t.rows, wg, wu, p.f, p.d, H, p.f, smem);
-    else up_tile<128>(A, p.d, t.rows, wg, wu, p.f, p.d, H, p.f, smem);
+    up_any(t.bm, A, p.d, t.rows, wg, wu, p.f, p.d, H, p.f, smem);
   }
 
   static TASKFN void down(const Params& p, int mt, int n, int ks, char* smem) {
@@ -778,12 +818,11 @@ struct Stages {
     const int k_lo = slice_lo(ks, p.n_up_n, p.splitk) * kBN;
     const int K = slice_lo(ks + 1, p.n_up_n, p.splitk) * kBN - k_lo;
     const Elem* A = reinterpret_cast<const Elem*>(p.H) + (size_t)t.row0 * p.f + k_lo;
+    const int n0 = n * kBN * p.down_nb;
     const Elem* wd = reinterpret_cast<const Elem*>(p.wd) + (size_t)t.e * p.f * p.d +
-                     (size_t)k_lo * p.d + (size_t)n * kBN;
-    float* out = o_slice(p, ks) + (size_t)t.row0 * p.d + (size_t)n * kBN;
-    if (t.bm == 32) down_tile<32>(A, p.f, t.rows, wd, p.d, K, out, p.d, smem);
-    else if (t.bm == 64) down_tile<64>(A, p.f, t.rows, wd, p.d, K, out, p.d, smem);
-    else down_tile<128>(A, p.f, t.rows, wd, p.d, K, out, p.d, smem);
+                     (size_t)k_lo * p.d + n0;
+    float* out = o_slice(p, ks) + (size_t)t.row0 * p.d + n0;
+    down_any(t.bm, p.down_nb, A, p.f, t.rows, wd, p.d, K, out, p.d, smem);
   }
 
   // DOWN output rows of K slice ks: [T*k][d] fp32.
@@ -793,27 +832,24 @@ struct Stages {
 
   // Shared (always-on) experts: every token, weight 1, input x directly.
   static TASKFN void shared_up(const Params& p, int s, int m, int n, char* smem) {
-    const int r0 = m * 128;
-    const int rows = min(128, p.T - r0);
+    const int r0 = m * p.th;
+    const int rows = min(p.th, p.T - r0);
     const Elem* A = reinterpret_cast<const Elem*>(p.x) + (size_t)r0 * p.d;
     const size_t so = (size_t)s * p.d * p.fs + (size_t)n * kBN;
     const Elem* wg = reinterpret_cast<const Elem*>(p.sg) + so;
     const Elem* wu = reinterpret_cast<const Elem*>(p.su) + so;
     Elem* H = reinterpret_cast<Elem*>(p.Hs) + ((size_t)s * p.T + r0) * p.fs + (size_t)n * kBN;
-    if (rows <= 32) up_tile<32>(A, p.d, rows, wg, wu, p.fs, p.d, H, p.fs, smem);
-    else if (rows <= 64) up_tile<64>(A, p.d, rows, wg, wu, p.fs, p.d, H, p.fs, smem);
-    else up_tile<128>(A, p.d, rows, wg, wu, p.fs, p.d, H, p.fs, smem);
+    up_any(row_class(rows), A, p.d, rows, wg, wu, p.fs, p.d, H, p.fs, smem);
   }
 
   static TASKFN void shared_down(const Params& p, int s, int m, int n, char* smem) {
-    const int r0 = m * 128;
-    const int rows = min(128, p.T - r0);
+    const int r0 = m * p.th;
+    const int rows = min(p.th, p.T - r0);
+    const int n0 = n * kBN * p.down_nb;
     const Elem* A = reinterpret_cast<const Elem*>(p.Hs) + ((size_t)s * p.T + r0) * p.fs;
-    const Elem* wd = reinterpret_cast<const Elem*>(p.sd) + (size_t)s * p.fs * p.d + (size_t)n * kBN;
-    float* out = p.Ys + ((size_t)s * p.T + r0) * p.d + (size_t)n * kBN;
-    if (rows <= 32) down_tile<32>(A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem);
-    else if (rows <= 64) down_tile<64>(A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem);
-    else down_tile<128>(A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem);
+    const Elem* wd = reinterpret_cast<const Elem*>(p.sd) + (size_t)s * p.fs * p.d + n0;
+    float* out = p.Ys + ((size_t)s * p.T + r0) * p.d + n0;
+    down_any(row_class(rows), p.down_nb, A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem);
   }
 
   // ------------------------------------------------------------- combine

@@ -36,7 +36,7 @@ def _stream(device) -> ctypes.c_void_p:
 def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model",
               split_k: int = 0, max_workers: int = 0, fixed_mem_workers: int = 0,
               flags: int = 0, trace: Optional[torch.Tensor] = None,
-              timeout_ms: int = 0) -> Desc:
+              timeout_ms: int = 0, row_tile: int = 0) -> Desc:
     d = Desc()
     d.T, d.d, d.E, d.k, d.f = shape.T, shape.d, shape.E, shape.k, shape.f
     d.e_begin, d.e_end = shape.e_begin, shape.local_end
@@ -54,6 +54,7 @@ def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model
         d.trace_cap = trace.numel() // 4
         d.flags |= _abi.FLAG_TRACE
     d.timeout_ms = timeout_ms
+    d.row_tile = row_tile
     return d
 
 
@@ -119,14 +120,14 @@ class MoELayer:
                  mode: str = "dynamic", split: str = "cost_model", split_k: int = 0,
                  max_workers: int = 0, fixed_mem_workers: int = 0, flags: int = 0,
                  trace: Optional[torch.Tensor] = None, timeout_ms: int = 0,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, row_tile: int = 0):
         self.shape = shape
         dev = weights["w_gate"].device
         if dev.type != "cuda":
             raise ValueError("weights must be on a GPU")
         self.device = dev
         self.desc = make_desc(shape, mode, split, split_k, max_workers, fixed_mem_workers,
-                              flags, trace, timeout_ms)
+                              flags, trace, timeout_ms, row_tile)
         self._trace = trace
         et = _elem_dtype(shape)
         d, E, f, El = shape.d, shape.E, shape.f, shape.E_loc

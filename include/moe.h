@@ -110,6 +110,8 @@ typedef struct moe_desc {
   uint64_t* trace;    /* device buffer for MOE_FLAG_TRACE, or NULL          */
   int trace_cap;      /* records that fit in trace (3 x uint64 each)        */
   int timeout_ms;     /* device watchdog per wait; 0 = 2000 ms              */
+  int row_tile;       /* expert row-tile height 128 or 256 (bf16 only);
+                         0 = automatic (256 when T*k > 8192 in bf16)        */
 } moe_desc;
 
 /* Weights.  E_loc = e_end - e_begin.  Element type = desc.dtype.
@@ -157,13 +159,14 @@ typedef struct moe_info {
   int blocks_per_cu;    /* resident workgroups per CU for the megakernel   */
   int route_tiles;      /* router / position tiles (32 tokens each)        */
   int up_ntiles;        /* f / 128                                         */
-  int down_ntiles;      /* d / 128                                         */
+  int down_ntiles;      /* DOWN column tasks: d / 128, or d / 256 with 256-row tiles */
   int split_k;          /* DOWN split-K actually used                      */
   int permute_rows;     /* rows per permute task                           */
   int max_mtiles;       /* capacity of the expert row-tile table           */
   int max_tasks;        /* capacity of the ready queues                    */
   int route_splits;     /* router K slices per router tile                 */
   int combine_chunks;   /* combine tasks per 32-token tile (d / columns)   */
+  int row_tile;         /* expert row-tile height (128 or 256)             */
   size_t workspace_bytes;
 } moe_info;
 

@@ -17,14 +17,15 @@ def check_trace(raw, layer, routing):
     n_up = info["up_ntiles"]
     n_down = info["down_ntiles"]
     sk = info["split_k"]
-    pch = 128 // info["permute_rows"]
+    th = info["row_tile"]
+    pch = th // info["permute_rows"]
     counts = routing.expert_counts.cpu().numpy()
-    n_mt = int(sum((c + 127) // 128 for c in counts))
+    n_mt = int(sum((c + th - 1) // th for c in counts))
     ids, cnt = np.unique(tr["task"], return_counts=True)
     assert np.all(cnt == 1), "a task ran more than once"
     kinds = tr["kind"]
     pl = tr["payload"]
-    n_smt = (s.T + 127) // 128
+    n_smt = (s.T + th - 1) // th
     n_sup_n = (s.f_shared // 128) if s.n_shared else 0
     n_cc = info["combine_chunks"]
     expect = {ROUTE: n_rt * info["route_splits"], POS: n_rt, UP: n_mt * n_up,
@@ -67,7 +68,7 @@ def check_trace(raw, layer, routing):
     acc = 0
     for e in order:
         mt_base[e] = acc
-        acc += (int(counts[e]) + 127) // 128
+        acc += (int(counts[e]) + th - 1) // th
     offs = routing.offsets.cpu().numpy()
     idx = routing.topk_idx.cpu().numpy()
     spos = routing.slot_pos.cpu().numpy()
@@ -78,10 +79,10 @@ def check_trace(raw, layer, routing):
             if pos < 0:
                 continue
             e = int(idx[tok, j]) - s.e_begin
-            mt = mt_base[e] + (pos - int(offs[e])) // 128
+            mt = mt_base[e] + (pos - int(offs[e])) // th
             comb_need[tok // 32] = max(comb_need[tok // 32], down_end[mt])
         if s.n_shared:
-            comb_need[tok // 32] = max(comb_need[tok // 32], sdown_end[tok // 128])
+            comb_need[tok // 32] = max(comb_need[tok // 32], sdown_end[tok // th])
     for t, k, p in zip(tr["task"], kinds, pl):
         t, p = int(t), int(p)
         if k == UP:

@@ -52,6 +52,48 @@ def test_mid_bf16_all_modes(mid, mode, split):
     run_and_check(MID, g, n, mode, split, label="mid_bf16")
 
 
+# 256-row expert tiles (chosen automatically for large bf16 layers), forced
+# on a small layer whose hot experts span several tiles with ragged tails,
+# with a shared expert and 256-column DOWN tasks.
+BIG_TILE = LayerShape(T=1100, d=512, E=8, k=2, f=384, n_shared=1, f_shared=256, zipf_s=1.2)
+
+
+@pytest.fixture(scope="module")
+def big_tile():
+    g = gen_inputs(BIG_TILE, "big_tile", 6)
+    return g, host_inputs(g)
+
+
+@pytest.mark.parametrize("mode,split", MODES)
+def test_row_tile_256_all_modes(big_tile, mode, split):
+    g, n = big_tile
+    _, r, ro = run_and_check(BIG_TILE, g, n, mode, split, label="rt256", row_tile=256)
+    c = ro["counts"]
+    assert c.max() > 512 and (c % 256 != 0).all()
+
+
+def test_row_tile_256_trace_and_modes_agree(big_tile):
+    from analysis_util import check_trace
+    g, n = big_tile
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(BIG_TILE, g, mode="dynamic", trace=trace, timeout_ms=3000, row_tile=256)
+    assert layer.info["row_tile"] == 256 and layer.info["down_ntiles"] == BIG_TILE.d // 256
+    y, r = layer(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+    y2 = MoELayer(BIG_TILE, g, mode="static", split="fixed", row_tile=256)(g["x"], check_errors=True)
+    assert torch.equal(y, y2)
+
+
+def test_row_tile_256_split_k_and_odd_d():
+    # d = 384 is not a multiple of 256: 256-row tiles with 128-column DOWN tasks
+    s = LayerShape(T=700, d=384, E=4, k=2, f=1024, zipf_s=0.5)
+    g = gen_inputs(s, "rt256_odd", 7)
+    for sk in (1, 3):
+        run_and_check(s, g, None, "dynamic", "cost_model", split_k=sk, label="rt256sk%d" % sk,
+                      row_tile=256)
+
+
 @pytest.mark.parametrize("mode,split", [("dynamic", "cost_model"), ("static", "fixed"),
                                         ("multi_kernel", "none")])
 def test_local_expert_range(mode, split):
@@ -92,6 +134,7 @@ def test_all_tokens_one_expert():
     g["router_bias"] = b
     _, r, ro = run_and_check(s, g, None, "dynamic", "cost_model", label="hot_expert")
     assert int(ro["counts"][5]) == 700
+    run_and_check(s, g, None, "dynamic", "cost_model", label="hot_expert_rt256", row_tile=256)
 
 
 def test_few_workers():
