@@ -12,6 +12,7 @@
 #include "params.hpp"
 #include "tile.hpp"
 #include "tile2.hpp"
+#include "tile3.hpp"
 
 namespace moe {
 
@@ -71,6 +72,11 @@ struct GemmSel {
 template <int BM, int NB>
 struct GemmSel<bf16_t, BM, NB> {
   using T = Tile2<BM, NB, tile2_stages(BM, NB)>;
+};
+// 256-row tiles: 32-deep stages with the loads interleaved into the MFMAs
+template <int NB>
+struct GemmSel<bf16_t, 256, NB> {
+  using T = Tile3<NB>;
 };
 
 // Router tiles (32 tokens x 128 experts): a 4-stage ring for bf16 when the
@@ -699,6 +705,7 @@ struct Stages {
   static DEV void up_tile(const Elem* A, int lda, int rows, const Elem* wg, const Elem* wu,
                           int ldb, int K, Elem* Hout, int ldh, char* smem) {
     using TL = typename GemmSel<Elem, BM, 2>::T;
+    static_assert(TL::LDS_BYTES <= kSmemTile, "UP tile fits the tile LDS");
     typename TL::Args g;
     g.A = A;
     g.lda = lda;
@@ -741,6 +748,7 @@ struct Stages {
   static DEV void down_tile(const Elem* A, int lda, int rows, const Elem* wd, int ldb, int K,
                             float* out, int ldo, char* smem) {
     using TL = typename GemmSel<Elem, BM, NB>::T;
+    static_assert(TL::LDS_BYTES <= kSmemTile, "DOWN tile fits the tile LDS");
     typename TL::Args g;
     g.A = A;
     g.lda = lda;

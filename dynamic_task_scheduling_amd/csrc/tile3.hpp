@@ -1,0 +1,280 @@
+// tile3.hpp -- 256-row bf16 GEMM tile for gfx950 with global->LDS loads
+// interleaved into the MFMA stream.
+//
+// C[256, 128] (x NB matrices sharing A) = A[256, K] * B[K, 128], bf16 in,
+// fp32 accumulate, v_mfma_f32_32x32x16_bf16.  Four waves in a 2 x 2 grid;
+// each wave owns 128 rows x 64 columns of every matrix (FM = 4, FN = 2), the
+// shape that reads the fewest LDS bytes per MFMA with 256 accumulators.
+//
+// Why a second tile: with the loads of a K stage issued in one burst, a wave
+// sits on its queued global_load_lds instructions while its matrix pipe
+// idles (measured: the loads alone doubled the MFMA-only loop time).  Here a
+// stage is 32 deep, the ring holds S = 4 stages (6 with one B matrix), and
+// the loads of stage kt + S - 1 are issued one at a time between the MFMAs
+// of stage kt, so the matrix pipe keeps running while the address unit
+// drains them, and every load has two full stages of MFMA work to land.
+// The loop body has no data-dependent branch: past the last stage the ring
+// re-reads the last stage into the slot that is free anyway, so the
+// outstanding-load count before each wait is a constant.
+//
+// LDS layouts (one stage):
+//   A: 256 rows x 64 bytes (32 bf16 of K).  16-byte chunk c of row m sits at
+//      position c ^ ((m >> 1) & 3): the eight rows one 8-lane phase of a
+//      fragment read touches fall on eight distinct 16-byte bank groups.
+//   B: 32 rows (K) x 256 bytes (128 bf16 of N), chunk c of row k at
+//      c ^ 2 * (k & 3), read with ds_read_b64_tr_b16 into the K-contiguous
+//      MFMA operand (as in tile2.hpp).
+#pragma once
+#include "tile2.hpp"
+
+namespace moe {
+
+// One 16-byte global->LDS load per lane from sbase + voff to the uniform LDS
+// address lds (+ 16 * lane).  lds must already be wave-uniform (SGPR).
+DEV void dma16u(uint32_t voff, uint64_t sbase, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(sbase));
+}
+
+DEV uint64_t uniform_u64(uint64_t v) {
+  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+}
+
+template <int NB>
+struct Tile3 {
+  static constexpr int BM = 256;
+  static constexpr int BN = kBN;
+  static constexpr int BK = 32;
+  static constexpr int WM = 2, WN = 2;
+  static constexpr int WTM = 128, WTN = 64;
+  static constexpr int FM = 4, FN = 2;
+  static constexpr int A_BYTES = BM * 64;            // 16 KB
+  static constexpr int B_BYTES = BK * 256;           // 8 KB per matrix
+  static constexpr int STAGE = A_BYTES + NB * B_BYTES;
+  static constexpr int S = (147456 / STAGE) > 6 ? 6 : (147456 / STAGE);
+  static constexpr int LDS_BYTES = S * STAGE;
+  static constexpr int A_INST = 4;                   // per wave per stage (1 KB each)
+  static constexpr int B_INST = 2;                   // per wave per stage per matrix
+  static constexpr int LOADS = A_INST + NB * B_INST;
+  static constexpr int MF_PER_KK = NB * FM * FN;     // MFMAs per 16-deep step
+  static_assert(S >= 3 && (S - 2) * LOADS < 64, "ring depth / vmcnt range");
+  static_assert(LOADS <= MF_PER_KK, "one load slot per MFMA");
+
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  using Frag = f32x16_t;
+  static constexpr int FRAG = 16;
+  using Acc = Frag[NB][FM][FN];
+
+  struct Args {
+    const bf16_t* A;    // row 0 of the tile, K column 0
+    int lda;
+    int a_rows;         // valid rows (>= 1); later rows repeat the last one
+    const bf16_t* B[NB];
+    int ldb;
+    int K;              // multiple of 32
+  };
+
+  struct Lane {
+    uint32_t a_src[A_INST];
+    uint32_t b_src[B_INST];
+    uint32_t a_rd[FM][2];
+    uint32_t b_rd[FN];
+    uint32_t a_dst, b_dst;   // wave-uniform
+  };
+
+  struct Frags {
+    bf16x8_t a[FM];
+    bf16x8_t b[NB][FN];
+  };
+
+  static DEV void make_lane(const Args& g, int tid, Lane& L) {
+    const int wave = tid >> 6, lane = tid & 63;
+    // A: instruction i covers rows 16 i .. 16 i + 15; lane -> row l / 4,
+    // LDS chunk l % 4, which holds global chunk (l % 4) ^ ((m >> 1) & 3).
+#pragma unroll
+    for (int ii = 0; ii < A_INST; ++ii) {
+      const int i = wave * A_INST + ii;
+      const int m = 16 * i + (lane >> 2);
+      const int c = (lane & 3) ^ ((m >> 1) & 3);
+      const int mr = m < g.a_rows ? m : g.a_rows - 1;
+      L.a_src[ii] = (uint32_t)mr * (uint32_t)g.lda * 2u + (uint32_t)c * 16u;
+    }
+    // B: instruction i covers K rows 4 i .. 4 i + 3.
+#pragma unroll
+    for (int ii = 0; ii < B_INST; ++ii) {
+      const int i = wave * B_INST + ii;
+      const int k = 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ (2 * (k & 3));
+      L.b_src[ii] = (uint32_t)k * (uint32_t)g.ldb * 2u + (uint32_t)c * 16u;
+    }
+    L.a_dst = __builtin_amdgcn_readfirstlane((uint32_t)(wave * A_INST) * 1024u);
+    L.b_dst = __builtin_amdgcn_readfirstlane((uint32_t)A_BYTES + (uint32_t)(wave * B_INST) * 1024u);
+    const int wm = wave / WN, wn = wave % WN;
+    const int l16 = lane & 15, lg = lane >> 4, l32 = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = wm * WTM + fm * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int c = kk * 2 + lh;
+        L.a_rd[fm][kk] = (uint32_t)(m * 64 + ((c ^ ((m >> 1) & 3)) << 4));
+      }
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int n = wn * WTN + fn * 32 + 16 * (lg & 1) + 4 * (l16 & 3);
+      const int kl = 8 * (lg >> 1) + (l16 >> 2);
+      const int c = n >> 3, half = (n >> 2) & 1;
+      L.b_rd[fn] = (uint32_t)(A_BYTES + kl * 256 + ((c ^ (2 * (kl & 3))) << 4) + half * 8);
+    }
+  }
+
+  // Load j (0 <= j < LOADS) of a stage: A instructions first, then each B
+  // matrix's.  `stage` is the uniform LDS address of the ring slot.
+  static DEV void issue_one(const Lane& L, int j, uint64_t a_base, const uint64_t* b_base,
+                            uint32_t stage) {
+    if (j < A_INST) {
+      dma16u(L.a_src[j], a_base, stage + L.a_dst + j * 1024);
+    } else {
+      const int mtx = (j - A_INST) / B_INST, ii = (j - A_INST) % B_INST;
+      dma16u(L.b_src[ii], b_base[mtx], stage + L.b_dst + mtx * B_BYTES + ii * 1024);
+    }
+  }
+
+  template <int KK>
+  static DEV void load_frags(const Lane& L, uint32_t stage, Frags& f) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      f.a[fm] = *reinterpret_cast<const LDS_AS bf16x8_t*>((uintptr_t)(stage + L.a_rd[fm][KK]));
+#pragma unroll
+    for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const uint32_t b = stage + L.b_rd[fn] + mtx * B_BYTES + KK * 4096;
+        const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(uintptr_t)b);
+        const bf16x4_t v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(uintptr_t)(b + 1024));
+        f.b[mtx][fn] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+  }
+
+  static DEV void mfma_one(const Frags& f, Acc& acc, int i) {
+    const int mtx = i / (FM * FN), fm = (i / FN) % FM, fn = i % FN;
+    acc[mtx][fm][fn] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[fm], f.b[mtx][fn], acc[mtx][fm][fn], 0, 0, 0);
+  }
+
+  static DEV void mfmas(const Frags& f, Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < MF_PER_KK; ++i) mfma_one(f, acc, i);
+  }
+
+  // The MFMAs of one step with the LOADS loads of a stage spread between
+  // them (load j after MFMA j * MF_PER_KK / LOADS); sched_barrier keeps the
+  // compiler from regrouping them.
+  static DEV void mfmas_with_loads(const Frags& f, Acc& acc, const Lane& L, uint64_t a_base,
+                                   const uint64_t* b_base, uint32_t stage) {
+#pragma unroll
+    for (int i = 0; i < MF_PER_KK; ++i) {
+      mfma_one(f, acc, i);
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j)
+        if (j * MF_PER_KK / LOADS == i) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_one(L, j, a_base, b_base, stage);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  }
+
+  // Stage kt + 1 has landed (S - 2 newer stages may still be in flight) and
+  // every wave is done reading the slot the next loads refill.
+  static DEV void stage_barrier() {
+    wait_vmcnt<(S - 2) * LOADS>();
+    __builtin_amdgcn_s_waitcnt((0x3f & 0xf) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
+  // Full K loop; ends with every load drained and a barrier, so the caller
+  // may reuse `smem`.
+  static DEV void run(const Args& g, char* smem, Acc& acc) {
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[m][fm][fn] = Frag{};
+    Lane L;
+    make_lane(g, opaque_tid(), L);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    const uint64_t a0 = uniform_u64((uint64_t)(uintptr_t)g.A);
+    uint64_t b0[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) b0[m] = uniform_u64((uint64_t)(uintptr_t)g.B[m]);
+    const uint64_t b_step = (uint64_t)BK * (uint64_t)g.ldb * 2u;
+    const int nk = g.K / BK;
+    // stage kt's global bases (stages past the end re-read the last one)
+    auto bases = [&](int kt, uint64_t& a, uint64_t* b) __attribute__((always_inline)) {
+      const int kc = kt < nk ? kt : nk - 1;
+      a = a0 + (uint64_t)kc * (BK * 2);
+#pragma unroll
+      for (int m = 0; m < NB; ++m) b[m] = b0[m] + (uint64_t)kc * b_step;
+    };
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) {
+      uint64_t a, b[NB];
+      bases(s, a, b);
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) issue_one(L, j, a, b, base + s * STAGE);
+    }
+    stage_barrier();
+    Frags f0, f1;
+    load_frags<0>(L, base, f0);
+    uint32_t cur = base;                          // slot of stage kt
+    uint32_t refill = base + (S - 1) * STAGE;     // slot of stage kt + S - 1
+    for (int kt = 0; kt < nk; ++kt) {
+      uint64_t a, b[NB];
+      bases(kt + S - 1, a, b);
+      load_frags<1>(L, cur, f1);
+      mfmas_with_loads(f0, acc, L, a, b, refill);
+      const uint32_t next = (cur + STAGE == base + S * STAGE) ? base : cur + STAGE;
+      stage_barrier();
+      load_frags<0>(L, next, f0);
+      mfmas(f1, acc);
+      refill = cur;
+      cur = next;
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  // Visit every accumulator position: fn(row, col, fm, fn, i).  32x32
+  // result: column lane%32, rows 8*(i/4) + 4*(lane/32) + i%4.
+  template <typename F>
+  static DEV void for_each(F&& fn) {
+    const int tid_ = opaque_tid();
+    const int lane = tid_ & 63;
+    const int wave = tid_ >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fnn = 0; fnn < FN; ++fnn)
+#pragma unroll
+        for (int i = 0; i < FRAG; ++i) {
+          const int row = wm * WTM + fm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+          const int col = wn * WTN + fnn * 32 + (lane & 31);
+          fn(row, col, fm, fnn, i);
+        }
+  }
+};
+
+}  // namespace moe
