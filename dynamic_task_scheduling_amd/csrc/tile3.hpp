@@ -64,8 +64,14 @@ struct Tile3 {
   static constexpr int B_INST = 2;                   // per wave per stage per matrix
   static constexpr int LOADS = A_INST + NB * B_INST;
   static constexpr int MF_PER_KK = NB * FM * FN;     // MFMAs per 16-deep step
-  static_assert(S >= 3 && (S - 2) * LOADS < 64, "ring depth / vmcnt range");
-  static_assert(LOADS <= MF_PER_KK, "one load slot per MFMA");
+  // loads of a stage issued in the first / second half of an iteration
+  static constexpr int LOADS0 = (LOADS + 1) / 2;
+  static constexpr int LOADS1 = LOADS - LOADS0;
+  // loads still allowed in flight when stage kt + 1 must have landed: the
+  // S - 3 stages after it, and the first half of the stage after those
+  static constexpr int NEWER = (S - 3) * LOADS + LOADS0;
+  static_assert(S >= 3 && NEWER < 64, "ring depth / vmcnt range");
+  static_assert(LOADS0 <= MF_PER_KK, "one load slot per MFMA");
 
   typedef float f32x16_t __attribute__((ext_vector_type(16)));
   using Frag = f32x16_t;
@@ -176,28 +182,29 @@ struct Tile3 {
     for (int i = 0; i < MF_PER_KK; ++i) mfma_one(f, acc, i);
   }
 
-  // The MFMAs of one step with the LOADS loads of a stage spread between
-  // them (load j after MFMA j * MF_PER_KK / LOADS); sched_barrier keeps the
-  // compiler from regrouping them.
+  // The MFMAs of one step with loads J0 .. J0 + NJ - 1 of a stage spread
+  // evenly between them; sched_barrier keeps the compiler from regrouping
+  // them.
+  template <int J0, int NJ>
   static DEV void mfmas_with_loads(const Frags& f, Acc& acc, const Lane& L, uint64_t a_base,
                                    const uint64_t* b_base, uint32_t stage) {
 #pragma unroll
     for (int i = 0; i < MF_PER_KK; ++i) {
       mfma_one(f, acc, i);
 #pragma unroll
-      for (int j = 0; j < LOADS; ++j)
-        if (j * MF_PER_KK / LOADS == i) {
+      for (int j = 0; j < NJ; ++j)
+        if (j * MF_PER_KK / NJ == i) {
           __builtin_amdgcn_sched_barrier(0);
-          issue_one(L, j, a_base, b_base, stage);
+          issue_one(L, J0 + j, a_base, b_base, stage);
           __builtin_amdgcn_sched_barrier(0);
         }
     }
   }
 
-  // Stage kt + 1 has landed (S - 2 newer stages may still be in flight) and
-  // every wave is done reading the slot the next loads refill.
+  // Stage kt + 1 has landed (later loads may still be in flight) and every
+  // wave is done reading the slot the next loads refill.
   static DEV void stage_barrier() {
-    wait_vmcnt<(S - 2) * LOADS>();
+    wait_vmcnt<NEWER>();
     __builtin_amdgcn_s_waitcnt((0x3f & 0xf) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -235,7 +242,11 @@ struct Tile3 {
 #pragma unroll
       for (int j = 0; j < LOADS; ++j) issue_one(L, j, a, b, base + s * STAGE);
     }
-    stage_barrier();
+    // stage 0 landed: the later prologue stages may be in flight
+    wait_vmcnt<(S - 2) * LOADS>();
+    __builtin_amdgcn_s_waitcnt((0x3f & 0xf) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     Frags f0, f1;
     load_frags<0>(L, base, f0);
     uint32_t cur = base;                          // slot of stage kt
@@ -244,11 +255,12 @@ struct Tile3 {
       uint64_t a, b[NB];
       bases(kt + S - 1, a, b);
       load_frags<1>(L, cur, f1);
-      mfmas_with_loads(f0, acc, L, a, b, refill);
+      mfmas_with_loads<0, LOADS0>(f0, acc, L, a, b, refill);
       const uint32_t next = (cur + STAGE == base + S * STAGE) ? base : cur + STAGE;
       stage_barrier();
       load_frags<0>(L, next, f0);
-      mfmas(f1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas_with_loads<LOADS0, LOADS1>(f1, acc, L, a, b, refill);
       refill = cur;
       cur = next;
     }
