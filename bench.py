@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--split", default="cost_model")
+    ap.add_argument("--combine", default="auto", choices=["auto", "scatter", "tasks"],
+                    help="weighted combine: scatter-add in the DOWN epilogue, or combine tasks")
     ap.add_argument("--modes", default="dynamic,static,multi_kernel")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup+steps of the first mode in --modes only (for rocprofv3)")
@@ -114,7 +116,7 @@ def main():
     torch.cuda.synchronize()
 
     def make_layers(mode, split, trace=None):
-        return [MoELayer(s, t, mode=mode, split=split, trace=trace)
+        return [MoELayer(s, t, mode=mode, split=split, trace=trace, combine=args.combine)
                 for s, t in zip(wl.layers, tensors)]
 
     ys = [torch.empty((s.T, s.d), dtype=torch.float32, device=dev) for s in wl.layers]
@@ -188,7 +190,8 @@ def main():
     sched = {}
     if not args.profile_only:
         trace = torch.zeros(4 * 200000, dtype=torch.int64, device=dev)
-        Lt = MoELayer(wl.layers[0], tensors[0], mode="dynamic", split=args.split, trace=trace)
+        Lt = MoELayer(wl.layers[0], tensors[0], mode="dynamic", split=args.split, trace=trace,
+                      combine=args.combine)
         Lt(tensors[0]["x"], ys[0])
         torch.cuda.synchronize()
         tr = analysis.decode_trace(trace.cpu().numpy())
@@ -222,7 +225,7 @@ def main():
         "config": {"workload": wl.name, "layers": len(wl.layers), "tokens_per_step": tot_T,
                    "T": wl.layers[0].T if len(wl.layers) == 1 else "per-layer",
                    "d": wl.layers[0].d, "E": wl.layers[0].E, "k": wl.layers[0].k,
-                   "f": wl.layers[0].f, "split": args.split},
+                   "f": wl.layers[0].f, "split": args.split, "combine": args.combine},
         "tflops": tflops,
         "pct_mfma_peak": 100.0 * tflops / peak_fl,
         "hbm_gbs": gbs,

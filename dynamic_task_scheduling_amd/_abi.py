@@ -11,6 +11,7 @@ c_int, c_uint, c_void_p, c_size_t = ctypes.c_int, ctypes.c_uint, ctypes.c_void_p
 MOE_F32, MOE_BF16 = 0, 1
 MODES = {"dynamic": 0, "static": 1, "multi_kernel": 2}
 SPLITS = {"cost_model": 0, "fixed": 1, "none": 2}
+COMBINES = {"auto": 0, "scatter": 1, "tasks": 2}
 FLAG_CHECK, FLAG_TRACE, FLAG_PHASE_SYNC, FLAG_REF_SYNC, FLAG_NO_STEAL = 0x1, 0x2, 0x4, 0x8, 0x10
 
 ERRORS = {
@@ -30,7 +31,7 @@ class Desc(ctypes.Structure):
         ("dtype", c_int), ("mode", c_int), ("split_policy", c_int),
         ("fixed_mem_workers", c_int), ("split_k", c_int), ("max_workers", c_int),
         ("flags", c_uint), ("trace", c_void_p), ("trace_cap", c_int), ("timeout_ms", c_int),
-        ("row_tile", c_int),
+        ("row_tile", c_int), ("combine", c_int),
     ]
 
 
@@ -49,6 +50,7 @@ class Info(ctypes.Structure):
                 ("route_tiles", c_int), ("up_ntiles", c_int), ("down_ntiles", c_int),
                 ("split_k", c_int), ("permute_rows", c_int), ("max_mtiles", c_int),
                 ("max_tasks", c_int), ("route_splits", c_int), ("combine_chunks", c_int), ("row_tile", c_int),
+                ("combine", c_int),
                 ("workspace_bytes", c_size_t)]
 
 

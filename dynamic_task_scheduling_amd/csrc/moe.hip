@@ -50,6 +50,7 @@ int validate(const moe_desc* d) {
   if (mt * 128 >= (1ll << kKindShift)) return MOE_ERR_UNSUPPORTED;  // permute payloads
   if (d->row_tile != 0 && d->row_tile != 128 && d->row_tile != 256) return MOE_ERR_ARG;
   if (d->row_tile == 256 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->combine < MOE_COMBINE_AUTO || d->combine > MOE_COMBINE_TASKS) return MOE_ERR_ARG;
   return MOE_OK;
 }
 
@@ -92,9 +93,10 @@ void make_layout(const moe_desc* d, Layout* L) {
   p.n_up_n = d->f / kBN;
   p.n_down_n = d->d / (kBN * p.down_nb);
   int sk = d->split_k;
-  // automatic DOWN split-K: one slice per 7168 of f (measured: decode-shaped
-  // f = 14336 is fastest with 2; every slice adds fp32 atomics to y)
-  if (sk == 0) sk = std::max(1, std::min(8, d->f / 7168));
+  // automatic DOWN split-K: one slice per 3584 of f (measured on the
+  // decode-shaped f = 14336: 4 slices shorten the last wave of DOWN tasks,
+  // the tail of an HBM-bound layer; 8 add more partial traffic than they save)
+  if (sk == 0) sk = std::max(1, std::min(8, d->f / 3584));
   p.splitk = std::min(sk, p.n_up_n);
   p.n_s_up_n = p.fs / kBN;
   p.n_smt = (d->T + p.th - 1) / p.th;
@@ -115,6 +117,13 @@ void make_layout(const moe_desc* d, Layout* L) {
   p.max_perm = (int)((R + pr - 1) / pr + p.max_mt);
   p.n_sup = p.n_shared * p.n_smt * p.n_s_up_n;
   p.n_sdown = p.n_shared * p.n_smt * p.n_down_n;
+  // Combine: a layer with at most 4096 routed rows scatter-adds in the DOWN
+  // epilogue (no extra stage after the last DOWN tile; measured faster on
+  // the decode-shaped and 16-layer stress workloads); larger layers write O
+  // rows and sum them per token in combine tasks (fixed order, none of the
+  // atomic traffic on y that dominated large layers' DOWN time).
+  p.comb_scatter = d->combine == MOE_COMBINE_SCATTER ||
+                   (d->combine == MOE_COMBINE_AUTO && (long long)d->T * d->k <= 4096);
   // combine chunks: the widest of 512 / 256 / 128 columns that divides d
   // and still gives about two combine tasks per CU; small-T layers get
   // narrow chunks, so the combine that follows the last DOWN tile spreads
@@ -217,13 +226,13 @@ int dev_info(int dev, DevInfo* out) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return MOE_ERR_HIP;
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_dynamic<float>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_dynamic<float, false>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
     di.bpc[0][0] = b;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_static<float>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_static<float, false>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
     di.bpc[0][1] = b;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_dynamic<bf16_t>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_dynamic<bf16_t, false>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
     di.bpc[1][0] = b;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_static<bf16_t>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_static<bf16_t, false>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
     di.bpc[1][1] = b;
     di.cus = cus;
   }
@@ -259,9 +268,15 @@ int launch_layer(const moe_desc* d, Params& p, hipStream_t s) {
   hipLaunchKernelGGL(k_reset, dim3(reset_blocks), dim3(kThreads), 0, s, p);
   HIP_OK(hipGetLastError());
   if (d->mode == MOE_DYNAMIC) {
-    hipLaunchKernelGGL(k_dynamic<Elem>, dim3(p.workers), dim3(kThreads), 0, s, p);
+    if (p.comb_scatter)
+      hipLaunchKernelGGL((k_dynamic<Elem, true>), dim3(p.workers), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_dynamic<Elem, false>), dim3(p.workers), dim3(kThreads), 0, s, p);
   } else if (d->mode == MOE_STATIC_PARTITION) {
-    hipLaunchKernelGGL(k_static<Elem>, dim3(p.workers), dim3(kThreads), 0, s, p);
+    if (p.comb_scatter)
+      hipLaunchKernelGGL((k_static<Elem, true>), dim3(p.workers), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_static<Elem, false>), dim3(p.workers), dim3(kThreads), 0, s, p);
   } else {
     hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt * p.rsk), dim3(kThreads), 0, s, p);
     HIP_OK(hipGetLastError());
@@ -276,7 +291,8 @@ int launch_layer(const moe_desc* d, Params& p, hipStream_t s) {
     hipLaunchKernelGGL(k_stage_down<Elem>, dim3(p.max_mt * p.n_down_n * p.splitk + p.n_sdown),
                        dim3(kThreads), 0, s, p);
     HIP_OK(hipGetLastError());
-    hipLaunchKernelGGL(k_stage_comb<Elem>, dim3(p.n_rt * p.n_cc), dim3(kThreads), 0, s, p);
+    if (!p.comb_scatter)
+      hipLaunchKernelGGL(k_stage_comb<Elem>, dim3(p.n_rt * p.n_cc), dim3(kThreads), 0, s, p);
   }
   HIP_OK(hipGetLastError());
   return MOE_OK;
@@ -357,6 +373,7 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->route_splits = L.p.rsk;
   info->combine_chunks = L.p.n_cc;
   info->row_tile = L.p.th;
+  info->combine = L.p.comb_scatter ? MOE_COMBINE_SCATTER : MOE_COMBINE_TASKS;
   info->workspace_bytes = L.total;
   return MOE_OK;
 }

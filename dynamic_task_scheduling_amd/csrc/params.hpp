@@ -81,6 +81,8 @@ struct Params {
   int max_mt;      // capacity of the row-tile table
   int max_perm;    // capacity of the permute list
   int n_sup, n_sdown;
+  int comb_scatter; // 1: DOWN tiles scatter-add w * (H Wd) into y (small layers);
+                    // 0: DOWN tiles write O rows, combine tasks sum them
   int comb_cols;   // y columns per combine task (divides d)
   int n_cc;        // combine chunks per token tile = d / comb_cols
   int q_cap;       // slots per queue

@@ -247,7 +247,7 @@ struct Sched {
     const int n_perm = ld_relaxed(cw(p, CW_NPERM));
     const bool split = p.split_policy != 2;
     const int n_comp = n_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup + p.n_sdown +
-                       p.n_rt * p.n_cc;
+                       (p.comb_scatter ? 0 : p.n_rt * p.n_cc);
     publish_fence();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -313,7 +313,7 @@ struct Sched {
         // "positions pending" unit (k_reset) by that many tiles
         if (threadIdx.x == 0) {
           const int delta = nd * p.n_down_n * p.splitk - 1;
-          s_tmp[0] = (add_relaxed(p.cnt_comb + pl, delta) + delta == 0);
+          s_tmp[0] = !p.comb_scatter && (add_relaxed(p.cnt_comb + pl, delta) + delta == 0);
         }
         __syncthreads();
         const bool comb_ready = s_tmp[0] != 0;
@@ -353,8 +353,10 @@ struct Sched {
         const int mt = r / p.n_down_n;
         S::down(p, mt, r % p.n_down_n, ks, smem);
         *t_body = rtc();
-        const MTile t = p.mtiles[mt];
-        combine_arrive_rows(p, t.row0, t.rows, dyn);
+        if (!p.comb_scatter) {
+          const MTile t = p.mtiles[mt];
+          combine_arrive_rows(p, t.row0, t.rows, dyn);
+        }
         break;
       }
       case TK_SUP: {
@@ -372,7 +374,7 @@ struct Sched {
         const int sm = pl / p.n_down_n;
         S::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem);
         *t_body = rtc();
-        combine_arrive_shared(p, sm % p.n_smt, dyn);
+        if (!p.comb_scatter) combine_arrive_shared(p, sm % p.n_smt, dyn);
         break;
       }
       case TK_COMB: {
@@ -388,8 +390,13 @@ struct Sched {
 };
 
 // ------------------------------------------------------------- dynamic
-template <typename Elem>
-__global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
+// SCAT: the layer's combine mode as a compile-time constant, so each
+// instantiation holds only its own DOWN epilogue and combine code (the
+// persistent kernel's register allocation covers every task type at once).
+template <typename Elem, bool SCAT>
+__global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p_in) {
+  Params p = p_in;
+  p.comb_scatter = SCAT;
   __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
   __shared__ int s_tmp[4];
   __shared__ int s_worker;
@@ -445,8 +452,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
 }
 
 // -------------------------------------------------------------- static
-template <typename Elem>
-__global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
+template <typename Elem, bool SCAT>
+__global__ __launch_bounds__(kThreads, 1) void k_static(Params p_in) {
+  Params p = p_in;
+  p.comb_scatter = SCAT;
   __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
   __shared__ int s_tmp[4];
   if (threadIdx.x == 0) s_tmp[3] = add_relaxed(cw(p, CW_TICKET), 1);
@@ -488,6 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
     if (!grid_barrier(p, gen, s_tmp)) return;
     for (int i = w; i < n_down + p.n_sdown; i += W)
       exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
+    if (p.comb_scatter) return;
     if (!grid_barrier(p, gen, s_tmp)) return;
     for (int i = w; i < p.n_rt * p.n_cc; i += W) exec(make_task(TK_COMB, i));
     return;
@@ -523,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
     consume_fence();
     exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
   }
-  for (int i = w; i < p.n_rt * p.n_cc; i += W) {
+  for (int i = w; i < (p.comb_scatter ? 0 : p.n_rt * p.n_cc); i += W) {
     if (threadIdx.x == 0) s_tmp[1] = wait_zero(p, p.cnt_comb + i / p.n_cc);
     __syncthreads();
     const bool ok = s_tmp[1];

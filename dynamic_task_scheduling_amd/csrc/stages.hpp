@@ -270,6 +270,15 @@ struct Stages {
     const int rows = min(kTB, p.T - t0);
     // the bias load is issued first, so its latency hides under the GEMM
     const float bias_v = (p.rsk == 1 && p.bias && (int)threadIdx.x < p.E) ? p.bias[threadIdx.x] : 0.f;
+    // scatter-add combine: this slice zeroes its share of the tile's y rows
+    // (rows ks, ks + rsk, ...), which the DOWN tiles then accumulate into
+    if (p.comb_scatter) {
+      for (int r = ks; r < rows; r += p.rsk) {
+        float* yr = p.y + (size_t)(t0 + r) * p.d;
+        for (int i = threadIdx.x; i < p.d / 4; i += kThreads)
+          st_wt16(yr, i * 16, make_uint4(0, 0, 0, 0));
+      }
+    }
     const int Ks = p.d / p.rsk;
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);     // [32][E]
     float* part = p.rsk > 1 ? route_part_block(p, rt, ks) : nullptr;
@@ -744,9 +753,14 @@ struct Stages {
   // element is ever written twice and no atomics are needed.
   // NB = 2: two adjacent 128-column blocks of Wd share the A tile (a
   // 256-column task), written as two consecutive column blocks of Out.
+  // scatter (small layers): instead, out[tok(r), cols] += wt(r) * (A Wd)[r, :]
+  // with fp32 atomics -- the weighted scatter-add combine, fused into the
+  // DOWN epilogue; tok / wt of the tile's rows come from the LDS table
+  // down_rows() filled before the tile (so nothing extra stays live across
+  // the K loop).
   template <int BM, int NB>
   static DEV void down_tile(const Elem* A, int lda, int rows, const Elem* wd, int ldb, int K,
-                            float* out, int ldo, char* smem) {
+                            float* out, int ldo, char* smem, bool scatter = false) {
     using TL = typename GemmSel<Elem, BM, NB>::T;
     static_assert(TL::LDS_BYTES <= kSmemTile, "DOWN tile fits the tile LDS");
     typename TL::Args g;
@@ -773,10 +787,21 @@ struct Stages {
         st[row * SLD + col] = acc[m][fm][fn][i];
       });
       __syncthreads();
-      for (int i = threadIdx.x; i < rows * CPR; i += kThreads) {
-        const int r = i / CPR, c = i % CPR;
-        st_wt16(out + (size_t)r * ldo + m * kBN, c * 16,
-                *reinterpret_cast<const uint4*>(st + r * SLD + c * 4));
+      if (scatter) {
+        // one column per thread: each atomic instruction covers 64
+        // consecutive floats of one token row
+        const int* s_tok = down_rows_tok();
+        const float* s_wt = down_rows_wt();
+        for (int i = threadIdx.x; i < rows * kBN; i += kThreads) {
+          const int r = i / kBN, c = i % kBN;
+          unsafeAtomicAdd(out + (size_t)s_tok[r] * ldo + m * kBN + c, s_wt[r] * st[r * SLD + c]);
+        }
+      } else {
+        for (int i = threadIdx.x; i < rows * CPR; i += kThreads) {
+          const int r = i / CPR, c = i % CPR;
+          st_wt16(out + (size_t)r * ldo + m * kBN, c * 16,
+                  *reinterpret_cast<const uint4*>(st + r * SLD + c * 4));
+        }
       }
       __syncthreads();
     }
@@ -791,17 +816,35 @@ struct Stages {
     else if (bm == 128 || !TR::kBf16) f(std::integral_constant<int, 128>{});
     else if constexpr (TR::kBf16) f(std::integral_constant<int, 256>{});
   }
+  // LDS table of the scatter epilogue: token and weight of each tile row.
+  static DEV int* down_rows_tok() {
+    __shared__ int s_tok[256];
+    return s_tok;
+  }
+  static DEV float* down_rows_wt() {
+    __shared__ float s_wt[256];
+    return s_wt;
+  }
+  // Fill it: tok == nullptr means tokens row_tok0 + r with weight 1.
+  static DEV void down_rows(int rows, const int* tok, const float* wt, int row_tok0) {
+    const int r = threadIdx.x;
+    if (r < rows) {
+      down_rows_tok()[r] = tok ? tok[r] : row_tok0 + r;
+      down_rows_wt()[r] = tok ? wt[r] : 1.0f;
+    }
+  }
+
   static DEV void down_any(int bm, int nb, const Elem* A, int lda, int rows, const Elem* wd,
-                           int ldb, int K, float* out, int ldo, char* smem) {
+                           int ldb, int K, float* out, int ldo, char* smem, bool scatter) {
     by_class(bm, [&](auto c) __attribute__((always_inline)) {
       constexpr int BM = decltype(c)::value;
       if constexpr (TR::kBf16) {
         if (nb == 2) {
-          down_tile<BM, 2>(A, lda, rows, wd, ldb, K, out, ldo, smem);
+          down_tile<BM, 2>(A, lda, rows, wd, ldb, K, out, ldo, smem, scatter);
           return;
         }
       }
-      down_tile<BM, 1>(A, lda, rows, wd, ldb, K, out, ldo, smem);
+      down_tile<BM, 1>(A, lda, rows, wd, ldb, K, out, ldo, smem, scatter);
     });
   }
   static DEV void up_any(int bm, const Elem* A, int lda, int rows, const Elem* wg, const Elem* wu,
@@ -829,8 +872,13 @@ struct Stages {
     const int n0 = n * kBN * p.down_nb;
     const Elem* wd = reinterpret_cast<const Elem*>(p.wd) + (size_t)t.e * p.f * p.d +
                      (size_t)k_lo * p.d + n0;
+    if (p.comb_scatter) {
+      down_rows(t.rows, p.perm + t.row0, p.rw + t.row0, 0);   // read after the K loop's barriers
+      down_any(t.bm, p.down_nb, A, p.f, t.rows, wd, p.d, K, p.y + n0, p.d, smem, true);
+      return;
+    }
     float* out = o_slice(p, ks) + (size_t)t.row0 * p.d + n0;
-    down_any(t.bm, p.down_nb, A, p.f, t.rows, wd, p.d, K, out, p.d, smem);
+    down_any(t.bm, p.down_nb, A, p.f, t.rows, wd, p.d, K, out, p.d, smem, false);
   }
 
   // DOWN output rows of K slice ks: [T*k][d] fp32.
@@ -856,8 +904,14 @@ struct Stages {
     const int n0 = n * kBN * p.down_nb;
     const Elem* A = reinterpret_cast<const Elem*>(p.Hs) + ((size_t)s * p.T + r0) * p.fs;
     const Elem* wd = reinterpret_cast<const Elem*>(p.sd) + (size_t)s * p.fs * p.d + n0;
+    if (p.comb_scatter) {
+      down_rows(rows, nullptr, nullptr, r0);
+      down_any(row_class(rows), p.down_nb, A, p.fs, rows, wd, p.d, p.fs, p.y + n0, p.d, smem,
+               true);
+      return;
+    }
     float* out = p.Ys + ((size_t)s * p.T + r0) * p.d + n0;
-    down_any(row_class(rows), p.down_nb, A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem);
+    down_any(row_class(rows), p.down_nb, A, p.fs, rows, wd, p.d, p.fs, out, p.d, smem, false);
   }
 
   // ------------------------------------------------------------- combine

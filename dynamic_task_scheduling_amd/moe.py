@@ -36,7 +36,7 @@ def _stream(device) -> ctypes.c_void_p:
 def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model",
               split_k: int = 0, max_workers: int = 0, fixed_mem_workers: int = 0,
               flags: int = 0, trace: Optional[torch.Tensor] = None,
-              timeout_ms: int = 0, row_tile: int = 0) -> Desc:
+              timeout_ms: int = 0, row_tile: int = 0, combine: str = "auto") -> Desc:
     d = Desc()
     d.T, d.d, d.E, d.k, d.f = shape.T, shape.d, shape.E, shape.k, shape.f
     d.e_begin, d.e_end = shape.e_begin, shape.local_end
@@ -55,6 +55,7 @@ def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model
         d.flags |= _abi.FLAG_TRACE
     d.timeout_ms = timeout_ms
     d.row_tile = row_tile
+    d.combine = _abi.COMBINES[combine]
     return d
 
 
@@ -120,14 +121,15 @@ class MoELayer:
                  mode: str = "dynamic", split: str = "cost_model", split_k: int = 0,
                  max_workers: int = 0, fixed_mem_workers: int = 0, flags: int = 0,
                  trace: Optional[torch.Tensor] = None, timeout_ms: int = 0,
-                 workspace: Optional[torch.Tensor] = None, row_tile: int = 0):
+                 workspace: Optional[torch.Tensor] = None, row_tile: int = 0,
+                 combine: str = "auto"):
         self.shape = shape
         dev = weights["w_gate"].device
         if dev.type != "cuda":
             raise ValueError("weights must be on a GPU")
         self.device = dev
         self.desc = make_desc(shape, mode, split, split_k, max_workers, fixed_mem_workers,
-                              flags, trace, timeout_ms, row_tile)
+                              flags, trace, timeout_ms, row_tile, combine)
         self._trace = trace
         et = _elem_dtype(shape)
         d, E, f, El = shape.d, shape.E, shape.f, shape.E_loc

@@ -45,10 +45,10 @@ extern "C" {
  * intermediate buffers.  Accumulation is always fp32; y is always fp32. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-/* Scheduling mode.  Every mode runs the same device tile code in the same
- * arithmetic order (each output row is summed over its experts by one
- * combine task, in slot order), so every mode gives the same routing and
- * the same y, bit for bit.
+/* Scheduling mode.  Every mode runs the same device tile code and gives the
+ * same routing bit for bit; with MOE_COMBINE_TASKS (each output row summed
+ * over its experts by one combine task, in slot order) also the same y, bit
+ * for bit; with MOE_COMBINE_SCATTER y differs by fp32 summation order.
  *  MOE_DYNAMIC           one persistent kernel, dependency-driven ready
  *                        queues, count-sized worker split (the method).
  *  MOE_STATIC_PARTITION  one persistent kernel, tasks pre-assigned to
@@ -73,6 +73,21 @@ typedef enum {
   MOE_SPLIT_FIXED = 1,
   MOE_SPLIT_NONE = 2
 } moe_split_policy;
+
+/* How the weighted combine of the experts' rows is done.
+ *  MOE_COMBINE_AUTO     scatter-add when T * k <= 4096, else tasks.
+ *  MOE_COMBINE_SCATTER  each DOWN tile adds w * (H Wd) into y with fp32
+ *                       atomics (y zeroed by the router tasks); the last
+ *                       bits of y then depend on the order of the atomics.
+ *  MOE_COMBINE_TASKS    DOWN tiles write fp32 rows; one combine task per
+ *                       32 tokens and column chunk sums a token's experts in
+ *                       slot order once all their DOWN tiles are done; y is
+ *                       the same bit for bit in every mode and run. */
+typedef enum {
+  MOE_COMBINE_AUTO = 0,
+  MOE_COMBINE_SCATTER = 1,
+  MOE_COMBINE_TASKS = 2
+} moe_combine;
 
 /* Flags. */
 #define MOE_FLAG_CHECK 0x1u      /* synchronise and return device errors   */
@@ -112,6 +127,7 @@ typedef struct moe_desc {
   int timeout_ms;     /* device watchdog per wait; 0 = 2000 ms              */
   int row_tile;       /* expert row-tile height 128 or 256 (bf16 only);
                          0 = automatic (256 when T*k > 8192 in bf16)        */
+  int combine;        /* moe_combine                                        */
 } moe_desc;
 
 /* Weights.  E_loc = e_end - e_begin.  Element type = desc.dtype.
@@ -167,6 +183,7 @@ typedef struct moe_info {
   int route_splits;     /* router K slices per router tile                 */
   int combine_chunks;   /* combine tasks per 32-token tile (d / columns)   */
   int row_tile;         /* expert row-tile height (128 or 256)             */
+  int combine;          /* MOE_COMBINE_SCATTER or MOE_COMBINE_TASKS        */
   size_t workspace_bytes;
 } moe_info;
 

@@ -31,7 +31,7 @@ def check_trace(raw, layer, routing):
     expect = {ROUTE: n_rt * info["route_splits"], POS: n_rt, UP: n_mt * n_up,
               DOWN: n_mt * n_down * sk,
               SUP: s.n_shared * n_smt * n_sup_n, SDOWN: s.n_shared * n_smt * n_down,
-              COMB: n_rt * n_cc}
+              COMB: 0 if info["combine"] == 1 else n_rt * n_cc}
     for k, n in expect.items():
         assert int((kinds == k).sum()) == n, "kind %d ran %d times, expected %d" % (
             k, int((kinds == k).sum()), n)

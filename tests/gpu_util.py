@@ -77,15 +77,17 @@ def logits_bound(n, shape):
 
 
 def run_and_check(shape, g, n=None, mode="dynamic", split="cost_model", sample=None,
-                  split_k=0, max_workers=0, label="", row_tile=0):
+                  split_k=0, max_workers=0, label="", row_tile=0, combine="auto"):
     """Run one layer on the GPU and check it against the oracle.
     sample: None = every token; int = that many sampled tokens."""
     t0 = time.time()
-    log("[case] %s mode=%s split=%s T=%d d=%d E=%d k=%d f=%d local=[%d,%d) shared=%d row_tile=%d"
-        % (label, mode, split, shape.T, shape.d, shape.E, shape.k, shape.f, shape.e_begin,
-           shape.local_end, shape.n_shared, row_tile))
+    log("[case] %s mode=%s split=%s T=%d d=%d E=%d k=%d f=%d local=[%d,%d) shared=%d "
+        "row_tile=%d combine=%s" % (label, mode, split, shape.T, shape.d, shape.E, shape.k,
+                                   shape.f, shape.e_begin, shape.local_end, shape.n_shared,
+                                   row_tile, combine))
     layer = MoELayer(shape, g, mode=mode, split=split, split_k=split_k,
-                     max_workers=max_workers, timeout_ms=3000, row_tile=row_tile)
+                     max_workers=max_workers, timeout_ms=3000, row_tile=row_tile,
+                     combine=combine)
     y, r = layer(g["x"], return_routing=True, check_errors=True)
     torch.cuda.synchronize()
     if n is None:

@@ -49,7 +49,40 @@ def mid():
 @pytest.mark.parametrize("mode,split", MODES)
 def test_mid_bf16_all_modes(mid, mode, split):
     g, n = mid
-    run_and_check(MID, g, n, mode, split, label="mid_bf16")
+    run_and_check(MID, g, n, mode, split, label="mid_bf16", combine="tasks")
+
+
+# The scatter-add combine (automatic for layers with few routed rows) forced
+# on the mid layer, with a shared expert and split-K DOWN slices.
+@pytest.mark.parametrize("mode,split", MODES)
+def test_mid_scatter_combine_all_modes(mid, mode, split):
+    g, n = mid
+    run_and_check(MID, g, n, mode, split, label="mid_scatter", combine="scatter")
+    run_and_check(MID, g, n, mode, split, label="mid_scatter_sk3", combine="scatter", split_k=3)
+
+
+def test_scatter_combine_trace_and_agreement(mid):
+    from analysis_util import check_trace
+    g, n = mid
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(MID, g, mode="dynamic", trace=trace, timeout_ms=3000, combine="scatter")
+    assert layer.info["combine"] == 1
+    y, r = layer(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+    # the two combine paths agree up to fp32 summation order
+    yt = MoELayer(MID, g, mode="dynamic", combine="tasks")(g["x"], check_errors=True)
+    d = (y - yt).abs().max().item()
+    assert d <= 1e-5 * yt.abs().max().item(), "scatter vs tasks differ by %g" % d
+
+
+def test_auto_combine_choice():
+    small = LayerShape(T=512, d=256, E=8, k=8, f=256)
+    big = LayerShape(T=513, d=256, E=8, k=8, f=256)
+    g = gen_inputs(small, "auto_c", 8)
+    assert MoELayer(small, g).info["combine"] == 1     # T*k = 4096: scatter-add
+    g2 = gen_inputs(big, "auto_c", 8)
+    assert MoELayer(big, g2).info["combine"] == 2      # T*k = 4104: combine tasks
 
 
 # 256-row expert tiles (chosen automatically for large bf16 layers), forced
@@ -76,13 +109,17 @@ def test_row_tile_256_trace_and_modes_agree(big_tile):
     from analysis_util import check_trace
     g, n = big_tile
     trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
-    layer = MoELayer(BIG_TILE, g, mode="dynamic", trace=trace, timeout_ms=3000, row_tile=256)
+    layer = MoELayer(BIG_TILE, g, mode="dynamic", trace=trace, timeout_ms=3000, row_tile=256,
+                     combine="tasks")
     assert layer.info["row_tile"] == 256 and layer.info["down_ntiles"] == BIG_TILE.d // 256
     y, r = layer(g["x"], return_routing=True, check_errors=True)
     torch.cuda.synchronize()
     check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
-    y2 = MoELayer(BIG_TILE, g, mode="static", split="fixed", row_tile=256)(g["x"], check_errors=True)
+    y2 = MoELayer(BIG_TILE, g, mode="static", split="fixed", row_tile=256,
+                  combine="tasks")(g["x"], check_errors=True)
     assert torch.equal(y, y2)
+    run_and_check(BIG_TILE, g, n, "dynamic", "cost_model", label="rt256_tasks", row_tile=256,
+                  combine="tasks")
 
 
 def test_row_tile_256_split_k_and_odd_d():
@@ -178,7 +215,7 @@ def test_cross_mode_agreement(mid):
     ys = {}
     routes = {}
     for mode, split in MODES:
-        layer = MoELayer(MID, g, mode=mode, split=split, timeout_ms=3000)
+        layer = MoELayer(MID, g, mode=mode, split=split, timeout_ms=3000, combine="tasks")
         y, r = layer(g["x"], return_routing=True, check_errors=True)
         ys[(mode, split)] = y.clone()
         routes[(mode, split)] = r
@@ -197,7 +234,7 @@ def test_repeat_and_poisoned_workspace(mid):
     bytes before a call, give the same y bit for bit (no read before write;
     the result does not depend on the schedule)."""
     g, n = mid
-    layer = MoELayer(MID, g, mode="dynamic", timeout_ms=3000)
+    layer = MoELayer(MID, g, mode="dynamic", timeout_ms=3000, combine="tasks")
     y0 = layer(g["x"], check_errors=True).clone()
     for _ in range(3):
         y1 = layer(g["x"], check_errors=True)
@@ -209,15 +246,16 @@ def test_repeat_and_poisoned_workspace(mid):
     assert torch.equal(y2, y0), "call on a poisoned workspace differs"
 
 
+@pytest.mark.parametrize("combine", ["tasks", "scatter"])
 @pytest.mark.parametrize("mode,split", [("dynamic", "cost_model"), ("dynamic", "none"),
                                         ("static", "fixed")])
-def test_consecutive_calls_new_inputs(mode, split):
+def test_consecutive_calls_new_inputs(mode, split, combine):
     """One workspace, several calls with different token batches (so the
     routing, the gathered rows and the hidden rows all change): every call
     matches the oracle, so no call reads data left by an earlier one."""
     g = gen_inputs(MID, "mid", 1)
     n = host_inputs(g)
-    layer = MoELayer(MID, g, mode=mode, split=split, timeout_ms=3000)
+    layer = MoELayer(MID, g, mode=mode, split=split, timeout_ms=3000, combine=combine)
     for seed in (21, 22, 23):
         xs = torch.randn((MID.T, MID.d), generator=torch.Generator().manual_seed(seed))
         x = xs.to(torch.bfloat16).cuda()
@@ -236,7 +274,7 @@ def test_trace_happens_before(mid):
     from analysis_util import check_trace
     g, n = mid
     trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
-    layer = MoELayer(MID, g, mode="dynamic", trace=trace, timeout_ms=3000)
+    layer = MoELayer(MID, g, mode="dynamic", trace=trace, timeout_ms=3000, combine="tasks")
     y, r = layer(g["x"], return_routing=True, check_errors=True)
     torch.cuda.synchronize()
     check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
