@@ -207,7 +207,9 @@ def main():
         roof = {"bound": "mfma", "achieved": tflops, "peak": peak_fl, "unit": "TFLOP/s",
                 "frac": tflops / peak_fl}
     roof["traffic"] = load_traffic(wl.name) if n_launch_layers == 1 else None
-    roof["kernel"] = "k_dynamic<%s> (+ control reset)" % ("bf16" if is_bf16 else "fp32")
+    comb0 = MoELayer(wl.layers[0], tensors[0], mode="dynamic", combine=args.combine).info["combine"]
+    roof["kernel"] = "k_dynamic<%s, %s> (+ control reset)" % (
+        "bf16" if is_bf16 else "fp32", "true" if comb0 == 1 else "false")
 
     out = {
         "metric": METRIC,
