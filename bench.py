@@ -140,20 +140,25 @@ def main():
         return e0.elapsed_time(e1) / steps, wall
 
     modes = [m for m in args.modes.split(",") if m]
-    if args.profile_only:
+    if args.profile_only or args.no_baselines:
         modes = modes[:1]
+    split_of = {m: (args.split if m == "dynamic" else ("fixed" if m == "static" else "none"))
+                for m in modes}
+    all_layers = {m: make_layers(m, split_of[m]) for m in modes}
+    # One untimed pass over every mode first, so that no mode is timed on a
+    # GPU still ramping its clocks (the first-timed mode would otherwise pay
+    # for it); then each mode: W warm-up steps and exactly K timed steps.
+    if not args.profile_only:
+        for m in modes:
+            timed(all_layers[m], 1, args.warmup)
     ms = {}
     for m in modes:
-        split = args.split if m == "dynamic" else ("fixed" if m == "static" else "none")
-        layers = make_layers(m, split)
-        ms[m], wall = timed(layers, args.steps, args.warmup)
-        errs = [L.device_error() for L in layers]
+        ms[m], wall = timed(all_layers[m], args.steps, args.warmup)
+        errs = [L.device_error() for L in all_layers[m]]
         if any(errs):
             print("device error in mode %s: %s" % (m, errs), file=sys.stderr)
             sys.exit(3)
-        del layers
-        if args.profile_only or args.no_baselines:
-            break
+    del all_layers
     torch.cuda.synchronize()
 
     # routing stats + algorithmic work (from one routed call)
