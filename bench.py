@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--combine", default="auto", choices=["auto", "scatter", "tasks"],
                     help="weighted combine: scatter-add in the DOWN epilogue, or combine tasks")
     ap.add_argument("--modes", default="dynamic,static,multi_kernel")
+    ap.add_argument("--affinity", action="store_true",
+                    help="dynamic mode: per-XCD ready queues for UP tasks")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup+steps of the first mode in --modes only (for rocprofv3)")
     args = ap.parse_args()
@@ -105,7 +107,7 @@ def main():
 
     import numpy as np
     import torch
-    from dynamic_task_scheduling_amd import analysis, configs
+    from dynamic_task_scheduling_amd import _abi, analysis, configs
     from dynamic_task_scheduling_amd.moe import MoELayer
     from dynamic_task_scheduling_amd.synth import make_layer, to_numpy
 
@@ -116,7 +118,8 @@ def main():
     torch.cuda.synchronize()
 
     def make_layers(mode, split, trace=None):
-        return [MoELayer(s, t, mode=mode, split=split, trace=trace, combine=args.combine)
+        fl = _abi.FLAG_XCD_AFFINITY if (args.affinity and mode == "dynamic") else 0
+        return [MoELayer(s, t, mode=mode, split=split, trace=trace, combine=args.combine, flags=fl)
                 for s, t in zip(wl.layers, tensors)]
 
     ys = [torch.empty((s.T, s.d), dtype=torch.float32, device=dev) for s in wl.layers]

@@ -22,7 +22,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   Params p;          // geometry only (pointers filled by carve)
   int esz;
-  size_t off_ctrl, off_slots, off_logits, off_idx, off_w, off_hist, off_rtb, off_counts,
+  size_t off_ctrl, off_slots, off_uslots, off_logits, off_idx, off_w, off_hist, off_rtb, off_counts,
       off_offsets, off_eorder, off_route_part, off_cnt_route, off_perm, off_rw, off_slotpos, off_mtiles, off_cnt_perm,
       off_cnt_down, off_cnt_sdown, off_perm_list, off_mt_base, off_cnt_comb, off_xp, off_h, off_hs,
       off_o, off_ys, total;
@@ -149,6 +149,7 @@ void make_layout(const moe_desc* d, Layout* L) {
   const size_t Tk = (size_t)d->T * d->k;
   L->off_ctrl = take(sizeof(int) * CW_COUNT * kCtrlStride);
   L->off_slots = take(sizeof(int) * (size_t)kNumQueues * p.q_cap);
+  L->off_uslots = take(sizeof(int) * (size_t)kXcds * p.q_cap);
   L->off_logits = take(sizeof(float) * (size_t)d->T * d->E);
   L->off_route_part = take(p.rsk > 1 ? sizeof(float) * (size_t)p.rsk * p.n_rt * kTB * d->E : 0);
   L->off_cnt_route = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
@@ -182,6 +183,7 @@ void carve(Layout* L, void* ws) {
   char* b = static_cast<char*>(ws);
   p.ctrl = reinterpret_cast<int*>(b + L->off_ctrl);
   p.slots = reinterpret_cast<int*>(b + L->off_slots);
+  p.uslots = reinterpret_cast<int*>(b + L->off_uslots);
   p.logits = reinterpret_cast<float*>(b + L->off_logits);
   p.route_part = reinterpret_cast<float*>(b + L->off_route_part);
   p.cnt_route = reinterpret_cast<int*>(b + L->off_cnt_route);

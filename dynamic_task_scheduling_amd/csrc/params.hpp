@@ -50,8 +50,12 @@ enum CtrlWord : int {
   CW_BAR_COUNT = 18,   // grid barrier (static mode)
   CW_BAR_GEN = 19,
   CW_TRACE = 20,       // trace cursor
-  CW_COUNT = 21
+  CW_UHEAD = 21,       // + XCD: per-XCD UP queues (XCD affinity)
+  CW_UTAIL = 29,       // + XCD
+  CW_UTOTAL = 37,      // + XCD
+  CW_COUNT = 45
 };
+constexpr int kXcds = 8;   // MI355X: 8 XCDs, each with its own L2
 constexpr int kCtrlStride = 32;
 
 struct MTile {
@@ -109,6 +113,7 @@ struct Params {
   // workspace
   int* ctrl;
   int* slots;      // [kNumQueues][q_cap]
+  int* uslots;     // [kXcds][q_cap] per-XCD UP queues (XCD affinity)
   float* logits;   // [T][E]
   float* route_part;  // [rsk][T][E] router partial sums (rsk > 1)
   int* cnt_route;  // [n_rt] router slices still running

@@ -34,6 +34,16 @@ constexpr int kFlagTrace = 0x2;
 constexpr int kFlagPhaseSync = 0x4;
 constexpr int kFlagRefSync = 0x8;
 constexpr int kFlagNoSteal = 0x10;
+constexpr int kFlagXcdAffinity = 0x20;
+
+// XCD affinity: the UP task of column tile n goes to the ready queue of XCD
+// n % 8, so the workers of one XCD keep reading the same weight panels
+// through their own L2 (m.xxqk.cn/news/657744 s3.2, affinity); a worker
+// whose compute-queue slot is still empty takes an already-pushed UP task,
+// its own XCD's queue first.  Only pushed tasks are taken: a task whose slot
+// index is below the queue's tail is filled now or within one store.
+DEV bool affinity(const Params& p) { return (p.flags & kFlagXcdAffinity) != 0; }
+DEV int* ucw(const Params& p, int word, int x) { return p.ctrl + (word + x) * kCtrlStride; }
 
 DEV int* cw(const Params& p, int word) { return p.ctrl + word * kCtrlStride; }
 
@@ -62,6 +72,20 @@ DEV int wait_slot(const Params& p, const int* sl) {
     }
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// Thread 0: take an already-pushed UP task from the XCD queues, own first.
+DEV int take_up(const Params& p) {
+  const int x0 = xcc_id() & (kXcds - 1);
+  for (int i = 0; i < kXcds; ++i) {
+    const int x = (x0 + i) & (kXcds - 1);
+    if (ld_relaxed(ucw(p, CW_UHEAD, x)) < ld_relaxed(ucw(p, CW_UTAIL, x))) {
+      const int h = add_relaxed(ucw(p, CW_UHEAD, x), 1);
+      if (h < ld_relaxed(ucw(p, CW_UTOTAL, x)) && h < p.q_cap)
+        return wait_slot(p, p.uslots + (size_t)x * p.q_cap + h);
+    }
+  }
+  return kClaimExhausted;
 }
 
 DEV int claim(const Params& p, int q, int& pend, bool steal) {
@@ -93,6 +117,10 @@ DEV int claim(const Params& p, int q, int& pend, bool steal) {
       const int hm = add_relaxed(cw(p, CW_HEAD + QM), 1);
       if (hm < ld_relaxed(cw(p, CW_TOTAL + QM)) && hm < p.q_cap)
         return wait_slot(p, p.slots + (size_t)QM * p.q_cap + hm);
+    }
+    if (q == QC && affinity(p)) {
+      const int t = take_up(p);
+      if (t != kClaimExhausted) return t;
     }
     if (timed_out(p, t0)) {
       set_error(p, 5 /* MOE_ERR_TIMEOUT */);
@@ -246,13 +274,17 @@ struct Sched {
     const int n_mt = ld_relaxed(cw(p, CW_NMT));
     const int n_perm = ld_relaxed(cw(p, CW_NPERM));
     const bool split = p.split_policy != 2;
-    const int n_comp = n_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup + p.n_sdown +
+    const int n_up_qc = affinity(p) ? 0 : n_mt * p.n_up_n;
+    const int n_comp = n_up_qc + n_mt * p.n_down_n * p.splitk + p.n_sup + p.n_sdown +
                        (p.comb_scatter ? 0 : p.n_rt * p.n_cc);
     publish_fence();
     __syncthreads();
     if (threadIdx.x == 0) {
       st_relaxed(cw(p, CW_TOTAL + QM), split ? n_perm : 0);
       st_relaxed(cw(p, CW_TOTAL + QC), n_comp + (split ? 0 : n_perm));
+      if (affinity(p))
+        for (int x = 0; x < kXcds; ++x)
+          st_relaxed(ucw(p, CW_UTOTAL, x), n_mt * ((p.n_up_n - x + kXcds - 1) / kXcds));
       st_relaxed(cw(p, CW_SPLIT_READY), 1);
     }
     // position tiles go to QA
@@ -331,9 +363,24 @@ struct Sched {
         const int mt = pl / p.pch, c = pl % p.pch;
         S::permute(p, mt, c);
         *t_body = rtc();
-        if (arrive_last(p.cnt_perm + mt, -1, 1, s_tmp) && dyn)
-          push_burst(p, QC, p.n_up_n, s_tmp,
-                     [&](int n) { return make_task(TK_UP, mt * p.n_up_n + n); });
+        if (arrive_last(p.cnt_perm + mt, -1, 1, s_tmp) && dyn) {
+          if (affinity(p)) {
+            // one thread per column tile, into XCD n % 8's queue
+            const int n = threadIdx.x;
+            if (n < p.n_up_n) {
+              const int x = n % kXcds;
+              const int slot = add_relaxed(ucw(p, CW_UTAIL, x), 1);
+              if (slot < p.q_cap)
+                st_relaxed(p.uslots + (size_t)x * p.q_cap + slot, make_task(TK_UP, mt * p.n_up_n + n) + 1);
+              else
+                set_error(p, 6 /* MOE_ERR_CAPACITY */);
+            }
+            __syncthreads();
+          } else {
+            push_burst(p, QC, p.n_up_n, s_tmp,
+                       [&](int n) { return make_task(TK_UP, mt * p.n_up_n + n); });
+          }
+        }
         break;
       }
       case TK_UP: {
@@ -643,6 +690,11 @@ __global__ __launch_bounds__(kThreads) void k_reset(Params p) {
   // combine tiles: the shared DOWN tiles over their tokens, plus one unit
   // that the tile's POS task replaces by its routed DOWN tiles
   for (int i = gid; i < p.n_rt; i += stride) p.cnt_comb[i] = 1 + p.n_shared * p.n_down_n;
+  if (p.flags & kFlagXcdAffinity) {
+    const size_t nu = (size_t)kXcds * p.q_cap;
+    for (size_t i = gid; i < nu; i += stride) p.uslots[i] = 0;
+    if (gid < kXcds) p.ctrl[(CW_UTOTAL + gid) * kCtrlStride] = 0x7fffffff;
+  }
   if (gid == 0) {
     p.ctrl[(CW_TAIL + QA) * kCtrlStride] = n_route;
     p.ctrl[(CW_TOTAL + QA) * kCtrlStride] = n_route + p.n_rt;

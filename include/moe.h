@@ -95,6 +95,7 @@ typedef enum {
 #define MOE_FLAG_PHASE_SYNC 0x4u /* static mode: barriers between stages (default on) */
 #define MOE_FLAG_REF_SYNC 0x8u   /* static mode: per-task counter waits instead of barriers */
 #define MOE_FLAG_NO_STEAL 0x10u  /* dynamic split: compute workers never take permute tasks */
+#define MOE_FLAG_XCD_AFFINITY 0x20u /* dynamic: UP tasks of column tile n on XCD n % 8's queue */
 
 /* Return codes. */
 #define MOE_OK 0

@@ -269,6 +269,30 @@ def test_consecutive_calls_new_inputs(mode, split, combine):
         compare_y(y.cpu().numpy(), yo, "bf16")
 
 
+@pytest.mark.parametrize("split", ["cost_model", "none"])
+def test_xcd_affinity(big_tile, split):
+    """Per-XCD UP queues: same results bit for bit, every task once, every
+    task after its producers."""
+    from analysis_util import check_trace
+    from dynamic_task_scheduling_amd import _abi
+    g, n = big_tile
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(BIG_TILE, g, mode="dynamic", split=split, trace=trace, timeout_ms=3000,
+                     row_tile=256, combine="tasks", flags=_abi.FLAG_XCD_AFFINITY)
+    y, r = layer(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+    y2 = MoELayer(BIG_TILE, g, mode="dynamic", row_tile=256, combine="tasks")(g["x"], check_errors=True)
+    assert torch.equal(y, y2)
+    run_and_check(MID, *gen_and_host(MID, "mid", 1), "dynamic", split, label="mid_aff",
+                  flags=_abi.FLAG_XCD_AFFINITY)
+
+
+def gen_and_host(shape, tag, seed):
+    g = gen_inputs(shape, tag, seed)
+    return g, host_inputs(g)
+
+
 def test_trace_happens_before(mid):
     """Every task runs exactly once and starts after its producers ended."""
     from analysis_util import check_trace
