@@ -190,11 +190,14 @@ class MoELayer:
 
 
 def route_from_logits(shape: LayerShape, logits: torch.Tensor,
-                      workspace: Optional[torch.Tensor] = None) -> RoutingResult:
-    """Routing tables from given fp32 logits [T,E] (same device code as the layer)."""
+                      workspace: Optional[torch.Tensor] = None,
+                      check_errors: bool = False) -> RoutingResult:
+    """Routing tables from given fp32 logits [T,E] (same device code as the layer).
+    check_errors: synchronise and raise on a device-detected error (e.g. a
+    non-finite logit)."""
     dev = logits.device
     _check_tensor("logits", logits, (shape.T, shape.E), torch.float32, dev)
-    desc = make_desc(shape, "multi_kernel")
+    desc = make_desc(shape, "multi_kernel", flags=_abi.FLAG_CHECK if check_errors else 0)
     n = workspace_size(desc)
     if workspace is None or workspace.numel() < n:
         workspace = torch.empty((n,), dtype=torch.uint8, device=dev)

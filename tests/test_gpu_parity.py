@@ -135,8 +135,59 @@ def test_row_tile_256_split_k_and_odd_d():
                                         ("multi_kernel", "none")])
 def test_local_expert_range(mode, split):
     g = gen_inputs(MID_LOCAL, "mid_local", 2)
-    _, r, ro = run_and_check(MID_LOCAL, g, None, mode, split, label="mid_local")
-    assert (ro["slot_pos"] < 0).any()
+    for combine in ("scatter", "tasks"):
+        y, r, ro = run_and_check(MID_LOCAL, g, None, mode, split, label="mid_local_" + combine,
+                                 combine=combine)
+        assert (ro["slot_pos"] < 0).any()
+
+
+@pytest.mark.parametrize("combine", ["scatter", "tasks"])
+def test_tokens_without_local_expert_are_zero(combine):
+    """A narrow local range (8 of 32 experts, k = 2): many tokens have no
+    local expert, and their rows of y are exactly zero (no shared experts)."""
+    s = LayerShape(T=211, d=256, E=32, k=2, f=256, e_begin=24, e_end=32, zipf_s=1.5)
+    g = gen_inputs(s, "narrow_local", 11)
+    y, r, ro = run_and_check(s, g, None, "dynamic", "cost_model", label="narrow_" + combine,
+                             combine=combine)
+    none_local = np.all(ro["slot_pos"] < 0, axis=1)
+    assert none_local.any() and not none_local.all()
+    assert torch.all(y[torch.as_tensor(np.nonzero(none_local)[0], device=y.device)] == 0)
+
+
+def test_empty_batch():
+    """T = 0: nothing to route or compute; the call succeeds without a launch."""
+    s = LayerShape(T=0, d=256, E=8, k=2, f=256)
+    g = gen_inputs(LayerShape(T=4, d=256, E=8, k=2, f=256), "empty", 9)
+    g["x"] = g["x"][:0].contiguous()
+    y = MoELayer(s, g, mode="dynamic")(g["x"], check_errors=True)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)
+
+
+@pytest.mark.parametrize("combine", ["scatter", "tasks"])
+def test_every_expert_and_max_shared(combine):
+    """k = E (every expert takes every token) with the maximum of four shared
+    experts."""
+    s = LayerShape(T=150, d=256, E=8, k=8, f=256, n_shared=4, f_shared=128)
+    g = gen_inputs(s, "k_eq_E", 10)
+    _, r, ro = run_and_check(s, g, None, "dynamic", "cost_model", label="kE_" + combine,
+                             combine=combine)
+    assert np.all(ro["counts"] == s.T)
+
+
+def test_nonfinite_logit_reported():
+    """A NaN or infinite logit is a device-detected error (MOE_ERR_NONFINITE),
+    raised when the caller asks for the check."""
+    from dynamic_task_scheduling_amd._abi import MoEError
+    s = LayerShape(T=40, d=128, E=16, k=4, f=128)
+    for bad in (float("nan"), float("inf")):
+        lg = torch.randn((s.T, s.E), generator=torch.Generator().manual_seed(3))
+        lg[7, 5] = bad
+        with pytest.raises(MoEError) as ei:
+            route_from_logits(s, lg.cuda(), check_errors=True)
+        assert ei.value.code == 7
+    # a clean call afterwards succeeds (the error word is reset per call)
+    route_from_logits(s, torch.randn((s.T, s.E)).cuda(), check_errors=True)
 
 
 def test_split_k_uneven():
