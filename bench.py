@@ -1,20 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark: one MoE layer per step on one MI355X through the C ABI.
 
-Default workload: the decode-shaped bf16 layer (T=128, d=4096, E=8,
-f=14336, k=2, Zipf(1.2) router bias) -- weight streaming, HBM-bound.
+Headline workload (default, the largest single-GPU configuration): one GPU's
+share of a 2-way expert-parallel layer -- T=8192 tokens, d=7168, 128 of 256
+experts local, f=2048, top-8, Zipf(1.5) router bias -- MFMA-bound.
 `--config N` picks another workload (1 tiny fp32, 2 decode, 3 fine-grained
 prefill, 4 one-GPU expert share, 5 sixteen-layer stress).
 
 A step is one full layer (router, top-k, permute, expert GEMMs, combine) in
 the dynamic persistent megakernel; inputs are resident in HBM before timing.
 The static-partition megakernel and the multi-kernel baseline run the same
-inputs for the reported gains.  Prints ONE JSON line.
+inputs for the reported gains; the other workloads and the scheduler
+ablations follow under extra keys.  Prints ONE JSON line.
+
+`--calibrate-copy MIB` instead runs a plain device copy of known size (the
+reference for scaling the FETCH_SIZE / WRITE_SIZE hardware counters).
 """
 import argparse
 import hashlib
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -25,6 +32,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (MFMA / vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer tokens/s + TFLOP/s (% bf16 MFMA peak) on 1 MI355X; vs static split"
+HEADLINE_CONFIG = 4
 
 
 def kernel_source_sha() -> str:
@@ -51,17 +59,26 @@ def load_traffic(workload_name: str):
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, layers_host, budget_s=12.0):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, n0, budget_s=12.0):
     """Time the CPU oracle (as it stands) on a bounded token sample of layer 0."""
     import numpy as np
     import oracle
     s = wl.layers[0]
-    n = layers_host[0]
-    lg = n["logits"]
+    lg = n0["logits"]
     t0 = time.perf_counter()
     ro = oracle.route(lg, s.k, s.e_begin, s.local_end)
     t_route = time.perf_counter() - t0
-    shared = (n["ws_gate"], n["ws_up"], n["ws_down"]) if s.n_shared else None
+    shared = (n0["ws_gate"], n0["ws_up"], n0["ws_down"]) if s.n_shared else None
     ntok = 1
     spent = 0.0
     done = 0
@@ -70,7 +87,8 @@ def cpu_baseline(wl, layers_host, budget_s=12.0):
     while done < s.T and spent < budget_s:
         toks = order[done:done + ntok]
         t0 = time.perf_counter()
-        oracle.moe_rows(n["x"], n["w_gate"], n["w_up"], n["w_down"], ro, toks, s.e_begin, shared)
+        oracle.moe_rows(n0["x"], n0["w_gate"], n0["w_up"], n0["w_down"], ro, toks, s.e_begin,
+                        shared)
         dt = time.perf_counter() - t0
         spent += dt
         done += len(toks)
@@ -78,9 +96,181 @@ def cpu_baseline(wl, layers_host, budget_s=12.0):
         ntok = int(max(1, min(s.T - done, (budget_s - spent) / max(per, 1e-6))))
     tok_s = done / (spent + t_route * done / s.T)
     return {"value": tok_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d tokens of layer 0 (full routing of all %d tokens + expert "
+            "cpu": cpu_model(),
+            "sample": "%d of %d tokens of %s layer 0 (full routing of all %d tokens + expert "
                       "SwiGLU rows of the sampled tokens), fp64 C oracle, %.1f s"
-                      % (done, s.T, s.T, spent + t_route)}
+                      % (done, s.T, wl.name, s.T, spent + t_route)}
+
+
+def calibrate_copy(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": n, "reps": 3}), flush=True)
+
+
+class Runner:
+    """Layers of one workload on the GPU, and the timing of a scheduling mode."""
+
+    def __init__(self, cfg, dev, combine="auto"):
+        import torch
+        from dynamic_task_scheduling_amd import configs
+        from dynamic_task_scheduling_amd.synth import make_layer
+        self.torch = torch
+        self.dev = dev
+        self.wl = configs.workload(cfg)
+        self.tensors = [make_layer(s, self.wl.name, li, 0, dev) for li, s in enumerate(self.wl.layers)]
+        self.ys = [torch.empty((s.T, s.d), dtype=torch.float32, device=dev) for s in self.wl.layers]
+        self.combine = combine
+        torch.cuda.synchronize()
+
+    def layers(self, mode, split, flags=0, trace=None):
+        from dynamic_task_scheduling_amd.moe import MoELayer
+        return [MoELayer(s, t, mode=mode, split=split, trace=trace, combine=self.combine, flags=flags)
+                for s, t in zip(self.wl.layers, self.tensors)]
+
+    def step(self, layers):
+        for L, t, y in zip(layers, self.tensors, self.ys):
+            L(t["x"], y)
+
+    def timed(self, layers, steps, warmup):
+        """W untimed steps, then exactly K timed steps between two
+        synchronisations; events between steps give per-step times."""
+        torch = self.torch
+        stream = torch.cuda.current_stream(self.dev)
+        for _ in range(warmup):
+            self.step(layers)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            self.step(layers)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        errs = [L.device_error() for L in layers]
+        if any(errs):
+            raise RuntimeError("device error %s" % errs)
+        return {"mean": ev[0].elapsed_time(ev[steps]) / steps, "median": statistics.median(per),
+                "min": min(per)}
+
+    def routed(self):
+        """Routing stats and algorithmic work from one routed call per layer."""
+        import numpy as np
+        from dynamic_task_scheduling_amd import configs
+        from dynamic_task_scheduling_amd.moe import MoELayer
+        flops = hbm = 0.0
+        stats, logits0, sched = [], None, []
+        for li, (s, t) in enumerate(zip(self.wl.layers, self.tensors)):
+            L = MoELayer(s, t, mode="dynamic", combine=self.combine)
+            y, r = L(t["x"], return_routing=True)
+            sched.append(L.last_schedule())
+            c = r.expert_counts.cpu().numpy()
+            R, A = int(c.sum()), int((c > 0).sum())
+            flops += configs.flops(s, R)
+            hbm += configs.algo_bytes(s, A)
+            stats.append({"R": R, "active": A, "max": int(c.max()), "median": float(np.median(c)),
+                          "zero": int((c == 0).sum())})
+            if li == 0:
+                logits0 = r.logits.cpu().numpy()
+        return flops, hbm, stats, logits0, sched
+
+    def trace(self, split="cost_model"):
+        """Schedule statistics and the cost-model calibration from one traced
+        call of layer 0 (a separate run: tracing perturbs timing slightly)."""
+        from dynamic_task_scheduling_amd import analysis
+        torch = self.torch
+        trace = torch.zeros(4 * 400000, dtype=torch.int64, device=self.dev)
+        s0 = self.wl.layers[0]
+        L = self.layers("dynamic", split, trace=trace)[0]
+        y, r = L(self.tensors[0]["x"], self.ys[0], return_routing=True)
+        torch.cuda.synchronize()
+        tr = analysis.decode_trace(trace.cpu().numpy())
+        info = L.info
+        st = analysis.schedule_stats(tr, info["workers"])
+        st["workers"] = info["workers"]
+        st["by_kind_us"] = {k: round(v["sum_us"], 1) for k, v in analysis.by_kind(tr).items()}
+        cal = analysis.calibrate(tr, info, s0, r.expert_counts.cpu().numpy())
+        return st, cal
+
+
+def gains(ms):
+    out = {}
+    if "static" in ms:
+        out["gain_vs_static"] = ms["static"]["mean"] / ms["dynamic"]["mean"]
+    if "multi_kernel" in ms:
+        out["gain_vs_multi_kernel"] = ms["multi_kernel"]["mean"] / ms["dynamic"]["mean"]
+    return out
+
+
+def roofline_of(flops, hbm, t_s, bf16):
+    peak_fl = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    ridge = peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / hbm < ridge:
+        a = hbm / t_s / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": a / PEAK_HBM_GBS}
+    a = flops / t_s / 1e12
+    return {"bound": "mfma", "achieved": a, "peak": peak_fl, "unit": "TFLOP/s", "frac": a / peak_fl}
+
+
+MODE_SPLIT = {"dynamic": "cost_model", "static": "fixed", "multi_kernel": "none"}
+
+
+def measure_modes(run, steps, warmup, modes=("dynamic", "static", "multi_kernel"), split=None):
+    layers = {m: run.layers(m, split if (split and m == "dynamic") else MODE_SPLIT[m]) for m in modes}
+    # one untimed pass over every mode first, so that no mode is timed on a
+    # GPU still ramping its clocks
+    for m in modes:
+        run.timed(layers[m], 1, warmup)
+    ms = {m: run.timed(layers[m], steps, warmup) for m in modes}
+    del layers
+    return ms
+
+
+def ablations(run, steps, warmup):
+    """Scheduler ablations on one workload: the split policy, compute workers
+    stealing permute tasks, per-XCD UP queues, and the static baseline's
+    synchronisation (grid barriers vs per-task counter waits)."""
+    from dynamic_task_scheduling_amd import _abi
+    variants = [
+        ("dynamic/split=cost_model", "dynamic", "cost_model", 0),
+        ("dynamic/split=fixed", "dynamic", "fixed", 0),
+        ("dynamic/split=none", "dynamic", "none", 0),
+        ("dynamic/steal=0", "dynamic", "cost_model", _abi.FLAG_NO_STEAL),
+        ("dynamic/xcd_affinity", "dynamic", "cost_model", _abi.FLAG_XCD_AFFINITY),
+        ("static/sync=phase_barrier", "static", "fixed", 0),
+        ("static/sync=ref_count", "static", "fixed", _abi.FLAG_REF_SYNC),
+        ("multi_kernel", "multi_kernel", "none", 0),
+    ]
+    out = {}
+    for name, mode, split, fl in variants:
+        L = run.layers(mode, split, flags=fl)
+        run.timed(L, 1, warmup)
+        out[name] = round(run.timed(L, steps, warmup)["mean"], 4)
+        if mode == "dynamic":
+            out[name + ":mem_workers"] = L[0].last_schedule()["mem_workers"]
+        del L
+    return out
+
+
+def summarize(run, ms, steps_note=None):
+    flops, hbm, stats, _, sched = run.routed()
+    t = ms["dynamic"]["mean"] * 1e-3
+    bf16 = run.wl.layers[0].dtype == "bf16"
+    roof = roofline_of(flops, hbm, t, bf16)
+    tot_T = sum(s.T for s in run.wl.layers)
+    out = {"ms": {m: round(v["mean"], 4) for m, v in ms.items()},
+           "tokens_per_s": tot_T / t, "tflops": flops / t / 1e12, "hbm_gbs": hbm / t / 1e9,
+           "roofline_bound": roof["bound"], "roofline_frac": roof["frac"],
+           "mem_workers": [s["mem_workers"] for s in sched][:16]}
+    out.update(gains(ms))
+    return out
 
 
 def main():
@@ -88,137 +278,55 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=HEADLINE_CONFIG)
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-ablations", action="store_true")
     ap.add_argument("--split", default="cost_model")
     ap.add_argument("--combine", default="auto", choices=["auto", "scatter", "tasks"],
                     help="weighted combine: scatter-add in the DOWN epilogue, or combine tasks")
-    ap.add_argument("--modes", default="dynamic,static,multi_kernel")
-    ap.add_argument("--affinity", action="store_true",
-                    help="dynamic mode: per-XCD ready queues for UP tasks")
     ap.add_argument("--profile-only", action="store_true",
-                    help="run warmup+steps of the first mode in --modes only (for rocprofv3)")
+                    help="time only the dynamic mode (for rocprofv3 runs)")
+    ap.add_argument("--mode", default="dynamic", help="mode timed by --profile-only")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
-    import numpy as np
     import torch
-    from dynamic_task_scheduling_amd import _abi, analysis, configs
-    from dynamic_task_scheduling_amd.moe import MoELayer
-    from dynamic_task_scheduling_amd.synth import make_layer, to_numpy
+    from dynamic_task_scheduling_amd.synth import to_numpy
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = configs.workload(args.config)
-    tensors = [make_layer(s, wl.name, li, 0, dev) for li, s in enumerate(wl.layers)]
-    torch.cuda.synchronize()
+    run = Runner(args.config, dev, args.combine)
+    wl = run.wl
 
-    def make_layers(mode, split, trace=None):
-        fl = _abi.FLAG_XCD_AFFINITY if (args.affinity and mode == "dynamic") else 0
-        return [MoELayer(s, t, mode=mode, split=split, trace=trace, combine=args.combine, flags=fl)
-                for s, t in zip(wl.layers, tensors)]
-
-    ys = [torch.empty((s.T, s.d), dtype=torch.float32, device=dev) for s in wl.layers]
-
-    def timed(layers, steps, warmup):
-        stream = torch.cuda.current_stream(dev)
-        for _ in range(warmup):
-            for L, t, y in zip(layers, tensors, ys):
-                L(t["x"], y)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(steps):
-            for L, t, y in zip(layers, tensors, ys):
-                L(t["x"], y)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / steps
-        return e0.elapsed_time(e1) / steps, wall
-
-    modes = [m for m in args.modes.split(",") if m]
-    if args.profile_only or args.no_baselines:
-        modes = modes[:1]
-    split_of = {m: (args.split if m == "dynamic" else ("fixed" if m == "static" else "none"))
-                for m in modes}
-    all_layers = {m: make_layers(m, split_of[m]) for m in modes}
-    # One untimed pass over every mode first, so that no mode is timed on a
-    # GPU still ramping its clocks (the first-timed mode would otherwise pay
-    # for it); then each mode: W warm-up steps and exactly K timed steps.
-    if not args.profile_only:
-        for m in modes:
-            timed(all_layers[m], 1, args.warmup)
-    ms = {}
-    for m in modes:
-        ms[m], wall = timed(all_layers[m], args.steps, args.warmup)
-        errs = [L.device_error() for L in all_layers[m]]
-        if any(errs):
-            print("device error in mode %s: %s" % (m, errs), file=sys.stderr)
-            sys.exit(3)
-    del all_layers
-    torch.cuda.synchronize()
-
-    # routing stats + algorithmic work (from one routed call)
-    routed = []
-    for s, t in zip(wl.layers, tensors):
-        L = MoELayer(s, t, mode="dynamic")
-        y, r = L(t["x"], return_routing=True)
-        routed.append(r)
-    torch.cuda.synchronize()
-    tot_T = sum(s.T for s in wl.layers)
-    flops = 0.0
-    hbm = 0.0
-    count_stats = []
-    for s, r in zip(wl.layers, routed):
-        c = r.expert_counts.cpu().numpy()
-        R = int(c.sum())
-        A = int((c > 0).sum())
-        flops += configs.flops(s, R)
-        hbm += configs.algo_bytes(s, A)
-        count_stats.append({"R": R, "active": A, "max": int(c.max()), "median": float(np.median(c)),
-                            "zero": int((c == 0).sum())})
     if args.profile_only:
-        print(json.dumps({"profile_only": True, "ms_by_mode": ms}), flush=True)
+        L = run.layers(args.mode, args.split if args.mode == "dynamic" else MODE_SPLIT[args.mode])
+        r = run.timed(L, args.steps, args.warmup)
+        print(json.dumps({"profile_only": True, "workload": wl.name, "mode": args.mode,
+                          "ms": r}), flush=True)
         return
-    t_dyn = ms["dynamic"] * 1e-3
-    tflops = flops / t_dyn / 1e12
-    gbs = hbm / t_dyn / 1e9
-    is_bf16 = wl.layers[0].dtype == "bf16"
-    peak_fl = PEAK_BF16_TFLOPS if is_bf16 else PEAK_FP32_TFLOPS
-    ridge = peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9)
-    bound = "hbm" if flops / hbm < ridge else "mfma"
 
-    # schedule statistics from one traced call of layer 0 (separate run)
-    sched = {}
-    if not args.profile_only:
-        trace = torch.zeros(4 * 200000, dtype=torch.int64, device=dev)
-        Lt = MoELayer(wl.layers[0], tensors[0], mode="dynamic", split=args.split, trace=trace,
-                      combine=args.combine)
-        Lt(tensors[0]["x"], ys[0])
-        torch.cuda.synchronize()
-        tr = analysis.decode_trace(trace.cpu().numpy())
-        sched = analysis.schedule_stats(tr, Lt.info["workers"])
-        sched["workers"] = Lt.info["workers"]
-        del Lt, trace
-
-    n_launch_layers = len(wl.layers)
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS}
-    else:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": peak_fl, "unit": "TFLOP/s",
-                "frac": tflops / peak_fl}
-    roof["traffic"] = load_traffic(wl.name) if n_launch_layers == 1 else None
-    comb0 = MoELayer(wl.layers[0], tensors[0], mode="dynamic", combine=args.combine).info["combine"]
+    modes = ("dynamic",) if args.no_baselines else ("dynamic", "static", "multi_kernel")
+    ms = measure_modes(run, args.steps, args.warmup, modes, split=args.split)
+    flops, hbm, count_stats, logits0, sched = run.routed()
+    st, cal = run.trace(args.split)
+    t_dyn = ms["dynamic"]["mean"] * 1e-3
+    bf16 = wl.layers[0].dtype == "bf16"
+    roof = roofline_of(flops, hbm, t_dyn, bf16)
+    roof["traffic"] = load_traffic(wl.name) if len(wl.layers) == 1 else None
     roof["kernel"] = "k_dynamic<%s, %s> (+ control reset)" % (
-        "bf16" if is_bf16 else "fp32", "true" if comb0 == 1 else "false")
-
+        "bf16" if bf16 else "fp32", "true" if run.layers("dynamic", args.split)[0].info["combine"] == 1
+        else "false")
+    tot_T = sum(s.T for s in wl.layers)
     out = {
         "metric": METRIC,
         "value": tot_T / t_dyn,
@@ -226,39 +334,56 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms["dynamic"],
+        "ms_per_step": ms["dynamic"]["mean"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if is_bf16 else "fp32",
+        "dtype": "bf16" if bf16 else "fp32",
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": len(wl.layers), "tokens_per_step": tot_T,
                    "T": wl.layers[0].T if len(wl.layers) == 1 else "per-layer",
                    "d": wl.layers[0].d, "E": wl.layers[0].E, "k": wl.layers[0].k,
-                   "f": wl.layers[0].f, "split": args.split, "combine": args.combine},
-        "tflops": tflops,
-        "pct_mfma_peak": 100.0 * tflops / peak_fl,
-        "hbm_gbs": gbs,
-        "pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS,
+                   "f": wl.layers[0].f, "local_experts": wl.layers[0].E_loc,
+                   "split": args.split, "combine": args.combine},
+        "tflops": flops / t_dyn / 1e12,
+        "pct_mfma_peak": 100.0 * flops / t_dyn / 1e12 / (PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS),
+        "hbm_gbs": hbm / t_dyn / 1e9,
+        "pct_hbm_peak": 100.0 * hbm / t_dyn / 1e9 / PEAK_HBM_GBS,
         "algo_flop": flops,
         "algo_bytes": hbm,
-        "ms_by_mode": ms,
-        "gain_vs_static": (ms["static"] / ms["dynamic"]) if "static" in ms else None,
-        "gain_vs_multi_kernel": (ms["multi_kernel"] / ms["dynamic"]) if "multi_kernel" in ms else None,
+        "ms_by_mode": {m: round(v["mean"], 4) for m, v in ms.items()},
+        "ms_stats": {m: {k: round(x, 4) for k, x in v.items()} for m, v in ms.items()},
         "counts": count_stats if len(count_stats) <= 2 else {
             "R_total": sum(c["R"] for c in count_stats),
             "active_min": min(c["active"] for c in count_stats),
             "active_max": max(c["active"] for c in count_stats)},
-        "schedule": sched,
+        "mem_workers": [s["mem_workers"] for s in sched],
+        "schedule": st,
+        "cost_model_calibration": cal,
         "roofline": roof,
     }
-    if not args.no_cpu and not args.profile_only:
-        host = []
-        s0, t0_ = wl.layers[0], tensors[0]
-        n0 = {k: to_numpy(v) for k, v in t0_.items()}
-        n0["logits"] = routed[0].logits.cpu().numpy()
-        host.append(n0)
-        out["cpu_baseline"] = cpu_baseline(wl, host)
+    out.update(gains(ms))
+    if not args.no_ablations and not args.no_baselines:
+        out["ablations"] = ablations(run, max(5, args.steps // 2), max(2, args.warmup // 2))
+    n0 = None
+    if not args.no_cpu:
+        n0 = {k: to_numpy(v) for k, v in run.tensors[0].items()}
+        n0["logits"] = logits0
+    del run
+    torch.cuda.empty_cache()
+    if not args.no_others and not args.no_baselines:
+        others = {}
+        for cfg in (2, 3, 5):
+            if cfg == args.config:
+                continue
+            r2 = Runner(cfg, dev, args.combine)
+            ms2 = measure_modes(r2, max(5, args.steps // 2), max(2, args.warmup // 2))
+            others[r2.wl.name] = summarize(r2, ms2)
+            del r2
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
+    if n0 is not None:
+        out["cpu_baseline"] = cpu_baseline(wl, n0)
     print(json.dumps(out), flush=True)
 
 

@@ -22,7 +22,7 @@ ERRORS = {
 
 # Every function the header declares (checked by the CPU tests).
 EXPORTS = ["moe_workspace_size", "moe_query", "moe_layer", "moe_route_from_logits",
-           "moe_last_device_error", "moe_strerror"]
+           "moe_last_device_error", "moe_last_schedule", "moe_strerror"]
 
 
 class Desc(ctypes.Structure):
@@ -32,7 +32,7 @@ class Desc(ctypes.Structure):
         ("dtype", c_int), ("mode", c_int), ("split_policy", c_int),
         ("fixed_mem_workers", c_int), ("split_k", c_int), ("max_workers", c_int),
         ("flags", c_uint), ("trace", c_void_p), ("trace_cap", c_int), ("timeout_ms", c_int),
-        ("row_tile", c_int), ("combine", c_int),
+        ("row_tile", c_int), ("combine", c_int), ("timeout_ticks", c_int),
     ]
 
 
@@ -52,7 +52,15 @@ class Info(ctypes.Structure):
                 ("split_k", c_int), ("permute_rows", c_int), ("max_mtiles", c_int),
                 ("max_tasks", c_int), ("route_splits", c_int), ("combine_chunks", c_int), ("row_tile", c_int),
                 ("combine", c_int),
-                ("workspace_bytes", c_size_t)]
+                ("workspace_bytes", c_size_t),
+                ("cost_mfma_flops_per_cu", ctypes.c_float),
+                ("cost_gather_bytes_per_worker", ctypes.c_float),
+                ("cost_hbm_bytes", ctypes.c_float)]
+
+
+class Schedule(ctypes.Structure):
+    _fields_ = [("mem_workers", c_int), ("row_tiles", c_int), ("permute_tasks", c_int),
+                ("error", c_int)]
 
 
 class MoEError(RuntimeError):
@@ -86,6 +94,8 @@ def lib():
         L.moe_route_from_logits.restype = c_int
         L.moe_last_device_error.argtypes = [P(Desc), c_void_p, c_void_p]
         L.moe_last_device_error.restype = c_int
+        L.moe_last_schedule.argtypes = [P(Desc), c_void_p, c_void_p, P(Schedule)]
+        L.moe_last_schedule.restype = c_int
         L.moe_strerror.argtypes = [c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         _lib = L

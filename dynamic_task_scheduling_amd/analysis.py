@@ -107,6 +107,61 @@ def by_kind(tr: Dict[str, np.ndarray]) -> Dict[str, Dict[str, float]]:
     return out
 
 
+def row_tiles(counts, th: int):
+    """Expert row tiles in the builder's order -- experts by descending count,
+    ties to the lower index, each expert's tiles consecutive: (expert, rows)."""
+    order = sorted(range(len(counts)), key=lambda e: (-int(counts[e]), e))
+    tiles = []
+    for e in order:
+        c = int(counts[e])
+        for m in range((c + th - 1) // th):
+            tiles.append((e, min(th, c - th * m)))
+    return tiles
+
+
+def calibrate(tr: Dict[str, np.ndarray], info: Dict[str, float], shape, counts) -> Dict[str, float]:
+    """The cost model's per-worker rates re-measured from a task trace: the
+    bytes/s a gather (permute) task moves (rows read and written), and the
+    MFMA flop/s of full-height UP and DOWN tiles (executed flops), each the
+    median over its tasks; beside them the constants the library froze."""
+    esz = 4 if shape.dtype == "fp32" else 2
+    th = info["row_tile"]
+    pr = info["permute_rows"]
+    pch = th // pr
+    n_up, n_down, sk = info["up_ntiles"], info["down_ntiles"], info["split_k"]
+    tiles = row_tiles(counts, th)
+    dur = (tr["t_end"] - tr["t_start"]) / CLOCK_HZ
+    g_rates, up_rates, down_rates = [], [], []
+    for k, p, t in zip(tr["kind"], tr["payload"], dur):
+        if t <= 0:
+            continue
+        k, p = int(k), int(p)
+        if k == 3:                                     # PERM
+            mt, c = divmod(p, pch)
+            if mt < len(tiles):
+                rows = min(pr, tiles[mt][1] - c * pr)
+                g_rates.append(2.0 * rows * shape.d * esz / t)
+        elif k == 4:                                   # UP, full tiles only
+            mt = p // n_up
+            if mt < len(tiles) and tiles[mt][1] == th:
+                up_rates.append(4.0 * th * shape.d * 128 / t)
+        elif k == 5:                                   # DOWN, full tiles only
+            mt = p // sk // n_down
+            if mt < len(tiles) and tiles[mt][1] == th:
+                cols = shape.d // n_down
+                down_rates.append(2.0 * th * (shape.f / sk) * cols / t)
+    med = lambda xs: float(np.median(xs)) if xs else None
+    return {
+        "gather_bytes_per_s_per_worker": med(g_rates),
+        "up_flops_per_s_per_cu": med(up_rates),
+        "down_flops_per_s_per_cu": med(down_rates),
+        "tasks": {"perm": len(g_rates), "up_full": len(up_rates), "down_full": len(down_rates)},
+        "frozen": {"gather_bytes_per_s_per_worker": info.get("cost_gather_bytes_per_worker"),
+                   "mfma_flops_per_s_per_cu": info.get("cost_mfma_flops_per_cu"),
+                   "hbm_bytes_per_s": info.get("cost_hbm_bytes")},
+    }
+
+
 def geomean(xs) -> float:
     xs = [x for x in xs if x and x > 0]
     return math.exp(sum(math.log(x) for x in xs) / len(xs)) if xs else float("nan")

@@ -107,6 +107,15 @@ DEV int opaque_tid() {
   asm volatile("" : "+v"(t));
   return t;
 }
+// The thread index as every task body and scheduler step reads it: opaque at
+// each use, so no lane-dependent value is computed once before the
+// persistent loop and kept (or spilled) across all task types.
+DEV int tidx() { return opaque_tid(); }
+
+// A value every lane of the wave holds (a workgroup-wide result broadcast
+// through LDS), read from the first lane into a scalar register, so that the
+// branches and addresses that depend on it are scalar.
+DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Constant-rate device clock (100 MHz on CDNA3/CDNA4) for watchdogs and
 // the optional task trace.

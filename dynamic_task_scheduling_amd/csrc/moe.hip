@@ -8,9 +8,58 @@
 #include <mutex>
 
 #include "../../include/moe.h"
+#include "launch.hpp"
 #include "sched.hpp"
 
 using namespace moe;
+
+namespace moe {
+
+// Initial value of control word w (the first int of its 128-byte line; the
+// rest of the line is padding).  QA starts with the router tasks in its
+// slots, QC with the shared-expert UP tiles; queue totals other than QA's are
+// unknown until the builder publishes them.
+__host__ __device__ inline int ctrl_init(const Params& p, int w) {
+  const int n_route = p.n_rt * p.rsk;
+  if (w == CW_TAIL + QA) return n_route;
+  if (w == CW_TOTAL + QA) return n_route + p.n_rt;
+  if (w == CW_TAIL + QC) return p.n_sup;
+  if (w == CW_TOTAL + QM || w == CW_TOTAL + QC) return 0x7fffffff;
+  if (w >= CW_UTOTAL && w < CW_UTOTAL + kXcds) return 0x7fffffff;
+  return 0;
+}
+
+// Control block reset + queue seeding, launched before every call.  Every
+// word of the control block has exactly one writer here (the thread whose
+// index it is), which stores the word's initial value directly.
+__global__ __launch_bounds__(kThreads) void k_reset(Params p) {
+  const int gid = blockIdx.x * kThreads + threadIdx.x;
+  const int stride = gridDim.x * kThreads;
+  const int ncw = CW_COUNT * kCtrlStride;
+  for (int i = gid; i < ncw; i += stride)
+    p.ctrl[i] = (i % kCtrlStride == 0) ? ctrl_init(p, i / kCtrlStride) : 0;
+  const size_t ns = (size_t)kNumQueues * p.q_cap;
+  const int n_route = p.n_rt * p.rsk;
+  for (size_t i = gid; i < ns; i += stride) {
+    const size_t q = i / p.q_cap, j = i % p.q_cap;
+    int v = 0;
+    if (q == QA && j < (size_t)n_route) v = make_task(TK_ROUTE, (int)j) + 1;
+    else if (q == QC && j < (size_t)p.n_sup) v = make_task(TK_SUP, (int)j) + 1;
+    p.slots[i] = v;
+  }
+  for (int i = gid; i < p.n_rt; i += stride) p.cnt_route[i] = p.rsk;
+  const int nsm = p.n_shared * p.n_smt;
+  for (int i = gid; i < nsm; i += stride) p.cnt_sdown[i] = p.n_s_up_n + 1;
+  // combine tiles: the shared DOWN tiles over their tokens, plus one unit
+  // that the tile's POS task replaces by its routed DOWN tiles
+  for (int i = gid; i < p.n_rt; i += stride) p.cnt_comb[i] = 1 + p.n_shared * p.n_down_n;
+  if (p.flags & MOE_FLAG_XCD_AFFINITY) {
+    const size_t nu = (size_t)kXcds * p.q_cap;
+    for (size_t i = gid; i < nu; i += stride) p.uslots[i] = 0;
+  }
+}
+
+}  // namespace moe
 
 namespace {
 
@@ -228,13 +277,13 @@ int dev_info(int dev, DevInfo* out) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return MOE_ERR_HIP;
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_dynamic<float, false>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    if (occupancy_dynamic_f32(&b) != hipSuccess) return MOE_ERR_HIP;
     di.bpc[0][0] = b;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_static<float, false>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    if (occupancy_static_f32(&b) != hipSuccess) return MOE_ERR_HIP;
     di.bpc[0][1] = b;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_dynamic<bf16_t, false>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    if (occupancy_dynamic_bf16(&b) != hipSuccess) return MOE_ERR_HIP;
     di.bpc[1][0] = b;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_static<bf16_t, false>, kThreads, 0) != hipSuccess) return MOE_ERR_HIP;
+    if (occupancy_static_bf16(&b) != hipSuccess) return MOE_ERR_HIP;
     di.bpc[1][1] = b;
     di.cus = cus;
   }
@@ -263,40 +312,28 @@ int workers_for(const moe_desc* d, int* workers, int* cus, int* bpc) {
     if ((x) != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
-template <typename Elem>
-int launch_layer(const moe_desc* d, Params& p, hipStream_t s) {
+int launch_reset(const Params& p, hipStream_t s) {
   const int reset_blocks = (int)std::min<long long>(
       1024, ((long long)kNumQueues * p.q_cap + kThreads - 1) / kThreads + 1);
   hipLaunchKernelGGL(k_reset, dim3(reset_blocks), dim3(kThreads), 0, s, p);
   HIP_OK(hipGetLastError());
-  if (d->mode == MOE_DYNAMIC) {
-    if (p.comb_scatter)
-      hipLaunchKernelGGL((k_dynamic<Elem, true>), dim3(p.workers), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((k_dynamic<Elem, false>), dim3(p.workers), dim3(kThreads), 0, s, p);
-  } else if (d->mode == MOE_STATIC_PARTITION) {
-    if (p.comb_scatter)
-      hipLaunchKernelGGL((k_static<Elem, true>), dim3(p.workers), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((k_static<Elem, false>), dim3(p.workers), dim3(kThreads), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt * p.rsk), dim3(kThreads), 0, s, p);
-    HIP_OK(hipGetLastError());
-    hipLaunchKernelGGL(k_stage_build<Elem>, dim3(1), dim3(kThreads), 0, s, p);
-    HIP_OK(hipGetLastError());
-    hipLaunchKernelGGL(k_stage_pos<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
-    HIP_OK(hipGetLastError());
-    hipLaunchKernelGGL(k_stage_perm<Elem>, dim3(p.max_perm), dim3(kThreads), 0, s, p);
-    HIP_OK(hipGetLastError());
-    hipLaunchKernelGGL(k_stage_up<Elem>, dim3(p.max_mt * p.n_up_n + p.n_sup), dim3(kThreads), 0, s, p);
-    HIP_OK(hipGetLastError());
-    hipLaunchKernelGGL(k_stage_down<Elem>, dim3(p.max_mt * p.n_down_n * p.splitk + p.n_sdown),
-                       dim3(kThreads), 0, s, p);
-    HIP_OK(hipGetLastError());
-    if (!p.comb_scatter)
-      hipLaunchKernelGGL(k_stage_comb<Elem>, dim3(p.n_rt * p.n_cc), dim3(kThreads), 0, s, p);
-  }
-  HIP_OK(hipGetLastError());
+  return MOE_OK;
+}
+
+int launch_layer(const moe_desc* d, const Params& p, hipStream_t s) {
+  int rc = launch_reset(p, s);
+  if (rc) return rc;
+  const bool bf16 = d->dtype == MOE_BF16;
+  const bool scat = p.comb_scatter != 0;
+  hipError_t e;
+  if (d->mode == MOE_DYNAMIC)
+    e = bf16 ? (scat ? launch_dynamic_bf16_scatter(p, s) : launch_dynamic_bf16_rows(p, s))
+             : launch_dynamic_f32(scat, p, s);
+  else if (d->mode == MOE_STATIC_PARTITION)
+    e = bf16 ? launch_static_bf16(scat, p, s) : launch_static_f32(scat, p, s);
+  else
+    e = bf16 ? launch_stages_bf16(p, s) : launch_stages_f32(p, s);
+  HIP_OK(e);
   return MOE_OK;
 }
 
@@ -317,6 +354,17 @@ int copy_routing(const moe_desc* d, const Params& p, const moe_routing* r, hipSt
   return MOE_OK;
 }
 
+// Cost-model constants, measured once on MI355X and frozen (bench.py reports
+// the same quantities re-measured from a task trace beside them): the
+// sustained per-CU MFMA rate in expert tiles, the bytes/s one worker moves in
+// a gather task, and the device HBM bandwidth a streaming tile sustains.
+void set_cost_model(const moe_desc* d, Params* p) {
+  p->cm_mfma_rate = (d->dtype == MOE_BF16 ? 4.9e12f : 0.3e12f);
+  p->cm_cu_bw = 16e9f;
+  p->cm_hbm_bw = 6.0e12f;
+  p->cm_slack = 0.5f;
+}
+
 int fill_params(const moe_desc* d, Layout* L, void* ws, size_t ws_bytes) {
   int rc = validate(d);
   if (rc) return rc;
@@ -333,13 +381,8 @@ int fill_params(const moe_desc* d, Layout* L, void* ws, size_t ws_bytes) {
   if (!(p.flags & MOE_FLAG_REF_SYNC)) p.flags |= MOE_FLAG_PHASE_SYNC;
   const long long ms = d->timeout_ms > 0 ? d->timeout_ms : 2000;
   p.timeout_ticks = ms * 100000ll;  // 100 MHz constant clock
-  // cost model constants (measured on MI355X): sustained per-CU bf16 MFMA
-  // rate in expert tiles, the bytes/s one worker moves in a gather task, and
-  // the device HBM bandwidth a streaming tile sustains
-  p.cm_mfma_rate = (d->dtype == MOE_BF16 ? 4.9e12f : 0.3e12f);
-  p.cm_cu_bw = 16e9f;
-  p.cm_hbm_bw = 6.0e12f;
-  p.cm_slack = 0.5f;
+  if (d->timeout_ticks > 0) p.timeout_ticks = d->timeout_ticks;
+  set_cost_model(d, &p);
   p.trace = (d->flags & MOE_FLAG_TRACE) ? d->trace : nullptr;
   p.trace_cap = d->trace_cap;
   return MOE_OK;
@@ -377,6 +420,10 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->row_tile = L.p.th;
   info->combine = L.p.comb_scatter ? MOE_COMBINE_SCATTER : MOE_COMBINE_TASKS;
   info->workspace_bytes = L.total;
+  set_cost_model(d, &L.p);
+  info->cost_mfma_flops_per_cu = L.p.cm_mfma_rate;
+  info->cost_gather_bytes_per_worker = L.p.cm_cu_bw;
+  info->cost_hbm_bytes = L.p.cm_hbm_bw;
   return MOE_OK;
 }
 
@@ -400,7 +447,7 @@ int moe_layer(const moe_desc* d, const void* x, const moe_weights* w, float* y,
   p.sd = w->ws_down;
   p.y = y;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = d->dtype == MOE_BF16 ? launch_layer<bf16_t>(d, p, s) : launch_layer<float>(d, p, s);
+  rc = launch_layer(d, p, s);
   if (rc) return rc;
   rc = copy_routing(d, p, routing, s);
   if (rc) return rc;
@@ -419,20 +466,9 @@ int moe_route_from_logits(const moe_desc* d, const float* logits, const moe_rout
   p.route_from_logits = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   HIP_OK(hipMemcpyAsync(p.logits, logits, sizeof(float) * d->T * d->E, hipMemcpyDeviceToDevice, s));
-  const int reset_blocks = (int)std::min<long long>(
-      1024, ((long long)kNumQueues * p.q_cap + kThreads - 1) / kThreads + 1);
-  hipLaunchKernelGGL(k_reset, dim3(reset_blocks), dim3(kThreads), 0, s, p);
-  HIP_OK(hipGetLastError());
-  if (d->dtype == MOE_BF16) {
-    hipLaunchKernelGGL(k_stage_route<bf16_t>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(k_stage_build<bf16_t>, dim3(1), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(k_stage_pos<bf16_t>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(k_stage_route<float>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(k_stage_build<float>, dim3(1), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(k_stage_pos<float>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
-  }
-  HIP_OK(hipGetLastError());
+  rc = launch_reset(p, s);
+  if (rc) return rc;
+  HIP_OK(d->dtype == MOE_BF16 ? launch_route_only_bf16(p, s) : launch_route_only_f32(p, s));
   rc = copy_routing(d, p, routing, s);
   if (rc) return rc;
   if (d->flags & MOE_FLAG_CHECK) return moe_last_device_error(d, workspace, stream);
@@ -450,6 +486,22 @@ int moe_last_device_error(const moe_desc* d, const void* workspace, void* stream
   HIP_OK(hipMemcpy(&err, base + sizeof(int) * CW_ERROR * kCtrlStride, sizeof(int),
                    hipMemcpyDeviceToHost));
   return err;
+}
+
+int moe_last_schedule(const moe_desc* d, const void* workspace, void* stream, moe_schedule* out) {
+  if (validate(d) != MOE_OK || !workspace || !out) return MOE_ERR_ARG;
+  Layout L;
+  make_layout(d, &L);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_OK(hipStreamSynchronize(s));
+  int cw[CW_COUNT * kCtrlStride];
+  HIP_OK(hipMemcpy(cw, static_cast<const char*>(workspace) + L.off_ctrl, sizeof cw,
+                   hipMemcpyDeviceToHost));
+  out->mem_workers = cw[CW_WMEM * kCtrlStride];
+  out->row_tiles = cw[CW_NMT * kCtrlStride];
+  out->permute_tasks = cw[CW_NPERM * kCtrlStride];
+  out->error = cw[CW_ERROR * kCtrlStride];
+  return MOE_OK;
 }
 
 const char* moe_strerror(int code) {

@@ -75,14 +75,19 @@ DEV int wait_slot(const Params& p, const int* sl) {
 }
 
 // Thread 0: take an already-pushed UP task from the XCD queues, own first.
+// A slot is claimed (by compare-and-swap on the head) only while it lies
+// below the queue's tail, so the claimed slot has been pushed (its store is
+// at most one instruction behind the tail increment): a worker never waits
+// here on a slot that may never be filled.
 DEV int take_up(const Params& p) {
   const int x0 = xcc_id() & (kXcds - 1);
   for (int i = 0; i < kXcds; ++i) {
     const int x = (x0 + i) & (kXcds - 1);
-    if (ld_relaxed(ucw(p, CW_UHEAD, x)) < ld_relaxed(ucw(p, CW_UTAIL, x))) {
-      const int h = add_relaxed(ucw(p, CW_UHEAD, x), 1);
-      if (h < ld_relaxed(ucw(p, CW_UTOTAL, x)) && h < p.q_cap)
-        return wait_slot(p, p.uslots + (size_t)x * p.q_cap + h);
+    int h = ld_relaxed(ucw(p, CW_UHEAD, x));
+    while (h < ld_relaxed(ucw(p, CW_UTAIL, x)) && h < p.q_cap) {
+      const int seen = cas_relaxed(ucw(p, CW_UHEAD, x), h, h + 1);
+      if (seen == h) return wait_slot(p, p.uslots + (size_t)x * p.q_cap + h);
+      h = seen;
     }
   }
   return kClaimExhausted;
@@ -151,52 +156,51 @@ template <typename F>
 DEV void push_burst(const Params& p, int q, int n, int* s_tmp, F&& id_of) {
   if (n <= 0) return;
   publish_fence();
-  if (threadIdx.x == 0) s_tmp[0] = add_relaxed(cw(p, CW_TAIL + q), n);
+  if (tidx() == 0) s_tmp[0] = add_relaxed(cw(p, CW_TAIL + q), n);
   __syncthreads();
-  const int base = s_tmp[0];
+  const int base = uniform(s_tmp[0]);
   __syncthreads();
   if (base + n > p.q_cap) {
-    if (threadIdx.x == 0) set_error(p, 6 /* MOE_ERR_CAPACITY */);
+    if (tidx() == 0) set_error(p, 6 /* MOE_ERR_CAPACITY */);
     return;
   }
   int* slots = p.slots + (size_t)q * p.q_cap + base;
-  for (int i = threadIdx.x; i < n; i += kThreads) st_relaxed(slots + i, id_of(i) + 1);
+  for (int i = tidx(); i < n; i += kThreads) st_relaxed(slots + i, id_of(i) + 1);
 }
 
 // All threads: the last of `target` arrivals on counter c returns true.
 DEV bool arrive_last(int* c, int delta, int last_old, int* s_tmp) {
   publish_fence();
   __syncthreads();
-  if (threadIdx.x == 0) s_tmp[0] = (add_relaxed(c, delta) == last_old);
+  if (tidx() == 0) s_tmp[0] = (add_relaxed(c, delta) == last_old);
   __syncthreads();
-  const bool last = s_tmp[0] != 0;
+  const bool last = uniform(s_tmp[0]) != 0;
   __syncthreads();
   if (last) consume_fence();
   return last;
 }
 
 // Grid barrier over all workers (static mode).  Returns false on abort.
+// The arrival counter only grows (it starts at 0 in every launch): barrier
+// number gen is passed once (gen + 1) * workers arrivals are counted, so no
+// store ever resets a word another worker may still be adding to.
 DEV bool grid_barrier(const Params& p, int& gen, int* s_tmp) {
   publish_fence();
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tidx() == 0) {
     int ok = 1;
-    const int arrived = add_relaxed(cw(p, CW_BAR_COUNT), 1);
-    if (arrived == p.workers - 1) {
-      st_relaxed(cw(p, CW_BAR_COUNT), 0);
-      st_relaxed(cw(p, CW_BAR_GEN), gen + 1);
-    } else {
-      const uint64_t t0 = rtc();
-      while (ld_relaxed(cw(p, CW_BAR_GEN)) == gen) {
-        if (ld_relaxed(cw(p, CW_ERROR)) != 0) { ok = 0; break; }
-        if (timed_out(p, t0)) { set_error(p, 5); ok = 0; break; }
-        __builtin_amdgcn_s_sleep(1);
-      }
+    const int target = (gen + 1) * p.workers;
+    add_relaxed(cw(p, CW_BAR_COUNT), 1);
+    const uint64_t t0 = rtc();
+    while (ld_relaxed(cw(p, CW_BAR_COUNT)) < target) {
+      if (ld_relaxed(cw(p, CW_ERROR)) != 0) { ok = 0; break; }
+      if (timed_out(p, t0)) { set_error(p, 5); ok = 0; break; }
+      __builtin_amdgcn_s_sleep(1);
     }
     s_tmp[0] = ok;
   }
   __syncthreads();
-  const bool ok = s_tmp[0] != 0;
+  const bool ok = uniform(s_tmp[0]) != 0;
   __syncthreads();
   ++gen;
   consume_fence();
@@ -205,7 +209,8 @@ DEV bool grid_barrier(const Params& p, int& gen, int* s_tmp) {
 
 DEV void trace_record(const Params& p, int task, int worker, uint64_t t_req,
                       uint64_t t_start, uint64_t t_end) {
-  if (!(p.flags & kFlagTrace) || p.trace == nullptr || threadIdx.x != 0) return;
+  if (!(p.flags & kFlagTrace) || p.trace == nullptr || tidx() != 0) return;
+  asm volatile("" : "+v"(task));
   const int i = add_relaxed(cw(p, CW_TRACE), 1);
   if (i < p.trace_cap) {
     uint64_t* r = p.trace + (size_t)i * 4;
@@ -243,7 +248,7 @@ DEV void push_combine(const Params& p, int rt) {
 DEV void combine_arrive_rows(const Params& p, int row0, int rows, bool dyn) {
   publish_fence();
   __syncthreads();
-  const int r = threadIdx.x;
+  const int r = tidx();
   if (r < rows) {
     const int blk = p.perm[row0 + r] / kTB;
     const int prev = r > 0 ? p.perm[row0 + r - 1] / kTB : -1;
@@ -258,14 +263,14 @@ DEV void combine_arrive_shared(const Params& p, int m, bool dyn) {
   publish_fence();
   __syncthreads();
   const int per = p.th / kTB;
-  const int blk = m * per + (int)threadIdx.x;
-  if ((int)threadIdx.x < per && blk < p.n_rt &&
+  const int blk = m * per + tidx();
+  if (tidx() < per && blk < p.n_rt &&
       add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn)
     push_combine(p, blk);
   __syncthreads();
 }
 
-template <typename Elem>
+template <typename Elem, bool SCAT>
 struct Sched {
   using S = Stages<Elem>;
 
@@ -276,10 +281,10 @@ struct Sched {
     const bool split = p.split_policy != 2;
     const int n_up_qc = affinity(p) ? 0 : n_mt * p.n_up_n;
     const int n_comp = n_up_qc + n_mt * p.n_down_n * p.splitk + p.n_sup + p.n_sdown +
-                       (p.comb_scatter ? 0 : p.n_rt * p.n_cc);
+                       (SCAT ? 0 : p.n_rt * p.n_cc);
     publish_fence();
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tidx() == 0) {
       st_relaxed(cw(p, CW_TOTAL + QM), split ? n_perm : 0);
       st_relaxed(cw(p, CW_TOTAL + QC), n_comp + (split ? 0 : n_perm));
       if (affinity(p))
@@ -291,7 +296,7 @@ struct Sched {
     push_burst(p, QA, p.n_rt, s_tmp, [&](int i) { return make_task(TK_POS, i); });
     // shared-expert DOWN tiles waited for the routing phase (zeroed y rows)
     const int nsm = p.n_shared * p.n_smt;
-    for (int i = threadIdx.x; i < nsm; i += kThreads) {
+    for (int i = tidx(); i < nsm; i += kThreads) {
       if (add_relaxed(p.cnt_sdown + i, -1) == 1) {
         int* sl = nullptr;
         const int base = add_relaxed(cw(p, CW_TAIL + QC), p.n_down_n);
@@ -317,7 +322,7 @@ struct Sched {
     switch (kind) {
       case TK_ROUTE: {
         const int rt = pl / p.rsk;
-        S::route(p, rt, pl % p.rsk, smem);
+        S::route(p, rt, pl % p.rsk, smem, SCAT);
         *t_body = rtc();
         if (p.rsk > 1) {
           // the last K slice of this tile reduces the partials and routes
@@ -343,12 +348,12 @@ struct Sched {
         // the combine of these tokens waits for the DOWN tiles of the nd row
         // tiles holding their rows; this replaces the counter's initial
         // "positions pending" unit (k_reset) by that many tiles
-        if (threadIdx.x == 0) {
+        if (tidx() == 0) {
           const int delta = nd * p.n_down_n * p.splitk - 1;
-          s_tmp[0] = !p.comb_scatter && (add_relaxed(p.cnt_comb + pl, delta) + delta == 0);
+          s_tmp[0] = !SCAT && (add_relaxed(p.cnt_comb + pl, delta) + delta == 0);
         }
         __syncthreads();
-        const bool comb_ready = s_tmp[0] != 0;
+        const bool comb_ready = uniform(s_tmp[0]) != 0;
         __syncthreads();
         if (comb_ready && dyn)
           push_burst(p, QC, p.n_cc, s_tmp, [&](int c) { return make_task(TK_COMB, pl * p.n_cc + c); });
@@ -366,7 +371,7 @@ struct Sched {
         if (arrive_last(p.cnt_perm + mt, -1, 1, s_tmp) && dyn) {
           if (affinity(p)) {
             // one thread per column tile, into XCD n % 8's queue
-            const int n = threadIdx.x;
+            const int n = tidx();
             if (n < p.n_up_n) {
               const int x = n % kXcds;
               const int slot = add_relaxed(ucw(p, CW_UTAIL, x), 1);
@@ -398,9 +403,9 @@ struct Sched {
         const int ks = pl % p.splitk;
         const int r = pl / p.splitk;
         const int mt = r / p.n_down_n;
-        S::down(p, mt, r % p.n_down_n, ks, smem);
+        S::down(p, mt, r % p.n_down_n, ks, smem, SCAT);
         *t_body = rtc();
-        if (!p.comb_scatter) {
+        if (!SCAT) {
           const MTile t = p.mtiles[mt];
           combine_arrive_rows(p, t.row0, t.rows, dyn);
         }
@@ -419,9 +424,9 @@ struct Sched {
       case TK_SDOWN: {
         const int n = pl % p.n_down_n;
         const int sm = pl / p.n_down_n;
-        S::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem);
+        S::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem, SCAT);
         *t_body = rtc();
-        if (!p.comb_scatter) combine_arrive_shared(p, sm % p.n_smt, dyn);
+        if (!SCAT) combine_arrive_shared(p, sm % p.n_smt, dyn);
         break;
       }
       case TK_COMB: {
@@ -430,164 +435,222 @@ struct Sched {
         break;
       }
       default:
-        if (threadIdx.x == 0) set_error(p, 1);
+        if (tidx() == 0) set_error(p, 1);
     }
     __syncthreads();
   }
 };
 
 // ------------------------------------------------------------- dynamic
+// Thread 0, once a worker's router-queue claim is exhausted: until the
+// builder has published the split, take the pre-seeded shared-expert UP tiles
+// (slots [0, n_sup) of the compute queue; they need no routing, so they fill
+// the routing phase's idle workers).  A slot is taken by compare-and-swap
+// only while the head is below n_sup, so nobody commits to a compute slot
+// before the split exists.  Returns a task, or kClaimExhausted once the split
+// is ready (*role then holds the worker's queue), or kClaimAbort.
+DEV int wait_split(const Params& p, int* role) {
+  const uint64_t t0 = rtc();
+  for (;;) {
+    const int ready = ld_relaxed(cw(p, CW_SPLIT_READY));
+    const int h = ld_relaxed(cw(p, CW_HEAD + QC));
+    const int err = ld_relaxed(cw(p, CW_ERROR));
+    if (err != 0) return kClaimAbort;
+    if (ready != 0) break;
+    if (h < p.n_sup) {
+      if (cas_relaxed(cw(p, CW_HEAD + QC), h, h + 1) == h) return make_task(TK_SUP, h);
+      continue;
+    }
+    if (timed_out(p, t0)) {
+      set_error(p, 5 /* MOE_ERR_TIMEOUT */);
+      return kClaimAbort;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  int nq = QC;
+  if (p.split_policy != 2) {
+    const int wm = ld_relaxed(cw(p, CW_WMEM));
+    nq = (add_relaxed(cw(p, CW_ROLE), 1) < wm) ? QM : QC;
+  }
+  *role = nq;
+  return kClaimExhausted;
+}
+
+// The launch parameters as the task bodies see them: the same kernel-argument
+// block, reached through an offset the compiler cannot prove is zero, so
+// nothing a task derives from the parameters (tile addresses, per-lane
+// offsets, loop bounds) is hoisted out of the persistent loop and held in
+// registers across every task type -- the parameters stay in the scalar
+// cache and are reloaded per task for a few cycles.
+DEV const Params& params_view(const Params& p) {
+  int off = 0;
+  asm volatile("" : "+s"(off));
+  return *reinterpret_cast<const Params*>(reinterpret_cast<const char*>(&p) + off);
+}
+
 // SCAT: the layer's combine mode as a compile-time constant, so each
 // instantiation holds only its own DOWN epilogue and combine code (the
 // persistent kernel's register allocation covers every task type at once).
+// The launch parameters stay in the kernel-argument segment (read-only,
+// loaded into scalar registers on use); the combine mode is passed down as a
+// template argument instead of being written into a private copy.
 template <typename Elem, bool SCAT>
-__global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p_in) {
-  Params p = p_in;
-  p.comb_scatter = SCAT;
+__global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
   __shared__ int s_tmp[4];
   __shared__ int s_worker;
-  if (threadIdx.x == 0) s_worker = add_relaxed(cw(p, CW_TICKET), 1);
+  if (tidx() == 0) s_worker = add_relaxed(cw(p, CW_TICKET), 1);
   int q = QA;
   int pend = -1;   // thread 0: claimed but not yet filled slot of queue q
   const bool steal = p.split_policy != 2 && !(p.flags & kFlagNoSteal);
   for (;;) {
     uint64_t t_req = rtc();
-    if (threadIdx.x == 0) s_tmp[1] = claim(p, q, pend, steal && q == QC);
+    if (tidx() == 0) {
+      int v = claim(p, q, pend, steal && q == QC);
+      int role = q;
+      // routing phase over for this worker: shared-expert tiles until the
+      // split is published, then the role the split assigns
+      if (v == kClaimExhausted && q == QA) v = wait_split(p, &role);
+      s_tmp[1] = v;
+      s_tmp[2] = role;
+    }
     __syncthreads();
-    const int v = s_tmp[1];
+    const int v = uniform(s_tmp[1]);
+    const int nq = uniform(s_tmp[2]);
     __syncthreads();
     if (v == kClaimAbort) break;
     if (v == kClaimExhausted) {
-      if (q == QA) {
-        // routing phase over: wait for the split, then take a role ticket
-        if (threadIdx.x == 0) {
-          const uint64_t t0 = rtc();
-          int nq = QC;
-          while (ld_relaxed(cw(p, CW_SPLIT_READY)) == 0) {
-            if (ld_relaxed(cw(p, CW_ERROR)) != 0 || timed_out(p, t0)) {
-              if (ld_relaxed(cw(p, CW_ERROR)) == 0) set_error(p, 5);
-              nq = -1;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-          if (nq >= 0 && p.split_policy != 2) {
-            const int wm = ld_relaxed(cw(p, CW_WMEM));
-            nq = (add_relaxed(cw(p, CW_ROLE), 1) < wm) ? QM : QC;
-          }
-          s_tmp[2] = nq;
-        }
-        __syncthreads();
-        q = s_tmp[2];
-        __syncthreads();
-        if (q < 0) break;
-        continue;
-      }
-      if (q == QM) {
-        q = QC;
-        continue;
-      }
+      if (q == QA) { q = nq; continue; }
+      if (q == QM) { q = QC; continue; }
       break;
     }
     consume_fence();
     const uint64_t t_start = rtc();
     uint64_t t_body;
-    Sched<Elem>::run(p, v, smem, s_tmp, true, &t_body, s_worker);
+    Sched<Elem, SCAT>::run(params_view(p), v, smem, s_tmp, true, &t_body, s_worker);
     trace_record(p, v, s_worker, t_req, t_start, t_body);
   }
 }
 
 // -------------------------------------------------------------- static
+// The worker walks a fixed plan: its round-robin share of each stage, with a
+// grid barrier between stages (phase sync), or -- MOE_FLAG_REF_SYNC -- a
+// fixed memory group for the gather, and a spin on each task's own
+// dependency counter instead of barriers.  The plan is a small state machine
+// with ONE call site of the task body, so the kernel holds one copy of every
+// tile (register allocation as in the dynamic kernel).
 template <typename Elem, bool SCAT>
-__global__ __launch_bounds__(kThreads, 1) void k_static(Params p_in) {
-  Params p = p_in;
-  p.comb_scatter = SCAT;
+__global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
   __shared__ int s_tmp[4];
-  if (threadIdx.x == 0) s_tmp[3] = add_relaxed(cw(p, CW_TICKET), 1);
+  if (tidx() == 0) s_tmp[3] = add_relaxed(cw(p, CW_TICKET), 1);
   __syncthreads();
-  const int w = s_tmp[3];
+  const int w = uniform(s_tmp[3]);
   const int W = p.workers;
-  int gen = 0;
-  using SC = Sched<Elem>;
-  auto exec = [&](int task) __attribute__((always_inline)) {
-    const uint64_t t0 = rtc();
-    uint64_t t_body;
-    SC::run(p, task, smem, s_tmp, false, &t_body, w);
-    trace_record(p, task, w, t0, t0, t_body);
-  };
-  // stage 1: router tiles and shared-expert UP tiles
+  const bool ref = (p.flags & kFlagRefSync) && W >= 2;
+  const int wm = max(1, p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8);
   const int n_route = p.n_rt * p.rsk;
   const int nA = n_route + p.n_sup;
-  for (int i = w; i < nA; i += W)
-    exec(i < n_route ? make_task(TK_ROUTE, i) : make_task(TK_SUP, i - n_route));
-  if (!grid_barrier(p, gen, s_tmp)) return;
-  if (w == 0) {
-    Stages<Elem>::build(p, smem);
-    __syncthreads();
-    // the routing stage (which zeroes y) is over: release the shared DOWN tiles
-    for (int i = threadIdx.x; i < p.n_shared * p.n_smt; i += kThreads)
-      add_relaxed(p.cnt_sdown + i, -1);
-  }
-  if (!grid_barrier(p, gen, s_tmp)) return;
-  for (int i = w; i < p.n_rt; i += W) exec(make_task(TK_POS, i));
-  if (!grid_barrier(p, gen, s_tmp)) return;
-  const int n_mt = ld_relaxed(cw(p, CW_NMT));
-  const int n_perm = ld_relaxed(cw(p, CW_NPERM));
-  const int n_up = n_mt * p.n_up_n;
-  const int n_down = n_mt * p.n_down_n * p.splitk;
-  if (!(p.flags & kFlagRefSync) || W < 2) {
-    for (int i = w; i < n_perm; i += W) exec(p.perm_list[i]);
-    if (!grid_barrier(p, gen, s_tmp)) return;
-    for (int i = w; i < n_up; i += W) exec(make_task(TK_UP, i));
-    if (!grid_barrier(p, gen, s_tmp)) return;
-    for (int i = w; i < n_down + p.n_sdown; i += W)
-      exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
-    if (p.comb_scatter) return;
-    if (!grid_barrier(p, gen, s_tmp)) return;
-    for (int i = w; i < p.n_rt * p.n_cc; i += W) exec(make_task(TK_COMB, i));
-    return;
-  }
-  // fixed split, per-task counter waits, no barriers
-  const int wm = max(1, p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8);
-  if (w < wm) {
-    for (int i = w; i < n_perm; i += wm) exec(p.perm_list[i]);
-  } else {
-    for (int i = w - wm; i < n_up; i += W - wm) {
-      if (threadIdx.x == 0) s_tmp[1] = wait_zero(p, p.cnt_perm + i / p.n_up_n);
+  enum { ST_A, ST_BUILD, ST_POS, ST_PERM, ST_UP, ST_DOWN, ST_COMB };
+  int st = ST_A, i = w, gen = 0;
+  int n_mt = 0, n_perm = 0, n_up = 0, n_down = 0;
+  for (;;) {
+    // this worker's next task: the rest of its share of the current stage,
+    // else the stage transition (barrier, builder) and the next stage
+    int task = -1;
+    const int* dep = nullptr;
+    for (;;) {
+      if (st == ST_A) {
+        // router tiles and shared-expert UP tiles
+        if (i < nA) {
+          task = i < n_route ? make_task(TK_ROUTE, i) : make_task(TK_SUP, i - n_route);
+          i += W;
+          break;
+        }
+        if (!grid_barrier(p, gen, s_tmp)) return;
+        st = ST_BUILD;
+      } else if (st == ST_BUILD) {
+        if (w == 0) {
+          Stages<Elem>::build(params_view(p), smem);
+          __syncthreads();
+          // the routing stage (which zeroes y) is over: release the shared DOWN tiles
+          for (int s = tidx(); s < p.n_shared * p.n_smt; s += kThreads)
+            add_relaxed(p.cnt_sdown + s, -1);
+        }
+        if (!grid_barrier(p, gen, s_tmp)) return;
+        st = ST_POS;
+        i = w;
+      } else if (st == ST_POS) {
+        if (i < p.n_rt) {
+          task = make_task(TK_POS, i);
+          i += W;
+          break;
+        }
+        if (!grid_barrier(p, gen, s_tmp)) return;
+        n_mt = uniform(ld_relaxed(cw(p, CW_NMT)));
+        n_perm = uniform(ld_relaxed(cw(p, CW_NPERM)));
+        n_up = n_mt * p.n_up_n;
+        n_down = n_mt * p.n_down_n * p.splitk;
+        st = ST_PERM;
+        i = !ref ? w : (w < wm ? w : n_perm);
+      } else if (st == ST_PERM) {
+        if (i < n_perm) {
+          task = p.perm_list[i];
+          i += ref ? wm : W;
+          break;
+        }
+        if (!ref && !grid_barrier(p, gen, s_tmp)) return;
+        st = ST_UP;
+        i = !ref ? w : (w >= wm ? w - wm : n_up);
+      } else if (st == ST_UP) {
+        if (i < n_up) {
+          task = make_task(TK_UP, i);
+          if (ref) dep = p.cnt_perm + i / p.n_up_n;
+          i += ref ? W - wm : W;
+          break;
+        }
+        if (!ref && !grid_barrier(p, gen, s_tmp)) return;
+        st = ST_DOWN;
+        i = w;
+      } else if (st == ST_DOWN) {
+        if (i < n_down + p.n_sdown) {
+          if (i < n_down) {
+            task = make_task(TK_DOWN, i);
+            const int ks = i % p.splitk, mt = i / p.splitk / p.n_down_n;
+            if (ref) dep = p.cnt_down + mt * p.splitk + ks;
+          } else {
+            task = make_task(TK_SDOWN, i - n_down);
+            if (ref) dep = p.cnt_sdown + (i - n_down) / p.n_down_n;
+          }
+          i += W;
+          break;
+        }
+        if (SCAT) return;
+        if (!ref && !grid_barrier(p, gen, s_tmp)) return;
+        st = ST_COMB;
+        i = w;
+      } else {
+        if (i < p.n_rt * p.n_cc) {
+          task = make_task(TK_COMB, i);
+          if (ref) dep = p.cnt_comb + i / p.n_cc;
+          i += W;
+          break;
+        }
+        return;
+      }
+    }
+    if (dep != nullptr) {
+      if (tidx() == 0) s_tmp[1] = wait_zero(p, dep);
       __syncthreads();
-      const bool ok = s_tmp[1];
+      const bool ok = uniform(s_tmp[1]) != 0;
       __syncthreads();
       if (!ok) return;
       consume_fence();
-      exec(make_task(TK_UP, i));
     }
-  }
-  for (int i = w; i < n_down + p.n_sdown; i += W) {
-    const int* c;
-    if (i < n_down) {
-      const int ks = i % p.splitk, mt = i / p.splitk / p.n_down_n;
-      c = p.cnt_down + mt * p.splitk + ks;
-    } else {
-      c = p.cnt_sdown + (i - n_down) / p.n_down_n;
-    }
-    if (threadIdx.x == 0) s_tmp[1] = wait_zero(p, c);
-    __syncthreads();
-    const bool ok = s_tmp[1];
-    __syncthreads();
-    if (!ok) return;
-    consume_fence();
-    exec(i < n_down ? make_task(TK_DOWN, i) : make_task(TK_SDOWN, i - n_down));
-  }
-  for (int i = w; i < (p.comb_scatter ? 0 : p.n_rt * p.n_cc); i += W) {
-    if (threadIdx.x == 0) s_tmp[1] = wait_zero(p, p.cnt_comb + i / p.n_cc);
-    __syncthreads();
-    const bool ok = s_tmp[1];
-    __syncthreads();
-    if (!ok) return;
-    consume_fence();
-    exec(make_task(TK_COMB, i));
+    const uint64_t t0 = rtc();
+    uint64_t t_body;
+    Sched<Elem, SCAT>::run(params_view(p), task, smem, s_tmp, false, &t_body, w);
+    trace_record(p, task, w, t0, t0, t_body);
   }
 }
 
@@ -600,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_route(Params p) {
     return;
   }
   const int rt = blockIdx.x / p.rsk;
-  Stages<Elem>::route(p, rt, blockIdx.x % p.rsk, smem);
+  Stages<Elem>::route(p, rt, blockIdx.x % p.rsk, smem, p.comb_scatter != 0);
   if (p.rsk > 1) {
     __shared__ int s_tmp[4];
     if (!arrive_last(p.cnt_route + rt, -1, 1, s_tmp)) return;
@@ -653,11 +716,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_stage_down(Params p) {
     const int n_mt = ld_relaxed(cw(p, CW_NMT));
     if (b >= n_mt * p.n_down_n * p.splitk) return;
     const int ks = b % p.splitk, r = b / p.splitk;
-    Stages<Elem>::down(p, r / p.n_down_n, r % p.n_down_n, ks, smem);
+    Stages<Elem>::down(p, r / p.n_down_n, r % p.n_down_n, ks, smem, p.comb_scatter != 0);
   } else {
     const int pl = b - routed;
     const int n = pl % p.n_down_n, sm = pl / p.n_down_n;
-    Stages<Elem>::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem);
+    Stages<Elem>::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem, p.comb_scatter != 0);
   }
 }
 
@@ -667,41 +730,30 @@ __global__ __launch_bounds__(kThreads) void k_stage_comb(Params p) {
   Stages<Elem>::combine(p, blockIdx.x / p.n_cc, blockIdx.x % p.n_cc, smem);
 }
 
-// Control block reset + queue seeding, launched before every call.
-__global__ __launch_bounds__(kThreads) void k_reset(Params p) {
-  const int gid = blockIdx.x * kThreads + threadIdx.x;
-  const int stride = gridDim.x * kThreads;
-  const int ncw = CW_COUNT * kCtrlStride;
-  for (int i = gid; i < ncw; i += stride) p.ctrl[i] = 0;
-  const size_t ns = (size_t)kNumQueues * p.q_cap;
-  const int n_route = p.n_rt * p.rsk;
-  // QA starts with the router tasks, QC with the shared-expert UP tiles
-  // (they need no routing, so they fill the routing phase's idle workers)
-  for (size_t i = gid; i < ns; i += stride) {
-    const size_t q = i / p.q_cap, j = i % p.q_cap;
-    int v = 0;
-    if (q == QA && j < (size_t)n_route) v = make_task(TK_ROUTE, (int)j) + 1;
-    else if (q == QC && j < (size_t)p.n_sup) v = make_task(TK_SUP, (int)j) + 1;
-    p.slots[i] = v;
-  }
-  for (int i = gid; i < p.n_rt; i += stride) p.cnt_route[i] = p.rsk;
-  const int nsm = p.n_shared * p.n_smt;
-  for (int i = gid; i < nsm; i += stride) p.cnt_sdown[i] = p.n_s_up_n + 1;
-  // combine tiles: the shared DOWN tiles over their tokens, plus one unit
-  // that the tile's POS task replaces by its routed DOWN tiles
-  for (int i = gid; i < p.n_rt; i += stride) p.cnt_comb[i] = 1 + p.n_shared * p.n_down_n;
-  if (p.flags & kFlagXcdAffinity) {
-    const size_t nu = (size_t)kXcds * p.q_cap;
-    for (size_t i = gid; i < nu; i += stride) p.uslots[i] = 0;
-    if (gid < kXcds) p.ctrl[(CW_UTOTAL + gid) * kCtrlStride] = 0x7fffffff;
-  }
-  if (gid == 0) {
-    p.ctrl[(CW_TAIL + QA) * kCtrlStride] = n_route;
-    p.ctrl[(CW_TOTAL + QA) * kCtrlStride] = n_route + p.n_rt;
-    p.ctrl[(CW_TAIL + QC) * kCtrlStride] = p.n_sup;
-    p.ctrl[(CW_TOTAL + QM) * kCtrlStride] = 0x7fffffff;
-    p.ctrl[(CW_TOTAL + QC) * kCtrlStride] = 0x7fffffff;
-  }
+// --------------------------------------------- host: stage sequences
+// The multi-kernel baseline: one ordinary launch per stage, in stage order on
+// stream s; the launch boundaries are its only synchronisation.
+template <typename Elem>
+hipError_t launch_stage_sequence(const Params& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt * p.rsk), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_stage_build<Elem>, dim3(1), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_stage_pos<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_stage_perm<Elem>, dim3(p.max_perm), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_stage_up<Elem>, dim3(p.max_mt * p.n_up_n + p.n_sup), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_stage_down<Elem>, dim3(p.max_mt * p.n_down_n * p.splitk + p.n_sdown),
+                     dim3(kThreads), 0, s, p);
+  if (!p.comb_scatter)
+    hipLaunchKernelGGL(k_stage_comb<Elem>, dim3(p.n_rt * p.n_cc), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// Routing only, from logits already in p.logits (p.route_from_logits = 1).
+template <typename Elem>
+hipError_t launch_route_sequence(const Params& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_stage_build<Elem>, dim3(1), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(k_stage_pos<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -31,13 +31,18 @@ DEV float mono_value(uint32_t m) {
   return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
 }
 
+// The error code passes through an empty asm so that the compare-and-swap
+// operands are formed where the error is raised, not once before the
+// persistent loop (where they would occupy registers across every task).
 DEV void set_error(const Params& p, int code) {
+  asm volatile("" : "+v"(code));
   cas_relaxed(p.ctrl + CW_ERROR * kCtrlStride, 0, code);
 }
 
 // Thread 0 appends one trace record for a scheduler phase (see trace_mark).
 DEV void trace_step(const Params& p, int phase, int worker, uint64_t t0, uint64_t t1) {
-  if (p.trace == nullptr || threadIdx.x != 0) return;
+  if (p.trace == nullptr || tidx() != 0) return;
+  asm volatile("" : "+s"(phase));
   const int i = add_relaxed(p.ctrl + 20 /* CW_TRACE */ * kCtrlStride, 1);
   if (i < p.trace_cap) {
     uint64_t* r = p.trace + (size_t)i * 4;
@@ -167,7 +172,7 @@ struct Stages {
   static DEV void topk(const Params& p, int t0, int rows, const float* L, int ldl,
                        int* hist_s) {
     static_assert(kTB == 32 && kThreads == 256 && kMaxK <= 8, "8 lanes per token");
-    const int tid = threadIdx.x;
+    const int tid = tidx();
     const int g = tid & 7;                  // lane within the token's group
     const int r = tid >> 3;                 // token row in the tile (0..31)
     const int E = p.E, k = p.k;
@@ -217,7 +222,7 @@ struct Stages {
   }
 
   static DEV void write_hist(const Params& p, int rt, const int* hist_s) {
-    for (int e = threadIdx.x; e < p.E_loc; e += kThreads)
+    for (int e = tidx(); e < p.E_loc; e += kThreads)
       st_wt(p.hist + (size_t)e * p.hist_ld + rt, hist_s[e]);
   }
 
@@ -265,17 +270,17 @@ struct Stages {
     return p.route_part + ((size_t)rt * p.rsk + ks) * kTB * p.E;
   }
 
-  static TASKFN void route(const Params& p, int rt, int ks, char* smem) {
+  static TASKFN void route(const Params& p, int rt, int ks, char* smem, bool scat) {
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     // the bias load is issued first, so its latency hides under the GEMM
-    const float bias_v = (p.rsk == 1 && p.bias && (int)threadIdx.x < p.E) ? p.bias[threadIdx.x] : 0.f;
+    const float bias_v = (p.rsk == 1 && p.bias && tidx() < p.E) ? p.bias[tidx()] : 0.f;
     // scatter-add combine: this slice zeroes its share of the tile's y rows
     // (rows ks, ks + rsk, ...), which the DOWN tiles then accumulate into
-    if (p.comb_scatter) {
+    if (scat) {
       for (int r = ks; r < rows; r += p.rsk) {
         float* yr = p.y + (size_t)(t0 + r) * p.d;
-        for (int i = threadIdx.x; i < p.d / 4; i += kThreads)
+        for (int i = tidx(); i < p.d / 4; i += kThreads)
           st_wt16(yr, i * 16, make_uint4(0, 0, 0, 0));
       }
     }
@@ -288,7 +293,7 @@ struct Stages {
       route_gemm<Tile<Elem, 32, 1>>(p, t0, rows, ks * Ks, Ks, Ls, part, smem);
     if (p.rsk == 1) {
       float* bias_s = reinterpret_cast<float*>(smem + kRouteTile + 32 * kMaxE * 4 + kMaxE * 4);
-      if ((int)threadIdx.x < p.E) bias_s[threadIdx.x] = bias_v;
+      if (tidx() < p.E) bias_s[tidx()] = bias_v;
       route_topk(p, rt, smem);
     }
   }
@@ -301,7 +306,7 @@ struct Stages {
     const int rows = min(kTB, p.T - t0);
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
     float* bias_s = reinterpret_cast<float*>(smem + kRouteTile + 32 * kMaxE * 4 + kMaxE * 4);
-    const float bias_v = (p.bias && (int)threadIdx.x < p.E) ? p.bias[threadIdx.x] : 0.f;
+    const float bias_v = (p.bias && tidx() < p.E) ? p.bias[tidx()] : 0.f;
     const int tid = opaque_tid();
     const int wave = tid >> 6, lane = tid & 63;
     const int bytes = p.rsk * kTB * p.E * 4;            // <= kRouteStage (host-checked)
@@ -317,12 +322,12 @@ struct Stages {
     const float* st = reinterpret_cast<const float*>(smem);
     const int n = rows * p.E;
     const int blk = kTB * p.E;
-    for (int i = threadIdx.x; i < n; i += kThreads) {
+    for (int i = tidx(); i < n; i += kThreads) {
       float v = 0.f;
       for (int ks = 0; ks < p.rsk; ++ks) v += st[ks * blk + i];
       Ls[i] = v;
     }
-    if ((int)threadIdx.x < p.E) bias_s[threadIdx.x] = bias_v;
+    if (tidx() < p.E) bias_s[tidx()] = bias_v;
     __syncthreads();
     route_topk(p, rt, smem);
   }
@@ -335,9 +340,9 @@ struct Stages {
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
     int* hist_s = reinterpret_cast<int*>(smem + kRouteTile + 32 * kMaxE * 4);
     const float* bias_s = reinterpret_cast<const float*>(hist_s + kMaxE);
-    for (int e = threadIdx.x; e < p.E_loc; e += kThreads) hist_s[e] = 0;
+    for (int e = tidx(); e < p.E_loc; e += kThreads) hist_s[e] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < rows * p.E; i += kThreads) {
+    for (int i = tidx(); i < rows * p.E; i += kThreads) {
       const float v = Ls[i] + bias_s[i % p.E];
       Ls[i] = v;
       p.logits[(size_t)t0 * p.E + i] = v;
@@ -353,7 +358,7 @@ struct Stages {
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     int* hist_s = reinterpret_cast<int*>(smem);
-    for (int e = threadIdx.x; e < p.E_loc; e += kThreads) hist_s[e] = 0;
+    for (int e = tidx(); e < p.E_loc; e += kThreads) hist_s[e] = 0;
     __syncthreads();
     topk(p, t0, rows, p.logits + (size_t)t0 * p.E, p.E, hist_s);
     __syncthreads();
@@ -364,7 +369,7 @@ struct Stages {
   // Workgroup-wide exclusive prefix sum of one int per thread; returns the
   // thread's exclusive prefix, *total receives the sum.  s_w: 4 ints of LDS.
   static DEV int block_exscan(int v, int* s_w, int* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = tidx() & 63, wave = tidx() >> 6;
     int inc = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -387,7 +392,7 @@ struct Stages {
 
   // Workgroup-wide float sum in a fixed order (deterministic).
   static DEV float block_sum(float v, float* s_w) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = tidx() & 63, wave = tidx() >> 6;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     if (lane == 0) s_w[wave] = v;
@@ -423,7 +428,7 @@ struct Stages {
     int* s_w = s_pb + 257;                                // [8] scan / reduction scratch
     float* s_wf = reinterpret_cast<float*>(s_w + 4);
     int* s_h = reinterpret_cast<int*>(smem + kBuildScratch);   // histogram staging
-    const int tid = threadIdx.x;
+    const int tid = tidx();
     const int El = p.E_loc;
     // 1. per-expert counts and per-tile exclusive bases, in column chunks of
     //    the [El][n_rt] histogram (row stride cwp = cw + 1: the per-expert
@@ -622,7 +627,7 @@ struct Stages {
     int* s_e = reinterpret_cast<int*>(smem);             // [256]
     int* s_mt = s_e + kThreads;                          // [256] row tile of each slot
     int* s_nd = s_mt + kThreads;                         // distinct row tiles
-    const int i = threadIdx.x;
+    const int i = tidx();
     if (i == 0) *s_nd = 0;
     int e = -1;
     float w = 0.f;
@@ -663,7 +668,7 @@ struct Stages {
       if (first) atomicAdd(s_nd, 1);
     }
     __syncthreads();
-    const int nd = *s_nd;
+    const int nd = uniform(*s_nd);
     __syncthreads();
     return nd;
   }
@@ -677,7 +682,7 @@ struct Stages {
     const MTile t = p.mtiles[mt];
     const int r0 = t.row0 + c * p.perm_rows;
     const int r1 = min(t.row0 + t.rows, r0 + p.perm_rows);
-    if ((int)threadIdx.x < r1 - r0) s_tok[threadIdx.x] = p.perm[r0 + threadIdx.x];
+    if (tidx() < r1 - r0) s_tok[tidx()] = p.perm[r0 + tidx()];
     __syncthreads();
     const int cpr = p.d * (int)sizeof(Elem) / 16;           // 16-byte chunks per row
     const int total = (r1 - r0) * cpr;
@@ -687,7 +692,7 @@ struct Stages {
     // 16 loads in flight per thread (64 KB per workgroup): a gather is a
     // latency-bound copy, so bytes in flight set its rate.
     constexpr int U = 16;
-    for (int i0 = threadIdx.x; i0 < total; i0 += U * kThreads) {
+    for (int i0 = tidx(); i0 < total; i0 += U * kThreads) {
       uint4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -738,7 +743,7 @@ struct Stages {
     });
     __syncthreads();
     constexpr int CPR = kBN * (int)sizeof(Elem) / 16;
-    for (int i = threadIdx.x; i < rows * CPR; i += kThreads) {
+    for (int i = tidx(); i < rows * CPR; i += kThreads) {
       const int r = i / CPR, c = i % CPR;
       st_wt16(Hout + (size_t)r * ldh, c * 16,
               *reinterpret_cast<const uint4*>(st + r * SLD + c * (16 / (int)sizeof(Elem))));
@@ -792,12 +797,12 @@ struct Stages {
         // consecutive floats of one token row
         const int* s_tok = down_rows_tok();
         const float* s_wt = down_rows_wt();
-        for (int i = threadIdx.x; i < rows * kBN; i += kThreads) {
+        for (int i = tidx(); i < rows * kBN; i += kThreads) {
           const int r = i / kBN, c = i % kBN;
           unsafeAtomicAdd(out + (size_t)s_tok[r] * ldo + m * kBN + c, s_wt[r] * st[r * SLD + c]);
         }
       } else {
-        for (int i = threadIdx.x; i < rows * CPR; i += kThreads) {
+        for (int i = tidx(); i < rows * CPR; i += kThreads) {
           const int r = i / CPR, c = i % CPR;
           st_wt16(out + (size_t)r * ldo + m * kBN, c * 16,
                   *reinterpret_cast<const uint4*>(st + r * SLD + c * 4));
@@ -827,7 +832,7 @@ struct Stages {
   }
   // Fill it: tok == nullptr means tokens row_tok0 + r with weight 1.
   static DEV void down_rows(int rows, const int* tok, const float* wt, int row_tok0) {
-    const int r = threadIdx.x;
+    const int r = tidx();
     if (r < rows) {
       down_rows_tok()[r] = tok ? tok[r] : row_tok0 + r;
       down_rows_wt()[r] = tok ? wt[r] : 1.0f;
@@ -864,7 +869,7 @@ struct Stages {
     up_any(t.bm, A, p.d, t.rows, wg, wu, p.f, p.d, H, p.f, smem);
   }
 
-  static TASKFN void down(const Params& p, int mt, int n, int ks, char* smem) {
+  static TASKFN void down(const Params& p, int mt, int n, int ks, char* smem, bool scat) {
     const MTile t = p.mtiles[mt];
     const int k_lo = slice_lo(ks, p.n_up_n, p.splitk) * kBN;
     const int K = slice_lo(ks + 1, p.n_up_n, p.splitk) * kBN - k_lo;
@@ -872,7 +877,7 @@ struct Stages {
     const int n0 = n * kBN * p.down_nb;
     const Elem* wd = reinterpret_cast<const Elem*>(p.wd) + (size_t)t.e * p.f * p.d +
                      (size_t)k_lo * p.d + n0;
-    if (p.comb_scatter) {
+    if (scat) {
       down_rows(t.rows, p.perm + t.row0, p.rw + t.row0, 0);   // read after the K loop's barriers
       down_any(t.bm, p.down_nb, A, p.f, t.rows, wd, p.d, K, p.y + n0, p.d, smem, true);
       return;
@@ -898,13 +903,13 @@ struct Stages {
     up_any(row_class(rows), A, p.d, rows, wg, wu, p.fs, p.d, H, p.fs, smem);
   }
 
-  static TASKFN void shared_down(const Params& p, int s, int m, int n, char* smem) {
+  static TASKFN void shared_down(const Params& p, int s, int m, int n, char* smem, bool scat) {
     const int r0 = m * p.th;
     const int rows = min(p.th, p.T - r0);
     const int n0 = n * kBN * p.down_nb;
     const Elem* A = reinterpret_cast<const Elem*>(p.Hs) + ((size_t)s * p.T + r0) * p.fs;
     const Elem* wd = reinterpret_cast<const Elem*>(p.sd) + (size_t)s * p.fs * p.d + n0;
-    if (p.comb_scatter) {
+    if (scat) {
       down_rows(rows, nullptr, nullptr, r0);
       down_any(row_class(rows), p.down_nb, A, p.fs, rows, wd, p.d, p.fs, p.y + n0, p.d, smem,
                true);
@@ -929,7 +934,7 @@ struct Stages {
     const int k = p.k;
     int* s_pos = reinterpret_cast<int*>(smem);               // [32 * k]
     float* s_w = reinterpret_cast<float*>(s_pos + kTB * kMaxK);
-    for (int i = threadIdx.x; i < rows * k; i += kThreads) {
+    for (int i = tidx(); i < rows * k; i += kThreads) {
       s_pos[i] = p.slot_pos[(size_t)t0 * k + i];
       s_w[i] = p.w[(size_t)t0 * k + i];
     }
@@ -940,7 +945,7 @@ struct Stages {
     const int n = rows * c4;
     // two (token, float4) items per thread per pass, every load of both
     // issued before any sum (a combine task is a latency-bound gather)
-    for (int i0 = threadIdx.x; i0 < n; i0 += 2 * kThreads) {
+    for (int i0 = tidx(); i0 < n; i0 += 2 * kThreads) {
       float4 v[2][kMaxK];
       float4 sh[2][4];
 #pragma unroll

@@ -36,7 +36,8 @@ def _stream(device) -> ctypes.c_void_p:
 def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model",
               split_k: int = 0, max_workers: int = 0, fixed_mem_workers: int = 0,
               flags: int = 0, trace: Optional[torch.Tensor] = None,
-              timeout_ms: int = 0, row_tile: int = 0, combine: str = "auto") -> Desc:
+              timeout_ms: int = 0, row_tile: int = 0, combine: str = "auto",
+              timeout_ticks: int = 0) -> Desc:
     d = Desc()
     d.T, d.d, d.E, d.k, d.f = shape.T, shape.d, shape.E, shape.k, shape.f
     d.e_begin, d.e_end = shape.e_begin, shape.local_end
@@ -56,6 +57,7 @@ def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model
     d.timeout_ms = timeout_ms
     d.row_tile = row_tile
     d.combine = _abi.COMBINES[combine]
+    d.timeout_ticks = timeout_ticks
     return d
 
 
@@ -122,14 +124,14 @@ class MoELayer:
                  max_workers: int = 0, fixed_mem_workers: int = 0, flags: int = 0,
                  trace: Optional[torch.Tensor] = None, timeout_ms: int = 0,
                  workspace: Optional[torch.Tensor] = None, row_tile: int = 0,
-                 combine: str = "auto"):
+                 combine: str = "auto", timeout_ticks: int = 0):
         self.shape = shape
         dev = weights["w_gate"].device
         if dev.type != "cuda":
             raise ValueError("weights must be on a GPU")
         self.device = dev
         self.desc = make_desc(shape, mode, split, split_k, max_workers, fixed_mem_workers,
-                              flags, trace, timeout_ms, row_tile, combine)
+                              flags, trace, timeout_ms, row_tile, combine, timeout_ticks)
         self._trace = trace
         et = _elem_dtype(shape)
         d, E, f, El = shape.d, shape.E, shape.f, shape.E_loc
@@ -182,6 +184,14 @@ class MoELayer:
         if routing is not None:
             return y, routing
         return y
+
+    def last_schedule(self) -> Dict[str, int]:
+        """The scheduler's decisions in the last call (synchronises)."""
+        out = _abi.Schedule()
+        with torch.cuda.device(self.device):
+            check(lib().moe_last_schedule(ctypes.byref(self.desc), _ptr(self.workspace),
+                                          _stream(self.device), ctypes.byref(out)))
+        return {name: getattr(out, name) for name, _ in _abi.Schedule._fields_}
 
     def device_error(self) -> int:
         with torch.cuda.device(self.device):

@@ -129,6 +129,10 @@ typedef struct moe_desc {
   int row_tile;       /* expert row-tile height 128 or 256 (bf16 only);
                          0 = automatic (256 when T*k > 8192 in bf16)        */
   int combine;        /* moe_combine                                        */
+  int timeout_ticks;  /* > 0: watchdog limit per wait in ticks of the 100 MHz
+                         device clock, overriding timeout_ms (lets a test
+                         force the watchdog; every wait then gives up and the
+                         call reports MOE_ERR_TIMEOUT)                      */
 } moe_desc;
 
 /* Weights.  E_loc = e_end - e_begin.  Element type = desc.dtype.
@@ -186,6 +190,10 @@ typedef struct moe_info {
   int row_tile;         /* expert row-tile height (128 or 256)             */
   int combine;          /* MOE_COMBINE_SCATTER or MOE_COMBINE_TASKS        */
   size_t workspace_bytes;
+  /* the cost model's frozen constants (measured once on MI355X) */
+  float cost_mfma_flops_per_cu;      /* sustained MFMA flop/s of one CU in expert tiles */
+  float cost_gather_bytes_per_worker; /* bytes/s one worker moves in a gather task */
+  float cost_hbm_bytes;              /* device bytes/s a streaming tile sustains */
 } moe_info;
 
 /* Bytes of workspace a call with this descriptor needs (0 on bad desc). */
@@ -214,6 +222,23 @@ int moe_route_from_logits(const moe_desc* desc, const float* logits,
  * call that used `workspace` (MOE_OK if none). */
 int moe_last_device_error(const moe_desc* desc, const void* workspace,
                           void* hip_stream);
+
+/* What the scheduler decided in the last call that used a workspace: the
+ * memory-bound worker group the post-routing cost model sized (the spatial
+ * scheduler of the Weave abstract, arxivdaily.com/papers/2609.21483), and the
+ * task counts the builder made from the per-expert counts. */
+typedef struct moe_schedule {
+  int mem_workers;    /* workers that start on the permute queue (0: no split) */
+  int row_tiles;      /* expert row tiles                                   */
+  int permute_tasks;  /* gather tasks                                       */
+  int error;          /* device error word (MOE_OK if none)                 */
+} moe_schedule;
+
+/* Synchronise `hip_stream` and fill `out` from the control block of the last
+ * call that used `workspace`.  Returns MOE_ERR_ARG on a bad descriptor or a
+ * NULL pointer, MOE_ERR_HIP if a copy fails. */
+int moe_last_schedule(const moe_desc* desc, const void* workspace, void* hip_stream,
+                      moe_schedule* out);
 
 /* Human-readable text for a return code. */
 const char* moe_strerror(int code);

@@ -76,6 +76,13 @@ def logits_bound(n, shape):
     return 1e-5 * math.sqrt(shape.d) * mx(x) * mx(wr) + 1e-6
 
 
+def check_logits(lg, n, shape):
+    lo = oracle.logits(n["x"], n["w_router"], n["router_bias"])
+    err = float(np.max(np.abs(lo.astype(np.float64) - lg))) if lg.size else 0.0
+    assert err <= logits_bound(n, shape), "logits differ by %g" % err
+    return err
+
+
 def run_and_check(shape, g, n=None, mode="dynamic", split="cost_model", sample=None,
                   split_k=0, max_workers=0, label="", row_tile=0, combine="auto", flags=0):
     """Run one layer on the GPU and check it against the oracle.
@@ -93,10 +100,10 @@ def run_and_check(shape, g, n=None, mode="dynamic", split="cost_model", sample=N
     if n is None:
         n = host_inputs(g)
     lg = r.logits.cpu().numpy()
-    # the GPU logits agree with the oracle's within fp32 reassociation
-    if shape.T <= 2048:
-        lo = oracle.logits(n["x"], n["w_router"], n["router_bias"])
-        assert np.max(np.abs(lo - lg)) <= logits_bound(n, shape), "logits differ"
+    # the GPU logits agree with the oracle's within fp32 reassociation, at
+    # every size (a wrong router GEMM must not pass as a self-consistent
+    # routing of wrong logits)
+    check_logits(lg, n, shape)
     ro = oracle.route(lg, shape.k, shape.e_begin, shape.local_end)
     check_routing(r, ro, shape)
     shared = None
@@ -117,3 +124,37 @@ def run_and_check(shape, g, n=None, mode="dynamic", split="cost_model", sample=N
     log("       ok: max|err|/max|y|=%.2e rel-L2=%.2e R=%d (%.1fs)" % (err, rel, ro["R"],
                                                                      time.time() - t0))
     return y, r, ro
+
+
+def check_full_layer(shape, g, n, modes, label=""):
+    """Full-size check of one layer in several modes against ONE oracle run:
+    every token's y, the logits against the oracle's, routing bit-exact; the
+    other modes' logits must equal the first mode's bit for bit (same router
+    code), so the same oracle routing and y apply to all of them."""
+    t0 = time.time()
+    first = None
+    y_o = ro = None
+    for mode, split in modes:
+        log("[full] %s mode=%s split=%s T=%d d=%d E=%d k=%d f=%d local=[%d,%d) shared=%d" % (
+            label, mode, split, shape.T, shape.d, shape.E, shape.k, shape.f, shape.e_begin,
+            shape.local_end, shape.n_shared))
+        layer = MoELayer(shape, g, mode=mode, split=split, timeout_ms=3000)
+        y, r = layer(g["x"], return_routing=True, check_errors=True)
+        torch.cuda.synchronize()
+        lg = r.logits.cpu().numpy()
+        if first is None:
+            err_l = check_logits(lg, n, shape)
+            ro = oracle.route(lg, shape.k, shape.e_begin, shape.local_end)
+            shared = (n["ws_gate"], n["ws_up"], n["ws_down"]) if shape.n_shared else None
+            t1 = time.time()
+            y_o = oracle.moe_layer(n["x"], n["w_gate"], n["w_up"], n["w_down"], ro,
+                                   shape.e_begin, shared)
+            log("       oracle: R=%d, logits max|err| %.2e, %.1fs" % (ro["R"], err_l, time.time() - t1))
+            first = lg
+        else:
+            assert np.array_equal(lg.view(np.uint32), first.view(np.uint32)), "logits differ across modes"
+        check_routing(r, ro, shape)
+        err, rel = compare_y(y.cpu().numpy(), y_o, shape.dtype)
+        log("       ok: max|err|/max|y|=%.2e rel-L2=%.2e (%.1fs)" % (err, rel, time.time() - t0))
+        del layer, y, r
+    return y_o, ro

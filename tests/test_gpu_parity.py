@@ -190,6 +190,18 @@ def test_nonfinite_logit_reported():
     route_from_logits(s, torch.randn((s.T, s.E)).cuda(), check_errors=True)
 
 
+def test_router_256_wide_k_sliced():
+    """The widest router (E = 256: two 128-column blocks of the router GEMM)
+    with K slices reduced in a fixed order, logits compared with the
+    oracle's, on a local expert range."""
+    s = LayerShape(T=200, d=1024, E=256, k=8, f=256, e_begin=64, e_end=192, zipf_s=1.2)
+    g = gen_inputs(s, "router256", 12)
+    layer = MoELayer(s, g)
+    assert layer.info["route_splits"] > 1
+    for mode, split in (("dynamic", "cost_model"), ("static", "fixed"), ("multi_kernel", "none")):
+        run_and_check(s, g, None, mode, split, label="router256")
+
+
 def test_split_k_uneven():
     s = LayerShape(T=96, d=256, E=4, k=2, f=1024, zipf_s=0.5)
     g = gen_inputs(s, "splitk", 3)
@@ -344,6 +356,67 @@ def gen_and_host(shape, tag, seed):
     return g, host_inputs(g)
 
 
+@pytest.mark.parametrize("mode,split", [("dynamic", "cost_model"), ("static", "fixed")])
+def test_watchdog_timeout_then_recovery(mid, mode, split):
+    """A watchdog limit of two clock ticks (20 ns): the kernel's own bounded
+    waits give up, every workgroup exits, the call reports MOE_ERR_TIMEOUT;
+    the next call on the same workspace with the normal limit matches the
+    oracle."""
+    from dynamic_task_scheduling_amd._abi import MoEError
+    g, n = mid
+    bad = MoELayer(MID, g, mode=mode, split=split, timeout_ticks=2, combine="tasks")
+    with pytest.raises(MoEError) as ei:
+        bad(g["x"], check_errors=True)
+    assert ei.value.code == 5
+    torch.cuda.synchronize()
+    good = MoELayer(MID, g, mode=mode, split=split, workspace=bad.workspace, combine="tasks")
+    y, r = good(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    ro = oracle.route(r.logits.cpu().numpy(), MID.k)
+    check_routing(r, ro, MID)
+    yo = oracle.moe_layer(n["x"], n["w_gate"], n["w_up"], n["w_down"], ro, 0,
+                          (n["ws_gate"], n["ws_up"], n["ws_down"]))
+    compare_y(y.cpu().numpy(), yo, "bf16")
+
+
+@pytest.mark.parametrize("mode", ["dynamic", "static", "multi_kernel"])
+def test_graph_capture_replay_new_inputs(mid, mode):
+    """moe_layer captured once in a HIP graph (fixed addresses: x, y, the
+    routing tables and the workspace), then replayed with new x contents
+    written into the same buffer; every replay matches the oracle, with
+    eager calls of the same layer between the replays."""
+    g, n = mid
+    from dynamic_task_scheduling_amd.moe import alloc_routing
+    split = {"dynamic": "cost_model", "static": "fixed", "multi_kernel": "none"}[mode]
+    layer = MoELayer(MID, g, mode=mode, split=split, timeout_ms=3000, combine="tasks")
+    x = g["x"].clone()
+    y = torch.empty((MID.T, MID.d), dtype=torch.float32, device="cuda")
+    rt = alloc_routing(MID, torch.device("cuda"))
+    layer(x, y, rt)                      # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer(x, y, rt)
+    torch.cuda.synchronize()
+    shared = (n["ws_gate"], n["ws_up"], n["ws_down"])
+    for seed in (31, 32, 33):
+        xs = torch.randn((MID.T, MID.d), generator=torch.Generator().manual_seed(seed))
+        x.copy_(xs.to(torch.bfloat16).cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert layer.device_error() == 0
+        nx = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        ro = oracle.route(rt.logits.cpu().numpy(), MID.k)
+        check_routing(rt, ro, MID)
+        yo = oracle.moe_layer(nx, n["w_gate"], n["w_up"], n["w_down"], ro, 0, shared)
+        compare_y(y.cpu().numpy(), yo, "bf16")
+        # an eager call in between (different output buffer), same result
+        y_e = layer(x, check_errors=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y_e, y)
+
+
 def test_trace_happens_before(mid):
     """Every task runs exactly once and starts after its producers ended."""
     from analysis_util import check_trace
@@ -356,30 +429,40 @@ def test_trace_happens_before(mid):
 
 
 # ------------------------------------------------------------ full sizes
-def _full(cfg, sample, modes=(("dynamic", "cost_model"),), layers=(0,)):
+# Every token of every full-size workload, in all three scheduling modes,
+# against one oracle run per layer (the oracle is a plain fp64 CPU loop:
+# tens of seconds on the largest layer, hence the per-test time limits).
+FULL_MODES = (("dynamic", "cost_model"), ("static", "fixed"), ("multi_kernel", "none"))
+
+
+def _full(cfg, layers=None):
+    from gpu_util import check_full_layer
+    from dynamic_task_scheduling_amd.synth import make_layer
     wl = workload(cfg)
-    for li in layers:
+    for li in (range(len(wl.layers)) if layers is None else layers):
         s = wl.layers[li]
-        from dynamic_task_scheduling_amd.synth import make_layer
         t = make_layer(s, wl.name, li, 0, "cuda")
         n = host_inputs(t)
-        for mode, split in modes:
-            run_and_check(s, t, n, mode, split, sample=sample, label="%s[%d]" % (wl.name, li))
-        del t
+        check_full_layer(s, t, n, FULL_MODES, label="%s[%d]" % (wl.name, li))
+        del t, n
         torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
 def test_full_decode():
-    _full(2, 12, modes=(("dynamic", "cost_model"), ("static", "fixed"), ("multi_kernel", "none")))
+    _full(2)
 
 
+@pytest.mark.timeout(900)
 def test_full_prefill():
-    _full(3, 12, modes=(("dynamic", "cost_model"), ("static", "fixed"), ("multi_kernel", "none")))
+    _full(3)
 
 
+@pytest.mark.timeout(1200)
 def test_full_ep_share():
-    _full(4, 8)
+    _full(4)
 
 
+@pytest.mark.timeout(900)
 def test_full_stress_layers():
-    _full(5, 8, layers=(0, 1, 15))
+    _full(5)
