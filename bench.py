@@ -288,7 +288,8 @@ def main():
                     help="weighted combine: scatter-add in the DOWN epilogue, or combine tasks")
     ap.add_argument("--profile-only", action="store_true",
                     help="time only the dynamic mode (for rocprofv3 runs)")
-    ap.add_argument("--mode", default="dynamic", help="mode timed by --profile-only")
+    ap.add_argument("--mode", default="dynamic",
+                    help="modes timed by --profile-only, comma-separated, in order")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -309,10 +310,12 @@ def main():
     wl = run.wl
 
     if args.profile_only:
-        L = run.layers(args.mode, args.split if args.mode == "dynamic" else MODE_SPLIT[args.mode])
-        r = run.timed(L, args.steps, args.warmup)
-        print(json.dumps({"profile_only": True, "workload": wl.name, "mode": args.mode,
-                          "ms": r}), flush=True)
+        res = {}
+        for mode in args.mode.split(","):
+            L = run.layers(mode, args.split if mode == "dynamic" else MODE_SPLIT[mode])
+            res[mode] = run.timed(L, args.steps, args.warmup)
+            del L
+        print(json.dumps({"profile_only": True, "workload": wl.name, "ms": res}), flush=True)
         return
 
     modes = ("dynamic",) if args.no_baselines else ("dynamic", "static", "multi_kernel")

@@ -62,6 +62,8 @@ def _load():
         lib.oracle_moe_layer.argtypes = [ci] * 9 + [vp, ci] + [vp] * 6 + [
             ci, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_moe_layer.restype = None
+        lib.oracle_residual_rmsnorm.argtypes = [ci, ci, vp, vp, vp, ctypes.c_double, vp, vp]
+        lib.oracle_residual_rmsnorm.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ci
         _lib = lib
@@ -186,6 +188,21 @@ def moe_layer(x, wg, wu, wd, routing: dict, e_begin: int = 0,
                          _ptr(_arr(routing["slot_pos"], np.int32)), _ptr(O),
                          _ptr(y))
     return y
+
+
+def residual_rmsnorm(y, residual, gamma, eps: float):
+    """h = residual + y and hn = RMSNorm(h) * gamma, both float64 [T,d]
+    (the layer tail: residual add, then the next block's RMSNorm)."""
+    lib = _load()
+    y = _arr(y, np.float64)
+    T, d = y.shape
+    res = None if residual is None else _arr(residual, np.float32)
+    g = _arr(gamma, np.float32)
+    assert g.shape == (d,) and (res is None or res.shape == (T, d))
+    h = np.empty((T, d), np.float64)
+    hn = np.empty((T, d), np.float64)
+    lib.oracle_residual_rmsnorm(T, d, _ptr(y), _ptr(res), _ptr(g), float(eps), _ptr(h), _ptr(hn))
+    return h, hn
 
 
 def full(x, wr, bias, wg, wu, wd, k: int, e_begin: int = 0, e_end=None,

@@ -285,6 +285,33 @@ void oracle_moe_layer(int T, int d, int E, int k, int f, int e_begin,
   free(Xp);
 }
 
+/* Residual add and RMSNorm of the layer output -- the "residual and
+ * normalisation" stages the blog walk-through keeps inside the big MoE kernel
+ * (xxqk.cn/news/665650 section 1).  No page writes the formula; this is the
+ * standard RMSNorm of the pre-norm transformer block, applied to the block
+ * output so it is the next block's normalised input:
+ *   h[t,c]  = residual[t,c] + y[t,c]
+ *   ms[t]   = (1/d) sum_{c ascending} h[t,c]^2
+ *   hn[t,c] = h[t,c] / sqrt(ms[t] + eps) * gamma[c]
+ * Arithmetic in fp64.  residual [T,d] fp32 (NULL = zero), gamma [d] fp32,
+ * y, h, hn [T,d] double. */
+void oracle_residual_rmsnorm(int T, int d, const double* y, const float* residual,
+                             const float* gamma, double eps, double* h,
+                             double* hn) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    const double* yr = y + (size_t)t * d;
+    double* hr = h + (size_t)t * d;
+    double ss = 0.0;
+    for (int c = 0; c < d; ++c) {
+      hr[c] = (residual ? (double)residual[(size_t)t * d + c] : 0.0) + yr[c];
+      ss += hr[c] * hr[c];
+    }
+    const double r = 1.0 / sqrt(ss / (double)d + eps);
+    for (int c = 0; c < d; ++c) hn[(size_t)t * d + c] = hr[c] * r * (double)gamma[c];
+  }
+}
+
 /* Threads the OpenMP runtime will use (for reporting). */
 int oracle_num_threads(void) {
   int n = 1;

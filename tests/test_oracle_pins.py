@@ -237,3 +237,53 @@ def test_tiny_config_runs_fast(oracle_mod):
                                 n["w_up"], n["w_down"], s.k, logits32=lg)
     assert np.array_equal(r["idx"], idx_b)
     assert np.max(np.abs(y - yb)) <= 1e-10 * np.max(np.abs(yb))
+
+
+# ------------------------------------------------ residual add + RMSNorm tail
+def _norm_case(rng, T=37, d=96):
+    y = rng.standard_normal((T, d))
+    res = rng.standard_normal((T, d)).astype(np.float32)
+    gamma = (1.0 + 0.5 * rng.standard_normal(d)).astype(np.float32)
+    return y, res, gamma
+
+
+def test_rmsnorm_zero_residual_is_identity(oracle_mod):
+    """residual = 0 (or absent) leaves the layer output unchanged."""
+    rng = np.random.default_rng(21)
+    y, res, gamma = _norm_case(rng)
+    h0, _ = oracle_mod.residual_rmsnorm(y, np.zeros_like(res), gamma, 1e-6)
+    h1, hn1 = oracle_mod.residual_rmsnorm(y, None, gamma, 1e-6)
+    assert np.array_equal(h0, y) and np.array_equal(h1, y)
+    # the residual enters once, added: h - y = residual up to one rounding
+    h, _ = oracle_mod.residual_rmsnorm(y, res, gamma, 1e-6)
+    assert np.allclose(h - y, res.astype(np.float64), rtol=0, atol=1e-14)
+
+
+def test_rmsnorm_matches_library(oracle_mod):
+    """Against torch's own RMSNorm (an independent implementation)."""
+    rng = np.random.default_rng(22)
+    for eps in (1e-6, 1e-2):
+        y, res, gamma = _norm_case(rng)
+        h, hn = oracle_mod.residual_rmsnorm(y, res, gamma, eps)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(h), (h.shape[1],),
+                                           torch.from_numpy(gamma.astype(np.float64)), eps)
+        assert np.allclose(hn, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_rmsnorm_closed_forms(oracle_mod):
+    """eps = 0, gamma = 1: every output row has mean square exactly 1 (up to
+    rounding), a positive rescaling of the row changes nothing, and a constant
+    row c*1 maps to sign(c)*1.  eps > 0: a zero row stays zero (no NaN)."""
+    rng = np.random.default_rng(23)
+    y, res, gamma = _norm_case(rng)
+    ones = np.ones(y.shape[1], np.float32)
+    _, hn = oracle_mod.residual_rmsnorm(y, None, ones, 0.0)
+    assert np.allclose((hn ** 2).mean(axis=1), 1.0, rtol=0, atol=1e-12)
+    _, hn3 = oracle_mod.residual_rmsnorm(3.5 * y, None, ones, 0.0)
+    assert np.allclose(hn3, hn, rtol=1e-13, atol=1e-13)
+    const = np.array([[2.0] * 8, [-0.25] * 8])
+    _, hc = oracle_mod.residual_rmsnorm(const, None, gamma[:8], 0.0)
+    assert np.allclose(hc[0], gamma[:8], rtol=1e-15, atol=0)
+    assert np.allclose(hc[1], -gamma[:8].astype(np.float64), rtol=1e-15, atol=0)
+    _, hz = oracle_mod.residual_rmsnorm(np.zeros((2, 8)), None, gamma[:8], 1e-6)
+    assert np.all(hz == 0.0)
