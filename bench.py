@@ -117,7 +117,7 @@ def calibrate_copy(mib: int) -> None:
 class Runner:
     """Layers of one workload on the GPU, and the timing of a scheduling mode."""
 
-    def __init__(self, cfg, dev, combine="auto"):
+    def __init__(self, cfg, dev, combine="auto", bands=0):
         import torch
         from dynamic_task_scheduling_amd import configs
         from dynamic_task_scheduling_amd.synth import make_layer
@@ -127,11 +127,14 @@ class Runner:
         self.tensors = [make_layer(s, self.wl.name, li, 0, dev) for li, s in enumerate(self.wl.layers)]
         self.ys = [torch.empty((s.T, s.d), dtype=torch.float32, device=dev) for s in self.wl.layers]
         self.combine = combine
+        self.bands = bands
         torch.cuda.synchronize()
 
-    def layers(self, mode, split, flags=0, trace=None):
+    def layers(self, mode, split, flags=0, trace=None, bands=None):
         from dynamic_task_scheduling_amd.moe import MoELayer
-        return [MoELayer(s, t, mode=mode, split=split, trace=trace, combine=self.combine, flags=flags)
+        b = self.bands if bands is None else bands
+        return [MoELayer(s, t, mode=mode, split=split, trace=trace, combine=self.combine, flags=flags,
+                         bands=b)
                 for s, t in zip(self.wl.layers, self.tensors)]
 
     def step(self, layers):
@@ -239,18 +242,21 @@ def ablations(run, steps, warmup):
     synchronisation (grid barriers vs per-task counter waits)."""
     from dynamic_task_scheduling_amd import _abi
     variants = [
-        ("dynamic/split=cost_model", "dynamic", "cost_model", 0),
-        ("dynamic/split=fixed", "dynamic", "fixed", 0),
-        ("dynamic/split=none", "dynamic", "none", 0),
-        ("dynamic/steal=0", "dynamic", "cost_model", _abi.FLAG_NO_STEAL),
-        ("dynamic/xcd_affinity", "dynamic", "cost_model", _abi.FLAG_XCD_AFFINITY),
-        ("static/sync=phase_barrier", "static", "fixed", 0),
-        ("static/sync=ref_count", "static", "fixed", _abi.FLAG_REF_SYNC),
-        ("multi_kernel", "multi_kernel", "none", 0),
+        ("dynamic/split=cost_model", "dynamic", "cost_model", 0, None),
+        ("dynamic/split=fixed", "dynamic", "fixed", 0, None),
+        ("dynamic/split=none", "dynamic", "none", 0, None),
+        ("dynamic/steal=0", "dynamic", "cost_model", _abi.FLAG_NO_STEAL, None),
+        ("dynamic/xcd_affinity", "dynamic", "cost_model", _abi.FLAG_XCD_AFFINITY, None),
+        ("dynamic/bands=1", "dynamic", "cost_model", 0, 1),
+        ("dynamic/bands=2", "dynamic", "cost_model", 0, 2),
+        ("dynamic/bands=4", "dynamic", "cost_model", 0, 4),
+        ("static/sync=phase_barrier", "static", "fixed", 0, None),
+        ("static/sync=ref_count", "static", "fixed", _abi.FLAG_REF_SYNC, None),
+        ("multi_kernel", "multi_kernel", "none", 0, None),
     ]
     out = {}
-    for name, mode, split, fl in variants:
-        L = run.layers(mode, split, flags=fl)
+    for name, mode, split, fl, bands in variants:
+        L = run.layers(mode, split, flags=fl, bands=bands)
         run.timed(L, 1, warmup)
         out[name] = round(run.timed(L, steps, warmup)["mean"], 4)
         if mode == "dynamic":
@@ -284,6 +290,8 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-ablations", action="store_true")
     ap.add_argument("--split", default="cost_model")
+    ap.add_argument("--bands", type=int, default=0,
+                    help="token bands of the row-tile order (0: automatic)")
     ap.add_argument("--combine", default="auto", choices=["auto", "scatter", "tasks"],
                     help="weighted combine: scatter-add in the DOWN epilogue, or combine tasks")
     ap.add_argument("--profile-only", action="store_true",
@@ -306,7 +314,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    run = Runner(args.config, dev, args.combine)
+    run = Runner(args.config, dev, args.combine, args.bands)
     wl = run.wl
 
     if args.profile_only:

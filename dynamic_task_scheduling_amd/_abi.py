@@ -21,8 +21,8 @@ ERRORS = {
 }
 
 # Every function the header declares (checked by the CPU tests).
-EXPORTS = ["moe_workspace_size", "moe_query", "moe_layer", "moe_route_from_logits",
-           "moe_last_device_error", "moe_last_schedule", "moe_strerror"]
+EXPORTS = ["moe_workspace_size", "moe_query", "moe_layer", "moe_layer_norm",
+           "moe_route_from_logits", "moe_last_device_error", "moe_last_schedule", "moe_strerror"]
 
 
 class Desc(ctypes.Structure):
@@ -32,7 +32,7 @@ class Desc(ctypes.Structure):
         ("dtype", c_int), ("mode", c_int), ("split_policy", c_int),
         ("fixed_mem_workers", c_int), ("split_k", c_int), ("max_workers", c_int),
         ("flags", c_uint), ("trace", c_void_p), ("trace_cap", c_int), ("timeout_ms", c_int),
-        ("row_tile", c_int), ("combine", c_int), ("timeout_ticks", c_int),
+        ("row_tile", c_int), ("combine", c_int), ("bands", c_int), ("timeout_ticks", c_int),
     ]
 
 
@@ -55,7 +55,7 @@ class Info(ctypes.Structure):
                 ("workspace_bytes", c_size_t),
                 ("cost_mfma_flops_per_cu", ctypes.c_float),
                 ("cost_gather_bytes_per_worker", ctypes.c_float),
-                ("cost_hbm_bytes", ctypes.c_float)]
+                ("cost_hbm_bytes", ctypes.c_float), ("bands", c_int)]
 
 
 class Schedule(ctypes.Structure):
@@ -89,6 +89,10 @@ def lib():
         L.moe_layer.argtypes = [P(Desc), c_void_p, P(Weights), c_void_p, P(Routing),
                                 c_void_p, c_size_t, c_void_p]
         L.moe_layer.restype = c_int
+        L.moe_layer_norm.argtypes = [P(Desc), c_void_p, P(Weights), c_void_p, c_void_p,
+                                     ctypes.c_float, c_void_p, c_void_p, P(Routing), c_void_p,
+                                     c_size_t, c_void_p]
+        L.moe_layer_norm.restype = c_int
         L.moe_route_from_logits.argtypes = [P(Desc), c_void_p, P(Routing), c_void_p,
                                             c_size_t, c_void_p]
         L.moe_route_from_logits.restype = c_int

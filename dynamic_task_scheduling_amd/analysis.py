@@ -11,7 +11,7 @@ import numpy as np
 
 KIND_SHIFT = 27
 KINDS = {1: "ROUTE", 2: "POS", 3: "PERM", 4: "UP", 5: "DOWN", 6: "SUP", 7: "SDOWN",
-         8: "PHASE", 9: "COMB"}   # PHASE: scheduler phases (builder steps, router reduction)
+         8: "PHASE", 9: "COMB", 10: "NORM"}   # PHASE: scheduler phases (builder steps, router reduction)
 CLOCK_HZ = 100e6   # s_memrealtime rate
 
 
@@ -107,15 +107,21 @@ def by_kind(tr: Dict[str, np.ndarray]) -> Dict[str, Dict[str, float]]:
     return out
 
 
-def row_tiles(counts, th: int):
-    """Expert row tiles in the builder's order -- experts by descending count,
-    ties to the lower index, each expert's tiles consecutive: (expert, rows)."""
+def row_tiles(counts, th: int, bands: int = 4):
+    """Expert row tiles in the builder's order: token bands in order (tile m
+    of an expert with nt tiles in band b when ceil(nt b / bands) <= m <
+    ceil(nt (b + 1) / bands)), inside a band experts by descending count
+    (ties to the lower index), an expert's tiles consecutive.  Returns
+    (expert, rows, m) per tile."""
     order = sorted(range(len(counts)), key=lambda e: (-int(counts[e]), e))
+    lo = lambda n, b: (n * b + bands - 1) // bands
     tiles = []
-    for e in order:
-        c = int(counts[e])
-        for m in range((c + th - 1) // th):
-            tiles.append((e, min(th, c - th * m)))
+    for b in range(bands):
+        for e in order:
+            c = int(counts[e])
+            n = (c + th - 1) // th
+            for m in range(lo(n, b), lo(n, b + 1)):
+                tiles.append((e, min(th, c - th * m), m))
     return tiles
 
 
@@ -129,7 +135,7 @@ def calibrate(tr: Dict[str, np.ndarray], info: Dict[str, float], shape, counts) 
     pr = info["permute_rows"]
     pch = th // pr
     n_up, n_down, sk = info["up_ntiles"], info["down_ntiles"], info["split_k"]
-    tiles = row_tiles(counts, th)
+    tiles = row_tiles(counts, th, info.get("bands", 4))
     dur = (tr["t_end"] - tr["t_start"]) / CLOCK_HZ
     g_rates, up_rates, down_rates = [], [], []
     for k, p, t in zip(tr["kind"], tr["payload"], dur):

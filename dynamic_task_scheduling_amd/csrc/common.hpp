@@ -84,6 +84,18 @@ DEV void st_wt16(void* base, uint32_t byte_off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(d, r, byte_off, 0, 16 /* sc1 */);
 }
 
+// 16 bytes read coherently with device-scope atomics from every XCD (four
+// agent-scope relaxed atomic loads): for data other workgroups may have
+// updated with atomics after this XCD's L2 could have cached a line of it.
+DEV float4 ld_coherent4(const float* p) {
+  float4 v;
+  v.x = __hip_atomic_load(p + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.y = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.z = __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.w = __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
 DEV int ld_relaxed(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

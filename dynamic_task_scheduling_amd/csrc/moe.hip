@@ -53,6 +53,8 @@ __global__ __launch_bounds__(kThreads) void k_reset(Params p) {
   // combine tiles: the shared DOWN tiles over their tokens, plus one unit
   // that the tile's POS task replaces by its routed DOWN tiles
   for (int i = gid; i < p.n_rt; i += stride) p.cnt_comb[i] = 1 + p.n_shared * p.n_down_n;
+  // a token tile's NORM task waits for its combine column chunks
+  for (int i = gid; i < p.n_rt; i += stride) p.cnt_norm[i] = p.n_cc;
   if (p.flags & MOE_FLAG_XCD_AFFINITY) {
     const size_t nu = (size_t)kXcds * p.q_cap;
     for (size_t i = gid; i < nu; i += stride) p.uslots[i] = 0;
@@ -73,7 +75,8 @@ struct Layout {
   int esz;
   size_t off_ctrl, off_slots, off_uslots, off_logits, off_idx, off_w, off_hist, off_rtb, off_counts,
       off_offsets, off_eorder, off_route_part, off_cnt_route, off_perm, off_rw, off_slotpos, off_mtiles, off_cnt_perm,
-      off_cnt_down, off_cnt_sdown, off_perm_list, off_mt_base, off_cnt_comb, off_xp, off_h, off_hs,
+      off_cnt_down, off_cnt_sdown, off_perm_list, off_cnt_comb, off_cnt_norm, off_xp,
+      off_h, off_hs,
       off_o, off_ys, total;
 };
 
@@ -100,6 +103,7 @@ int validate(const moe_desc* d) {
   if (d->row_tile != 0 && d->row_tile != 128 && d->row_tile != 256) return MOE_ERR_ARG;
   if (d->row_tile == 256 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->combine < MOE_COMBINE_AUTO || d->combine > MOE_COMBINE_TASKS) return MOE_ERR_ARG;
+  if (d->bands < 0 || d->bands > kMaxBands) return MOE_ERR_ARG;
   return MOE_OK;
 }
 
@@ -160,6 +164,9 @@ void make_layout(const moe_desc* d, Layout* L) {
     while (pr > 2 && (long long)pr * row_bytes > target) pr >>= 1;
   }
   p.perm_rows = pr;
+  // row-tile order: token bands (see the builder); 0 = automatic: one band
+  // (plain expert-major order, measured fastest on the expert-share layer)
+  p.bands = d->bands > 0 ? std::min(d->bands, kMaxBands) : 1;
   p.pch = p.th / pr;
   const long long R = (long long)d->T * d->k;
   p.max_mt = (int)(R / 128 + p.E_loc + 1);
@@ -217,8 +224,8 @@ void make_layout(const moe_desc* d, Layout* L) {
   L->off_cnt_down = take(sizeof(int) * (size_t)p.max_mt * p.splitk);
   L->off_cnt_sdown = take(sizeof(int) * (size_t)std::max(1, p.n_shared * p.n_smt));
   L->off_perm_list = take(sizeof(int) * p.max_perm);
-  L->off_mt_base = take(sizeof(int) * p.E_loc);
   L->off_cnt_comb = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
+  L->off_cnt_norm = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
   L->off_xp = take((size_t)L->esz * Tk * d->d);
   L->off_h = take((size_t)L->esz * Tk * d->f);
   L->off_hs = take((size_t)L->esz * d->n_shared * d->T * (d->n_shared ? d->f_shared : 0));
@@ -251,8 +258,8 @@ void carve(Layout* L, void* ws) {
   p.cnt_down = reinterpret_cast<int*>(b + L->off_cnt_down);
   p.cnt_sdown = reinterpret_cast<int*>(b + L->off_cnt_sdown);
   p.perm_list = reinterpret_cast<int*>(b + L->off_perm_list);
-  p.mt_base = reinterpret_cast<int*>(b + L->off_mt_base);
   p.cnt_comb = reinterpret_cast<int*>(b + L->off_cnt_comb);
+  p.cnt_norm = reinterpret_cast<int*>(b + L->off_cnt_norm);
   p.O = reinterpret_cast<float*>(b + L->off_o);
   p.Ys = reinterpret_cast<float*>(b + L->off_ys);
   p.Xp = b + L->off_xp;
@@ -388,6 +395,40 @@ int fill_params(const moe_desc* d, Layout* L, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+int run_layer(const moe_desc* d, const void* x, const moe_weights* w, const float* residual,
+              const float* norm_weight, float norm_eps, float* y, void* y_norm,
+              const moe_routing* routing, void* workspace, size_t ws_bytes, void* stream) {
+  Layout L;
+  int rc = fill_params(d, &L, workspace, ws_bytes);
+  if (rc) return rc;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !w || !y || !w->w_router || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_ARG;
+  if (d->n_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_ARG;
+  Params& p = L.p;
+  p.x = x;
+  p.wr = w->w_router;
+  p.bias = w->router_bias;
+  p.wg = w->w_gate;
+  p.wu = w->w_up;
+  p.wd = w->w_down;
+  p.sg = w->ws_gate;
+  p.su = w->ws_up;
+  p.sd = w->ws_down;
+  p.y = y;
+  p.resid = residual;
+  p.norm_w = norm_weight;
+  p.y_norm = y_norm;
+  p.norm_eps = norm_eps;
+  p.fuse_norm = y_norm != nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launch_layer(d, p, s);
+  if (rc) return rc;
+  rc = copy_routing(d, p, routing, s);
+  if (rc) return rc;
+  if (d->flags & MOE_FLAG_CHECK) return moe_last_device_error(d, workspace, stream);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,35 +465,23 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->cost_mfma_flops_per_cu = L.p.cm_mfma_rate;
   info->cost_gather_bytes_per_worker = L.p.cm_cu_bw;
   info->cost_hbm_bytes = L.p.cm_hbm_bw;
+  info->bands = L.p.bands;
   return MOE_OK;
 }
 
 int moe_layer(const moe_desc* d, const void* x, const moe_weights* w, float* y,
               const moe_routing* routing, void* workspace, size_t ws_bytes, void* stream) {
-  Layout L;
-  int rc = fill_params(d, &L, workspace, ws_bytes);
-  if (rc) return rc;
-  if (d->T == 0) return MOE_OK;
-  if (!x || !w || !y || !w->w_router || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_ARG;
-  if (d->n_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_ARG;
-  Params& p = L.p;
-  p.x = x;
-  p.wr = w->w_router;
-  p.bias = w->router_bias;
-  p.wg = w->w_gate;
-  p.wu = w->w_up;
-  p.wd = w->w_down;
-  p.sg = w->ws_gate;
-  p.su = w->ws_up;
-  p.sd = w->ws_down;
-  p.y = y;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = launch_layer(d, p, s);
-  if (rc) return rc;
-  rc = copy_routing(d, p, routing, s);
-  if (rc) return rc;
-  if (d->flags & MOE_FLAG_CHECK) return moe_last_device_error(d, workspace, stream);
-  return MOE_OK;
+  return run_layer(d, x, w, nullptr, nullptr, 0.f, y, nullptr, routing, workspace, ws_bytes,
+                   stream);
+}
+
+int moe_layer_norm(const moe_desc* d, const void* x, const moe_weights* w,
+                   const float* residual, const float* norm_weight, float norm_eps, float* y,
+                   void* y_norm, const moe_routing* routing, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  if (!norm_weight || !y_norm || !(norm_eps >= 0.f)) return MOE_ERR_ARG;
+  return run_layer(d, x, w, residual, norm_weight, norm_eps, y, y_norm, routing, workspace,
+                   ws_bytes, stream);
 }
 
 int moe_route_from_logits(const moe_desc* d, const float* logits, const moe_routing* routing,

@@ -16,6 +16,7 @@ enum TaskKind : int {
   TK_SDOWN = 7,  // payload (s * n_smt + m) * n_down_n + n: shared-expert DOWN -> Ys rows
   TK_BUILD = 8,  // (trace only) scheduler phases: payload = kPhase* id
   TK_COMB = 9,   // payload rt * n_cc + cc: y rows of tokens [32 rt, 32 rt + 32), column chunk cc
+  TK_NORM = 10,  // payload rt: RMSNorm of the (residual-added) y rows of tokens [32 rt, 32 rt + 32)
 };
 // Trace phase ids (payload of TK_BUILD records).
 constexpr int kPhaseBuild = 0;          // the whole post-routing builder
@@ -56,6 +57,7 @@ enum CtrlWord : int {
   CW_COUNT = 45
 };
 constexpr int kXcds = 8;   // MI355X: 8 XCDs, each with its own L2
+constexpr int kMaxBands = 4;  // token bands of the row-tile order
 constexpr int kCtrlStride = 32;
 
 struct MTile {
@@ -84,6 +86,7 @@ struct Params {
   int pch;         // permute chunks per row tile = th / perm_rows
   int max_mt;      // capacity of the row-tile table
   int max_perm;    // capacity of the permute list
+  int bands;       // token bands of the row-tile order (1..kMaxBands)
   int n_sup, n_sdown;
   int comb_scatter; // 1: DOWN tiles scatter-add w * (H Wd) into y (small layers);
                     // 0: DOWN tiles write O rows, combine tasks sum them
@@ -132,13 +135,19 @@ struct Params {
   int* cnt_down;   // [max_mt * splitk]
   int* cnt_sdown;  // [n_shared * n_smt]
   int* perm_list;  // [max_perm]
-  int* mt_base;    // [E_loc] first row tile of each local expert
   int* cnt_comb;   // [n_rt] DOWN / shared-DOWN tiles a combine tile still waits for
   void* Xp;        // [T*k][d]
   void* H;         // [T*k][f]
   void* Hs;        // [n_shared][T][fs]
   float* O;        // [splitk][T*k][d] fp32 DOWN output rows (per K slice)
   float* Ys;       // [n_shared][T][d] fp32 shared-expert DOWN output
+  // fused block tail (residual add + RMSNorm of the layer output)
+  const float* resid;    // [T][d] fp32 added to y, or null
+  const float* norm_w;   // [d] fp32 RMSNorm weight
+  void* y_norm;          // [T][d] Elem: RMSNorm(y) * norm_w
+  float norm_eps;
+  int fuse_norm;         // 1: NORM tasks follow the combine
+  int* cnt_norm;         // [n_rt] combine chunks a NORM task still waits for
   uint64_t* trace; // [trace_cap][4]
   int trace_cap;
   int route_from_logits;  // 1: logits are an input, y untouched

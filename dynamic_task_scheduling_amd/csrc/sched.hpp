@@ -229,44 +229,51 @@ DEV void trace_mark(const Params& p, int phase, int worker, uint64_t t0, uint64_
   trace_record(p, make_task(TK_BUILD, phase), worker, t0, t0, t1);
 }
 
-// One thread: push the combine tasks of token tile rt (all column chunks).
-DEV void push_combine(const Params& p, int rt) {
-  const int base = add_relaxed(cw(p, CW_TAIL + QC), p.n_cc);
-  if (base + p.n_cc > p.q_cap) {
+// One thread: token tile rt has all its expert rows: push the tasks that
+// follow -- its combine tasks (all column chunks), or, when the DOWN tiles
+// scatter-added into y themselves, its NORM task.
+DEV void push_tile_ready(const Params& p, int rt, bool scat) {
+  const int n = scat ? 1 : p.n_cc;
+  const int base = add_relaxed(cw(p, CW_TAIL + QC), n);
+  if (base + n > p.q_cap) {
     set_error(p, 6 /* MOE_ERR_CAPACITY */);
     return;
   }
   int* sl = p.slots + (size_t)QC * p.q_cap + base;
+  if (scat) {
+    st_relaxed(sl, make_task(TK_NORM, rt) + 1);
+    return;
+  }
   for (int c = 0; c < p.n_cc; ++c) st_relaxed(sl + c, make_task(TK_COMB, rt * p.n_cc + c) + 1);
 }
 
 // All threads, after a DOWN tile of rows [row0, row0 + rows): its results
 // are published, then each token tile those rows belong to loses one
 // pending tile; the arrival that empties a counter releases that tile's
-// combine tasks (dynamic mode).  An expert's rows are sorted by token, so
+// next tasks (dynamic mode).  An expert's rows are sorted by token, so
 // the tile's token tiles are the runs of perm[r] / 32.
-DEV void combine_arrive_rows(const Params& p, int row0, int rows, bool dyn) {
+DEV void combine_arrive_rows(const Params& p, int row0, int rows, bool dyn, bool scat) {
   publish_fence();
   __syncthreads();
   const int r = tidx();
   if (r < rows) {
     const int blk = p.perm[row0 + r] / kTB;
     const int prev = r > 0 ? p.perm[row0 + r - 1] / kTB : -1;
-    if (blk != prev && add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn) push_combine(p, blk);
+    if (blk != prev && add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn) push_tile_ready(p, blk, scat);
   }
   __syncthreads();
 }
 
 // Same for a shared-expert DOWN tile of the th tokens [th m, th m + th)
 // (th = 128 or 256: whole token tiles).
-DEV void combine_arrive_shared(const Params& p, int m, bool dyn) {
+DEV void combine_arrive_shared(const Params& p, int m, bool dyn, bool scat) {
   publish_fence();
   __syncthreads();
   const int per = p.th / kTB;
   const int blk = m * per + tidx();
   if (tidx() < per && blk < p.n_rt &&
       add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn)
-    push_combine(p, blk);
+    push_tile_ready(p, blk, scat);
   __syncthreads();
 }
 
@@ -281,7 +288,7 @@ struct Sched {
     const bool split = p.split_policy != 2;
     const int n_up_qc = affinity(p) ? 0 : n_mt * p.n_up_n;
     const int n_comp = n_up_qc + n_mt * p.n_down_n * p.splitk + p.n_sup + p.n_sdown +
-                       (SCAT ? 0 : p.n_rt * p.n_cc);
+                       (SCAT ? 0 : p.n_rt * p.n_cc) + (p.fuse_norm ? p.n_rt : 0);
     publish_fence();
     __syncthreads();
     if (tidx() == 0) {
@@ -348,15 +355,20 @@ struct Sched {
         // the combine of these tokens waits for the DOWN tiles of the nd row
         // tiles holding their rows; this replaces the counter's initial
         // "positions pending" unit (k_reset) by that many tiles
+        // (with scatter-add the counter only gates the NORM task)
         if (tidx() == 0) {
           const int delta = nd * p.n_down_n * p.splitk - 1;
-          s_tmp[0] = !SCAT && (add_relaxed(p.cnt_comb + pl, delta) + delta == 0);
+          s_tmp[0] = (!SCAT || p.fuse_norm) && (add_relaxed(p.cnt_comb + pl, delta) + delta == 0);
         }
         __syncthreads();
         const bool comb_ready = uniform(s_tmp[0]) != 0;
         __syncthreads();
-        if (comb_ready && dyn)
-          push_burst(p, QC, p.n_cc, s_tmp, [&](int c) { return make_task(TK_COMB, pl * p.n_cc + c); });
+        if (comb_ready && dyn) {
+          publish_fence();
+          __syncthreads();
+          if (tidx() == 0) push_tile_ready(p, pl, SCAT);
+          __syncthreads();
+        }
         if (arrive_last(cw(p, CW_POS_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
           const int n_perm = ld_relaxed(cw(p, CW_NPERM));
           const int q = (p.split_policy != 2) ? QM : QC;
@@ -405,9 +417,9 @@ struct Sched {
         const int mt = r / p.n_down_n;
         S::down(p, mt, r % p.n_down_n, ks, smem, SCAT);
         *t_body = rtc();
-        if (!SCAT) {
+        if (!SCAT || p.fuse_norm) {
           const MTile t = p.mtiles[mt];
-          combine_arrive_rows(p, t.row0, t.rows, dyn);
+          combine_arrive_rows(p, t.row0, t.rows, dyn, SCAT);
         }
         break;
       }
@@ -426,11 +438,19 @@ struct Sched {
         const int sm = pl / p.n_down_n;
         S::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem, SCAT);
         *t_body = rtc();
-        if (!SCAT) combine_arrive_shared(p, sm % p.n_smt, dyn);
+        if (!SCAT || p.fuse_norm) combine_arrive_shared(p, sm % p.n_smt, dyn, SCAT);
         break;
       }
       case TK_COMB: {
         S::combine(p, pl / p.n_cc, pl % p.n_cc, smem);
+        *t_body = rtc();
+        // the last column chunk of a token tile releases its NORM task
+        if (p.fuse_norm && arrive_last(p.cnt_norm + pl / p.n_cc, -1, 1, s_tmp) && dyn)
+          push_burst(p, QC, 1, s_tmp, [&](int) { return make_task(TK_NORM, pl / p.n_cc); });
+        break;
+      }
+      case TK_NORM: {
+        S::norm(p, pl, SCAT);
         *t_body = rtc();
         break;
       }
@@ -551,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
   const int wm = max(1, p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8);
   const int n_route = p.n_rt * p.rsk;
   const int nA = n_route + p.n_sup;
-  enum { ST_A, ST_BUILD, ST_POS, ST_PERM, ST_UP, ST_DOWN, ST_COMB };
+  enum { ST_A, ST_BUILD, ST_POS, ST_PERM, ST_UP, ST_DOWN, ST_COMB, ST_NORM };
   int st = ST_A, i = w, gen = 0;
   int n_mt = 0, n_perm = 0, n_up = 0, n_down = 0;
   for (;;) {
@@ -625,14 +645,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
           i += W;
           break;
         }
-        if (SCAT) return;
+        if (SCAT && !p.fuse_norm) return;
         if (!ref && !grid_barrier(p, gen, s_tmp)) return;
-        st = ST_COMB;
+        st = SCAT ? ST_NORM : ST_COMB;
         i = w;
-      } else {
+      } else if (st == ST_COMB) {
         if (i < p.n_rt * p.n_cc) {
           task = make_task(TK_COMB, i);
           if (ref) dep = p.cnt_comb + i / p.n_cc;
+          i += W;
+          break;
+        }
+        if (!p.fuse_norm) return;
+        if (!ref && !grid_barrier(p, gen, s_tmp)) return;
+        st = ST_NORM;
+        i = w;
+      } else {
+        // the block tail: after the combine chunks (or, with scatter-add,
+        // the DOWN tiles) of each token tile
+        if (i < p.n_rt) {
+          task = make_task(TK_NORM, i);
+          if (ref) dep = SCAT ? p.cnt_comb + i : p.cnt_norm + i;
           i += W;
           break;
         }
@@ -725,6 +758,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_stage_down(Params p) {
 }
 
 template <typename Elem>
+__global__ __launch_bounds__(kThreads) void k_stage_norm(Params p) {
+  Stages<Elem>::norm(p, blockIdx.x, p.comb_scatter != 0);
+}
+
+template <typename Elem>
 __global__ __launch_bounds__(kThreads) void k_stage_comb(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[kTB * kMaxK * 8];
   Stages<Elem>::combine(p, blockIdx.x / p.n_cc, blockIdx.x % p.n_cc, smem);
@@ -744,6 +782,8 @@ hipError_t launch_stage_sequence(const Params& p, hipStream_t s) {
                      dim3(kThreads), 0, s, p);
   if (!p.comb_scatter)
     hipLaunchKernelGGL(k_stage_comb<Elem>, dim3(p.n_rt * p.n_cc), dim3(kThreads), 0, s, p);
+  if (p.fuse_norm)
+    hipLaunchKernelGGL(k_stage_norm<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

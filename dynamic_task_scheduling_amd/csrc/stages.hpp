@@ -277,11 +277,14 @@ struct Stages {
     const float bias_v = (p.rsk == 1 && p.bias && tidx() < p.E) ? p.bias[tidx()] : 0.f;
     // scatter-add combine: this slice zeroes its share of the tile's y rows
     // (rows ks, ks + rsk, ...), which the DOWN tiles then accumulate into
+    // (with a fused residual the rows start from the residual instead)
     if (scat) {
       for (int r = ks; r < rows; r += p.rsk) {
         float* yr = p.y + (size_t)(t0 + r) * p.d;
+        const uint4* rr = p.resid ? reinterpret_cast<const uint4*>(p.resid + (size_t)(t0 + r) * p.d)
+                                  : nullptr;
         for (int i = tidx(); i < p.d / 4; i += kThreads)
-          st_wt16(yr, i * 16, make_uint4(0, 0, 0, 0));
+          st_wt16(yr, i * 16, rr ? rr[i] : make_uint4(0, 0, 0, 0));
       }
     }
     const int Ks = p.d / p.rsk;
@@ -423,9 +426,9 @@ struct Stages {
     int* s_cnt = reinterpret_cast<int*>(smem);            // [256] count of expert e
     int* s_off = s_cnt + 256;                             // [257] offset of expert e
     int* s_ord = s_off + 257;                             // [256] expert of rank r
-    int* s_mtb = s_ord + 256;                             // [257] tile base of rank r
-    int* s_pb = s_mtb + 257;                              // [257] permute base of rank r
-    int* s_w = s_pb + 257;                                // [8] scan / reduction scratch
+    int* s_bt = s_ord + 256;                    // [kMaxBands][257] tile base of (band, rank)
+    int* s_bp = s_bt + kMaxBands * 257;         // [kMaxBands][257] permute base of (band, rank)
+    int* s_w = s_bp + kMaxBands * 257;          // [8] scan / reduction scratch
     float* s_wf = reinterpret_cast<float*>(s_w + 4);
     int* s_h = reinterpret_cast<int*>(smem + kBuildScratch);   // histogram staging
     const int tid = tidx();
@@ -512,18 +515,31 @@ struct Stages {
     __syncthreads();
     mark(1);
     // 3. row tiles (th = 128 or 256 rows; the last one of an expert takes
-    //    the smallest class that holds it) and permute chunks, per rank; then
-    //    the table, filled by every thread in parallel (one tile per thread
-    //    per pass)
+    //    the smallest class that holds it) and permute chunks, then the
+    //    table, filled by every thread in parallel (one tile per thread per
+    //    pass).  Tile order (the temporal schedule of the expert work): the
+    //    tiles are dealt into `bands` token bands -- tile m of an expert with
+    //    nt tiles goes to band b = the b with lo(nt, b) <= m < lo(nt, b + 1),
+    //    lo(nt, b) = ceil(nt b / bands) -- since an expert's rows are sorted
+    //    by token, band b holds roughly the b-th quarter (for 4 bands) of
+    //    every expert's tokens.  Bands run in order, experts most loaded
+    //    first inside a band (longest work first), an expert's tiles
+    //    consecutive.  Every expert with a single tile lands in band 0, so
+    //    after band b every token tile of the first (b + 1) / bands of the
+    //    tokens has all its rows, and its combine overlaps the later bands'
+    //    expert GEMMs instead of waiting for the last expert; within a band an
+    //    expert's weight panels are still streamed once for all its tiles
+    //    there.  bands = 1: plain expert-major order.
     const float esz = TR::kBf16 ? 2.f : 4.f;
-    int nt = 0, np = 0;
+    const int NB = p.bands;
+    auto lo_of = [&](int nt_, int b) { return (nt_ * b + NB - 1) / NB; };
+    int nt = 0, c_r = 0;
     float cost = 0.f;
     if (tid < El) {
-      const int c = s_cnt[s_ord[tid]];
-      nt = (c + p.th - 1) / p.th;
+      c_r = s_cnt[s_ord[tid]];
+      nt = (c_r + p.th - 1) / p.th;
       if (nt > 0) {
-        const int last = c - p.th * (nt - 1);
-        np = (nt - 1) * p.pch + (last + p.perm_rows - 1) / p.perm_rows;
+        const int last = c_r - p.th * (nt - 1);
         // one worker's time for a tile: its MFMA work (padded rows), or its
         // share of HBM bandwidth for the tile's weights
         const float by = 3.f * esz * (float)p.d * (float)p.f;
@@ -535,34 +551,55 @@ struct Stages {
       }
     }
     int n_mt = 0, n_perm = 0;
-    const int mtb = block_exscan(nt, s_w, &n_mt);
-    const int pb = block_exscan(np, s_w, &n_perm);
-    if (tid < El) {
-      s_mtb[tid] = mtb;
-      s_pb[tid] = pb;
-      st_wt(p.mt_base + s_ord[tid], mtb);
-    }
-    if (tid == 0) {
-      s_mtb[El] = n_mt;
-      s_pb[El] = n_perm;
+    for (int b = 0; b < NB; ++b) {
+      // tiles and permute chunks of rank tid in band b
+      int bt = 0, bp = 0;
+      if (tid < El) {
+        const int m0 = lo_of(nt, b), m1 = lo_of(nt, b + 1);
+        bt = m1 - m0;
+        if (bt > 0) {
+          const int lastrows = min(p.th, c_r - p.th * (m1 - 1));
+          bp = (bt - 1) * p.pch + (lastrows + p.perm_rows - 1) / p.perm_rows;
+        }
+      }
+      int tot_t = 0, tot_p = 0;
+      const int ot = block_exscan(bt, s_w, &tot_t);
+      const int op = block_exscan(bp, s_w, &tot_p);
+      if (tid < El) {
+        s_bt[b * 257 + tid] = n_mt + ot;
+        s_bp[b * 257 + tid] = n_perm + op;
+      }
+      if (tid == 0) {
+        s_bt[b * 257 + El] = n_mt + tot_t;
+        s_bp[b * 257 + El] = n_perm + tot_p;
+      }
+      n_mt += tot_t;
+      n_perm += tot_p;
     }
     const float tot_cost = block_sum(cost, s_wf);
     if (n_mt > p.max_mt || n_perm > p.max_perm) {
       if (tid == 0) set_error(p, 6 /* MOE_ERR_CAPACITY */);
       return;
     }
+    __syncthreads();
     for (int mt = tid; mt < n_mt; mt += kThreads) {
-      // rank of this tile: the last rank whose tile base is <= mt (ranks
-      // with no rows sort last, so they never match a real tile)
+      // band: the last one starting at or before mt
+      int b = 0;
+      while (b + 1 < NB && s_bt[(b + 1) * 257] <= mt) ++b;
+      const int* bt_b = s_bt + b * 257;
+      // rank: the last one whose base in the band is <= mt (ranks without a
+      // tile in this band share the next rank's base, so they never match)
       int lo = 0, hi = El - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_mtb[mid] <= mt) lo = mid;
+        if (bt_b[mid] <= mt) lo = mid;
         else hi = mid - 1;
       }
       const int r = lo;
       const int e = s_ord[r];
-      const int m = mt - s_mtb[r];
+      const int ntr = (s_cnt[e] + p.th - 1) / p.th;
+      const int j = mt - bt_b[r];                 // tile j of this rank in the band
+      const int m = lo_of(ntr, b) + j;
       const int rows = min(p.th, s_cnt[e] - p.th * m);
       const int bm = row_class(rows);
       static_assert(sizeof(MTile) == 16, "MTile is one 16-byte store");
@@ -573,7 +610,7 @@ struct Stages {
       for (int ks = 0; ks < p.splitk; ++ks)
         st_wt(p.cnt_down + mt * p.splitk + ks,
               slice_lo(ks + 1, p.n_up_n, p.splitk) - slice_lo(ks, p.n_up_n, p.splitk));
-      const int pbase = s_pb[r] + m * p.pch;
+      const int pbase = s_bp[b * 257 + r] + j * p.pch;
       for (int c2 = 0; c2 < npt; ++c2) st_wt(p.perm_list + pbase + c2, make_task(TK_PERM, mt * p.pch + c2));
     }
     mark(3);
@@ -639,11 +676,10 @@ struct Stages {
     }
     s_e[i] = e;
     // this slot's segment base, loaded while the ranks are counted
-    int base = 0, eoff = 0, mtb = 0;
+    int base = 0, eoff = 0;
     if (e >= 0) {
       eoff = p.offsets[e];
       base = eoff + p.rt_base[(size_t)e * p.hist_ld + rt];
-      mtb = p.mt_base[e];
     }
     __syncthreads();
     int mt = -1;
@@ -657,7 +693,7 @@ struct Stages {
         st_wt(p.perm + pos, t0 + i / k);
         st_wt(p.rw + pos, w);
         st_wt(p.slot_pos + (size_t)t0 * k + i, pos);
-        mt = mtb + (pos - eoff) / p.th;
+        mt = (e << 16) | ((pos - eoff) / p.th);   // the row tile: (expert, tile of the expert)
       }
     }
     s_mt[i] = mt;
@@ -948,6 +984,7 @@ struct Stages {
     for (int i0 = tidx(); i0 < n; i0 += 2 * kThreads) {
       float4 v[2][kMaxK];
       float4 sh[2][4];
+      float4 rs[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int i = i0 + u * kThreads;
@@ -974,6 +1011,9 @@ struct Stages {
           if (i < n && s < p.n_shared)
             sh[u][s] = *reinterpret_cast<const float4*>(p.Ys + ((size_t)s * p.T + t0 + r) * p.d + col);
         }
+        rs[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < n && p.resid)
+          rs[u] = *reinterpret_cast<const float4*>(p.resid + (size_t)(t0 + r) * p.d + col);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -997,7 +1037,57 @@ struct Stages {
             acc.x += sh[u][s].x; acc.y += sh[u][s].y; acc.z += sh[u][s].z; acc.w += sh[u][s].w;
           }
         }
-        *reinterpret_cast<float4*>(p.y + (size_t)(t0 + r) * p.d + col) = acc;
+        // the residual last (the block output h = residual + MoE(x))
+        acc.x += rs[u].x; acc.y += rs[u].y; acc.z += rs[u].z; acc.w += rs[u].w;
+        // write-through: a NORM task on another XCD reads these rows
+        st_wt16(p.y + (size_t)(t0 + r) * p.d, (uint32_t)col * 4u,
+                make_uint4(__float_as_uint(acc.x), __float_as_uint(acc.y), __float_as_uint(acc.z),
+                           __float_as_uint(acc.w)));
+      }
+    }
+    __syncthreads();
+  }
+
+  // -------------------------------------------------------- block tail
+  // NORM(rt): y_norm[t] = y[t] / sqrt(mean_c y[t,c]^2 + eps) * gamma for the
+  // 32 tokens of tile rt, y already holding residual + MoE output -- the
+  // residual and normalisation stages the blog walk-through keeps inside the
+  // big MoE kernel (xxqk.cn/news/665650 section 1), fused so the layer output
+  // is not re-read by a separate kernel.  One wave per token in turn; each
+  // lane sums the squares of its columns in a fixed order, then a butterfly
+  // over the wave (every lane ends with the same bits), so the result does
+  // not depend on the schedule.  `coherent`: y was accumulated with atomics
+  // (scatter combine), so it is read with device-coherent loads.
+  static TASKFN void norm(const Params& p, int rt, bool coherent) {
+    const int t0 = rt * kTB;
+    const int rows = min(kTB, p.T - t0);
+    const int wave = tidx() >> 6, lane = tidx() & 63;
+    for (int r = wave; r < rows; r += kThreads / 64) {
+      const float* yr = p.y + (size_t)(t0 + r) * p.d;
+      float ss = 0.f;
+      for (int c = lane * 4; c < p.d; c += 256) {
+        const float4 v = coherent ? ld_coherent4(yr + c) : *reinterpret_cast<const float4*>(yr + c);
+        ss += v.x * v.x;
+        ss += v.y * v.y;
+        ss += v.z * v.z;
+        ss += v.w * v.w;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      const float scale = 1.0f / sqrtf(ss / (float)p.d + p.norm_eps);
+      Elem* out = reinterpret_cast<Elem*>(p.y_norm) + (size_t)(t0 + r) * p.d;
+      for (int c = lane * 4; c < p.d; c += 256) {
+        const float4 v = coherent ? ld_coherent4(yr + c) : *reinterpret_cast<const float4*>(yr + c);
+        const float4 g = *reinterpret_cast<const float4*>(p.norm_w + c);
+        const float o0 = v.x * scale * g.x, o1 = v.y * scale * g.y;
+        const float o2 = v.z * scale * g.z, o3 = v.w * scale * g.w;
+        if constexpr (TR::kBf16) {
+          *reinterpret_cast<uint2*>(out + c) =
+              make_uint2((uint32_t)f2bf(o0) | ((uint32_t)f2bf(o1) << 16),
+                         (uint32_t)f2bf(o2) | ((uint32_t)f2bf(o3) << 16));
+        } else {
+          *reinterpret_cast<float4*>(out + c) = make_float4(o0, o1, o2, o3);
+        }
       }
     }
     __syncthreads();

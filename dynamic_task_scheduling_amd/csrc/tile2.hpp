@@ -12,10 +12,10 @@
 //
 // LDS layouts (one stage):
 //   A: BM rows x 128 bytes (64 bf16 of K).  16-byte chunk c of row m sits at
-//      position c ^ (m & 7): the 16 rows one fragment read touches fall on 8
-//      distinct bank groups.
+//      position c ^ swz_a128(m): the 16 rows one 16-lane phase of a fragment
+//      read touches fall on 16 distinct 16-byte bank groups.
 //   B: 64 rows (K) x 256 bytes (128 bf16 of N), the weights' natural row-major
-//      layout; chunk c of row k at c ^ 2*(k & 3).  The MFMA B operand needs
+//      layout; chunk c of row k at c ^ swz_b(k).  The MFMA B operand needs
 //      8 consecutive K per lane, which ds_read_b64_tr_b16 delivers: each 16-lane
 //      group reads a 4 (K) x 16 (N) block and every lane receives one column.
 // A lane of a global_load_lds instruction writes its 16 bytes at
@@ -29,6 +29,21 @@ namespace moe {
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
+
+// LDS swizzles.  gfx950's LDS has 64 banks of 4 bytes (256 bytes per clock):
+// a 16-byte-per-lane read is served 16 lanes at a time and an 8-byte-per-lane
+// read 32 lanes at a time, so the lanes served together must fall on 16
+// distinct 16-byte bank groups of a 256-byte line.  Each function gives the
+// XOR applied to the 16-byte chunk index of a row.
+//   swz_a128: A rows of 128 bytes (8 chunks): a fragment read takes one chunk
+//             of 16 consecutive rows, two rows per 256-byte line.
+//   swz_a64:  A rows of 64 bytes (4 chunks): four rows per line.
+//   swz_b:    B rows of 256 bytes (16 chunks): a transposing read takes two
+//             chunks of 4 consecutive rows per 16 lanes, 32 lanes together
+//             read four chunks of 4 rows.
+DEV int swz_a128(int m) { return (m >> 1) & 7; }
+DEV int swz_a64(int m) { return (m >> 2) & 3; }
+DEV int swz_b(int k) { return 4 * (k & 3); }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
 // vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt left at their maxima).
@@ -150,21 +165,21 @@ struct Tile2 {
 
   static DEV void make_lane(const Args& g, int tid, Lane& L) {
     const int wave = tid >> 6, lane = tid & 63;
-    // DMA sources.  A: rows 8i..8i+7, chunk c of row m at c ^ (m & 7).
+    // DMA sources.  A: rows 8i..8i+7, chunk c of row m at c ^ swz_a128(m).
 #pragma unroll
     for (int ii = 0; ii < A_INST; ++ii) {
       const int i = wave * A_INST + ii;
       const int m = 8 * i + (lane >> 3);
-      const int c = (lane & 7) ^ (m & 7);
+      const int c = (lane & 7) ^ swz_a128(m);
       const int mr = m < g.a_rows ? m : g.a_rows - 1;
       L.a_src[ii] = (uint32_t)mr * (uint32_t)g.lda * 2u + (uint32_t)c * 16u;
     }
-    // B: K rows 4i..4i+3, chunk c of row k at c ^ 2*(k & 3).
+    // B: K rows 4i..4i+3, chunk c of row k at c ^ swz_b(k).
 #pragma unroll
     for (int ii = 0; ii < B_INST; ++ii) {
       const int i = wave * B_INST + ii;
       const int k = 4 * i + (lane >> 4);
-      int c = (lane & 15) ^ (2 * (k & 3));
+      int c = (lane & 15) ^ swz_b(k);
       if constexpr (CLAMP_B) c = (c * 8 < g.b_cols) ? c : 0;
       L.b_src[ii] = (uint32_t)k * (uint32_t)g.ldb * 2u + (uint32_t)c * 16u;
     }
@@ -181,7 +196,7 @@ struct Tile2 {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int c = kk * 2 + lh;
-        L.a_rd[fm][kk] = (uint32_t)(m * 128 + ((c ^ (m & 7)) << 4));
+        L.a_rd[fm][kk] = (uint32_t)(m * 128 + ((c ^ swz_a128(m)) << 4));
       }
     }
 #pragma unroll
@@ -189,7 +204,7 @@ struct Tile2 {
       const int n = wn * WTN + fn * 32 + 16 * (lg & 1) + 4 * (l16 & 3);
       const int kl = 8 * (lg >> 1) + (l16 >> 2);
       const int c = n >> 3, half = (n >> 2) & 1;
-      L.b_rd[fn] = (uint32_t)(A_BYTES + kl * 256 + ((c ^ (2 * (kl & 3))) << 4) + half * 8);
+      L.b_rd[fn] = (uint32_t)(A_BYTES + kl * 256 + ((c ^ swz_b(kl)) << 4) + half * 8);
     }
   }
 

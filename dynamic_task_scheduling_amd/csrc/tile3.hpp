@@ -19,10 +19,10 @@
 //
 // LDS layouts (one stage):
 //   A: 256 rows x 64 bytes (32 bf16 of K).  16-byte chunk c of row m sits at
-//      position c ^ ((m >> 1) & 3): the eight rows one 8-lane phase of a
-//      fragment read touches fall on eight distinct 16-byte bank groups.
+//      position c ^ swz_a64(m): the sixteen rows one 16-lane phase of a
+//      fragment read touches fall on sixteen distinct 16-byte bank groups.
 //   B: 32 rows (K) x 256 bytes (128 bf16 of N), chunk c of row k at
-//      c ^ 2 * (k & 3), read with ds_read_b64_tr_b16 into the K-contiguous
+//      c ^ swz_b(k), read with ds_read_b64_tr_b16 into the K-contiguous
 //      MFMA operand (as in tile2.hpp).
 #pragma once
 #include "tile2.hpp"
@@ -103,12 +103,12 @@ struct Tile3 {
   static DEV void make_lane(const Args& g, int tid, Lane& L) {
     const int wave = tid >> 6, lane = tid & 63;
     // A: instruction i covers rows 16 i .. 16 i + 15; lane -> row l / 4,
-    // LDS chunk l % 4, which holds global chunk (l % 4) ^ ((m >> 1) & 3).
+    // LDS chunk l % 4, which holds global chunk (l % 4) ^ swz_a64(m).
 #pragma unroll
     for (int ii = 0; ii < A_INST; ++ii) {
       const int i = wave * A_INST + ii;
       const int m = 16 * i + (lane >> 2);
-      const int c = (lane & 3) ^ ((m >> 1) & 3);
+      const int c = (lane & 3) ^ swz_a64(m);
       const int mr = m < g.a_rows ? m : g.a_rows - 1;
       L.a_src[ii] = (uint32_t)mr * (uint32_t)g.lda * 2u + (uint32_t)c * 16u;
     }
@@ -117,7 +117,7 @@ struct Tile3 {
     for (int ii = 0; ii < B_INST; ++ii) {
       const int i = wave * B_INST + ii;
       const int k = 4 * i + (lane >> 4);
-      const int c = (lane & 15) ^ (2 * (k & 3));
+      const int c = (lane & 15) ^ swz_b(k);
       L.b_src[ii] = (uint32_t)k * (uint32_t)g.ldb * 2u + (uint32_t)c * 16u;
     }
     L.a_dst = __builtin_amdgcn_readfirstlane((uint32_t)(wave * A_INST) * 1024u);
@@ -130,7 +130,7 @@ struct Tile3 {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int c = kk * 2 + lh;
-        L.a_rd[fm][kk] = (uint32_t)(m * 64 + ((c ^ ((m >> 1) & 3)) << 4));
+        L.a_rd[fm][kk] = (uint32_t)(m * 64 + ((c ^ swz_a64(m)) << 4));
       }
     }
 #pragma unroll
@@ -138,7 +138,7 @@ struct Tile3 {
       const int n = wn * WTN + fn * 32 + 16 * (lg & 1) + 4 * (l16 & 3);
       const int kl = 8 * (lg >> 1) + (l16 >> 2);
       const int c = n >> 3, half = (n >> 2) & 1;
-      L.b_rd[fn] = (uint32_t)(A_BYTES + kl * 256 + ((c ^ (2 * (kl & 3))) << 4) + half * 8);
+      L.b_rd[fn] = (uint32_t)(A_BYTES + kl * 256 + ((c ^ swz_b(kl)) << 4) + half * 8);
     }
   }
 

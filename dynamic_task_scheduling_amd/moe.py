@@ -37,7 +37,7 @@ def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model
               split_k: int = 0, max_workers: int = 0, fixed_mem_workers: int = 0,
               flags: int = 0, trace: Optional[torch.Tensor] = None,
               timeout_ms: int = 0, row_tile: int = 0, combine: str = "auto",
-              timeout_ticks: int = 0) -> Desc:
+              timeout_ticks: int = 0, bands: int = 0) -> Desc:
     d = Desc()
     d.T, d.d, d.E, d.k, d.f = shape.T, shape.d, shape.E, shape.k, shape.f
     d.e_begin, d.e_end = shape.e_begin, shape.local_end
@@ -58,6 +58,7 @@ def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model
     d.row_tile = row_tile
     d.combine = _abi.COMBINES[combine]
     d.timeout_ticks = timeout_ticks
+    d.bands = bands
     return d
 
 
@@ -124,14 +125,14 @@ class MoELayer:
                  max_workers: int = 0, fixed_mem_workers: int = 0, flags: int = 0,
                  trace: Optional[torch.Tensor] = None, timeout_ms: int = 0,
                  workspace: Optional[torch.Tensor] = None, row_tile: int = 0,
-                 combine: str = "auto", timeout_ticks: int = 0):
+                 combine: str = "auto", timeout_ticks: int = 0, bands: int = 0):
         self.shape = shape
         dev = weights["w_gate"].device
         if dev.type != "cuda":
             raise ValueError("weights must be on a GPU")
         self.device = dev
         self.desc = make_desc(shape, mode, split, split_k, max_workers, fixed_mem_workers,
-                              flags, trace, timeout_ms, row_tile, combine, timeout_ticks)
+                              flags, trace, timeout_ms, row_tile, combine, timeout_ticks, bands)
         self._trace = trace
         et = _elem_dtype(shape)
         d, E, f, El = shape.d, shape.E, shape.f, shape.E_loc
@@ -164,7 +165,12 @@ class MoELayer:
 
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
                  routing: Optional[RoutingResult] = None, return_routing: bool = False,
-                 check_errors: bool = False):
+                 check_errors: bool = False, residual: Optional[torch.Tensor] = None,
+                 norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+                 y_norm: Optional[torch.Tensor] = None):
+        """y = MoE(x); with norm_weight also the fused block tail:
+        y = residual + MoE(x) and y_norm = RMSNorm(y) * norm_weight, returned
+        as (y, y_norm[, routing])."""
         s = self.shape
         _check_tensor("x", x, (s.T, s.d), _elem_dtype(s), self.device)
         if y is None:
@@ -176,14 +182,32 @@ class MoELayer:
         if check_errors:
             desc = Desc.from_buffer_copy(self.desc)
             desc.flags |= _abi.FLAG_CHECK
+        fused = norm_weight is not None
+        if fused:
+            _check_tensor("norm_weight", norm_weight, (s.d,), torch.float32, self.device)
+            if residual is not None:
+                _check_tensor("residual", residual, (s.T, s.d), torch.float32, self.device)
+            if y_norm is None:
+                y_norm = torch.empty((s.T, s.d), dtype=_elem_dtype(s), device=self.device)
+            _check_tensor("y_norm", y_norm, (s.T, s.d), _elem_dtype(s), self.device)
+        elif residual is not None:
+            raise ValueError("residual is fused only together with norm_weight")
         with torch.cuda.device(self.device):
-            rc = lib().moe_layer(ctypes.byref(desc), _ptr(x), ctypes.byref(self._w), _ptr(y),
-                                 _routing_struct(routing), _ptr(self.workspace),
-                                 self.workspace.numel(), _stream(self.device))
+            if fused:
+                rc = lib().moe_layer_norm(ctypes.byref(desc), _ptr(x), ctypes.byref(self._w),
+                                          _ptr(residual), _ptr(norm_weight), float(norm_eps),
+                                          _ptr(y), _ptr(y_norm), _routing_struct(routing),
+                                          _ptr(self.workspace), self.workspace.numel(),
+                                          _stream(self.device))
+            else:
+                rc = lib().moe_layer(ctypes.byref(desc), _ptr(x), ctypes.byref(self._w), _ptr(y),
+                                     _routing_struct(routing), _ptr(self.workspace),
+                                     self.workspace.numel(), _stream(self.device))
         check(rc)
+        out = (y, y_norm) if fused else (y,)
         if routing is not None:
-            return y, routing
-        return y
+            out = out + (routing,)
+        return out if len(out) > 1 else y
 
     def last_schedule(self) -> Dict[str, int]:
         """The scheduler's decisions in the last call (synchronises)."""

@@ -129,6 +129,9 @@ typedef struct moe_desc {
   int row_tile;       /* expert row-tile height 128 or 256 (bf16 only);
                          0 = automatic (256 when T*k > 8192 in bf16)        */
   int combine;        /* moe_combine                                        */
+  int bands;          /* row-tile order: tiles dealt into this many token
+                         bands, run band by band (1 = plain expert-major
+                         order); 0 = automatic (1)                          */
   int timeout_ticks;  /* > 0: watchdog limit per wait in ticks of the 100 MHz
                          device clock, overriding timeout_ms (lets a test
                          force the watchdog; every wait then gives up and the
@@ -194,32 +197,72 @@ typedef struct moe_info {
   float cost_mfma_flops_per_cu;      /* sustained MFMA flop/s of one CU in expert tiles */
   float cost_gather_bytes_per_worker; /* bytes/s one worker moves in a gather task */
   float cost_hbm_bytes;              /* device bytes/s a streaming tile sustains */
+  int bands;            /* token bands of the row-tile order               */
 } moe_info;
 
-/* Bytes of workspace a call with this descriptor needs (0 on bad desc). */
+/* Bytes of workspace a call with this descriptor needs (0 on a bad
+ * descriptor).  The workspace holds every piece of scheduling state -- queues,
+ * dependency counters, task tables -- and the intermediate rows, so the
+ * library allocates nothing (the graft/overlap chapter, hncyxsy.com/news/277526,
+ * CUDA Graph section: state resident at fixed addresses, nothing allocated
+ * inside a captured region).  Caller-owned, any device allocation, 256-byte
+ * aligned; reusable across calls with the same descriptor. */
 size_t moe_workspace_size(const moe_desc* desc);
 
-/* Fill `info` for this descriptor on the current device. */
+/* Fill `info` for this descriptor on the current device: workers, tile and
+ * task geometry, and the cost model's frozen constants.  Host only (no
+ * launch).  MOE_ERR_ARG on a bad descriptor or NULL info, MOE_ERR_HIP if the
+ * device cannot be queried. */
 int moe_query(const moe_desc* desc, moe_info* info);
 
-/* Run one MoE layer: y[T,d] (fp32, overwritten) = sum over each token's kept
- * top-k experts of w * SwiGLU_e(x[t]) + sum of the shared experts.
- * `routing` may be NULL; otherwise the requested routing tables are written.
- * The workspace must be at least moe_workspace_size(desc) bytes. */
+/* Run one MoE layer (the stages the blog walk-through keeps inside one MoE
+ * kernel, xxqk.cn/news/665650 section 1 -- gate/router, top-k, dispatch
+ * (here: the expert-contiguous gather), expert FFN GEMMs, weighted combine --
+ * scheduled as desc.mode says; m.xxqk.cn/news/657744 section 2.1 for the task
+ * units):
+ *   y[T,d] (fp32, overwritten) = sum over each token's kept top-k experts of
+ *   w * SwiGLU_e(x[t]) + sum of the shared experts.
+ * x [T,d] in desc.dtype; weights per moe_weights; device pointers.  `routing`
+ * may be NULL; otherwise the requested tables are written (the
+ * routing(topk_idx, topk_w, expert_counts) check surface).  Asynchronous on
+ * hip_stream; argument errors (MOE_ERR_ARG / WORKSPACE / UNSUPPORTED) return
+ * before any launch, launch failures MOE_ERR_HIP; device errors go to the
+ * workspace (see moe_last_device_error) unless MOE_FLAG_CHECK is set. */
 int moe_layer(const moe_desc* desc, const void* x, const moe_weights* weights,
               float* y, const moe_routing* routing, void* workspace,
               size_t workspace_bytes, void* hip_stream);
 
-/* Routing only, from caller-supplied fp32 logits [T, E]: top-k, weights,
- * counts, offsets, perm and slot_pos, with the same device code the layer
- * uses.  Lets a checker feed identical logits to this library and to a
- * reference and compare the tables bit for bit. */
+/* moe_layer with the block tail fused in: the residual add and the
+ * normalisation the blog walk-through lists among the big kernel's stages
+ * (xxqk.cn/news/665650 section 1), done by tasks of the same persistent
+ * kernel as soon as a token tile's rows are complete, instead of a separate
+ * kernel re-reading y:
+ *   y[t]      = residual[t] + MoE(x)[t]                       (fp32)
+ *   y_norm[t] = y[t] / sqrt(mean_c y[t,c]^2 + norm_eps) * norm_weight
+ * residual [T,d] fp32 (NULL: no residual), norm_weight [d] fp32, y_norm
+ * [T,d] in desc.dtype (bf16 layers: rounded to nearest even).  Every other
+ * argument, the ownership and the errors as moe_layer; MOE_ERR_ARG also for a
+ * NULL norm_weight or y_norm, or a negative / NaN norm_eps. */
+int moe_layer_norm(const moe_desc* desc, const void* x, const moe_weights* weights,
+                   const float* residual, const float* norm_weight, float norm_eps,
+                   float* y, void* y_norm, const moe_routing* routing, void* workspace,
+                   size_t workspace_bytes, void* hip_stream);
+
+/* Routing only, from caller-supplied fp32 logits [T, E] (device): top-k,
+ * weights, counts, offsets, perm and slot_pos, with the same device code the
+ * layer uses (top-k with renormalised weights, xxqk.cn/news/665650 section 1).
+ * Lets a checker feed identical logits to this library and to a reference
+ * and compare the tables bit for bit.  Errors as moe_layer; a NaN or
+ * infinite logit is the device error MOE_ERR_NONFINITE. */
 int moe_route_from_logits(const moe_desc* desc, const float* logits,
                           const moe_routing* routing, void* workspace,
                           size_t workspace_bytes, void* hip_stream);
 
 /* Synchronise `hip_stream` and return the device error word of the last
- * call that used `workspace` (MOE_OK if none). */
+ * call that used `workspace` (MOE_OK if none): the watchdog and capacity
+ * checks the persistent scheduler makes instead of hanging (the early-exit
+ * and deadlock pitfalls of m.xxqk.cn/news/657744 section 3.3).  MOE_ERR_ARG
+ * on a bad descriptor or NULL workspace, MOE_ERR_HIP if the copy fails. */
 int moe_last_device_error(const moe_desc* desc, const void* workspace,
                           void* hip_stream);
 

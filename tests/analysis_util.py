@@ -6,10 +6,10 @@ import numpy as np
 
 from dynamic_task_scheduling_amd.analysis import decode_trace
 
-ROUTE, POS, PERM, UP, DOWN, SUP, SDOWN, COMB = 1, 2, 3, 4, 5, 6, 7, 9
+ROUTE, POS, PERM, UP, DOWN, SUP, SDOWN, COMB, NORM = 1, 2, 3, 4, 5, 6, 7, 9, 10
 
 
-def check_trace(raw, layer, routing):
+def check_trace(raw, layer, routing, fused_norm=False):
     tr = decode_trace(raw)
     info = layer.info
     s = layer.shape
@@ -31,7 +31,8 @@ def check_trace(raw, layer, routing):
     expect = {ROUTE: n_rt * info["route_splits"], POS: n_rt, UP: n_mt * n_up,
               DOWN: n_mt * n_down * sk,
               SUP: s.n_shared * n_smt * n_sup_n, SDOWN: s.n_shared * n_smt * n_down,
-              COMB: 0 if info["combine"] == 1 else n_rt * n_cc}
+              COMB: 0 if info["combine"] == 1 else n_rt * n_cc,
+              NORM: n_rt if fused_norm else 0}
     for k, n in expect.items():
         assert int((kinds == k).sum()) == n, "kind %d ran %d times, expected %d" % (
             k, int((kinds == k).sum()), n)
@@ -60,15 +61,11 @@ def check_trace(raw, layer, routing):
         if k == SDOWN:
             m = (int(p) // n_down) % n_smt
             sdown_end[m] = max(sdown_end[m], end[int(t)])
-    # row tiles: experts by descending count (ties: lower index), each
-    # expert's tiles consecutive; a combine tile waits for the DOWN tiles of
-    # every row tile that holds one of its tokens' kept slots
-    order = sorted(range(len(counts)), key=lambda e: (-int(counts[e]), e))
-    mt_base = {}
-    acc = 0
-    for e in order:
-        mt_base[e] = acc
-        acc += (int(counts[e]) + th - 1) // th
+    # row tiles in the builder's order (token bands, experts by descending
+    # count inside a band); a combine tile waits for the DOWN tiles of every
+    # row tile that holds one of its tokens' kept slots
+    from dynamic_task_scheduling_amd.analysis import row_tiles
+    tile_of = {(e, m): mt for mt, (e, rows, m) in enumerate(row_tiles(counts, th, info["bands"]))}
     offs = routing.offsets.cpu().numpy()
     idx = routing.topk_idx.cpu().numpy()
     spos = routing.slot_pos.cpu().numpy()
@@ -79,7 +76,7 @@ def check_trace(raw, layer, routing):
             if pos < 0:
                 continue
             e = int(idx[tok, j]) - s.e_begin
-            mt = mt_base[e] + (pos - int(offs[e])) // th
+            mt = tile_of[(e, (pos - int(offs[e])) // th)]
             comb_need[tok // 32] = max(comb_need[tok // 32], down_end[mt])
         if s.n_shared:
             comb_need[tok // 32] = max(comb_need[tok // 32], sdown_end[tok // th])
@@ -107,4 +104,10 @@ def check_trace(raw, layer, routing):
         elif k == COMB:
             assert st >= end[(POS << 27) | (p // n_cc)], "COMB before its POS tile"
             assert st >= comb_need[p // n_cc], "COMB before one of its DOWN tiles"
+        elif k == NORM:
+            assert st >= end[(POS << 27) | p], "NORM before its POS tile"
+            assert st >= comb_need[p], "NORM before one of its DOWN tiles"
+            if info["combine"] != 1:
+                last = max(end[(COMB << 27) | (p * n_cc + c)] for c in range(n_cc))
+                assert st >= last, "NORM before its combine chunks"
     return tr

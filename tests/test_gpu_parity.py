@@ -417,6 +417,84 @@ def test_graph_capture_replay_new_inputs(mid, mode):
         assert torch.equal(y_e, y)
 
 
+def _norm_inputs(shape, seed):
+    rng = torch.Generator().manual_seed(seed)
+    res = torch.randn((shape.T, shape.d), generator=rng)
+    gamma = (1.0 + 0.5 * torch.randn(shape.d, generator=rng)).float()
+    return res.cuda(), gamma.cuda()
+
+
+def check_fused_tail(shape, g, n, mode, split, combine, eps=1e-6, label="", seed=41):
+    """moe_layer_norm against the oracle: y = residual + MoE(x) and
+    y_norm = RMSNorm(y) * gamma; y_norm also against the fp64 RMSNorm of the
+    GPU's own y (only the bf16 rounding of y_norm may differ)."""
+    from gpu_util import log
+    res, gamma = _norm_inputs(shape, seed)
+    layer = MoELayer(shape, g, mode=mode, split=split, timeout_ms=3000, combine=combine)
+    y, yn, r = layer(g["x"], return_routing=True, check_errors=True, residual=res,
+                     norm_weight=gamma, norm_eps=eps)
+    torch.cuda.synchronize()
+    ro = oracle.route(r.logits.cpu().numpy(), shape.k, shape.e_begin, shape.local_end)
+    check_routing(r, ro, shape)
+    shared = (n["ws_gate"], n["ws_up"], n["ws_down"]) if shape.n_shared else None
+    y_moe = oracle.moe_layer(n["x"], n["w_gate"], n["w_up"], n["w_down"], ro, shape.e_begin, shared)
+    g_np = gamma.cpu().numpy()
+    h, hn = oracle.residual_rmsnorm(y_moe, res.cpu().numpy(), g_np, eps)
+    compare_y(y.cpu().numpy(), h, "bf16")
+    yn_np = yn.float().cpu().numpy().astype(np.float64)
+    err, rel = compare_y(yn_np, hn, "bf16")
+    _, hn_own = oracle.residual_rmsnorm(y.cpu().numpy().astype(np.float64), None, g_np, eps)
+    bound = 2.0 ** -8 * np.abs(hn_own) + 1e-5 * np.abs(hn_own).max()
+    assert np.all(np.abs(yn_np - hn_own) <= bound), "RMSNorm arithmetic"
+    log("       fused tail %s %s/%s %s ok: y_norm max|err| %.2e rel %.2e" % (label, mode, split, combine,
+                                                                            err, rel))
+    return layer, y, yn, res, gamma
+
+
+@pytest.mark.parametrize("combine", ["tasks", "scatter"])
+@pytest.mark.parametrize("mode,split", MODES)
+def test_fused_residual_rmsnorm(mid, mode, split, combine):
+    g, n = mid
+    layer, y, yn, res, gamma = check_fused_tail(MID, g, n, mode, split, combine, label="mid")
+    if combine == "tasks":
+        # fixed-order combine: the fused y is the plain layer's y plus the
+        # residual, bit for bit
+        y0 = MoELayer(MID, g, mode=mode, split=split, combine="tasks")(g["x"], check_errors=True)
+        assert torch.equal(y, y0 + res)
+
+
+def test_fused_tail_no_residual_and_local_range():
+    """No residual (y_norm = RMSNorm(MoE(x))), a local expert range with
+    tokens that have no local expert, fp32 layer."""
+    s = LayerShape(T=150, d=256, E=16, k=4, f=256, e_begin=4, e_end=12, zipf_s=1.2, dtype="fp32")
+    g = gen_inputs(s, "norm_local", 13)
+    n = host_inputs(g)
+    for combine in ("tasks", "scatter"):
+        layer = MoELayer(s, g, mode="dynamic", timeout_ms=3000, combine=combine)
+        gamma = torch.ones(s.d, dtype=torch.float32, device="cuda")
+        y, yn, r = layer(g["x"], return_routing=True, check_errors=True, norm_weight=gamma,
+                         norm_eps=1e-5)
+        torch.cuda.synchronize()
+        ro = oracle.route(r.logits.cpu().numpy(), s.k, s.e_begin, s.local_end)
+        y_moe = oracle.moe_layer(n["x"], n["w_gate"], n["w_up"], n["w_down"], ro, s.e_begin)
+        h, hn = oracle.residual_rmsnorm(y_moe, None, gamma.cpu().numpy(), 1e-5)
+        compare_y(y.cpu().numpy(), h, "fp32")
+        compare_y(yn.cpu().numpy(), hn, "fp32")
+
+
+@pytest.mark.parametrize("combine", ["tasks", "scatter"])
+def test_fused_tail_trace(mid, combine):
+    """Every NORM task runs once, after every task that writes its rows."""
+    from analysis_util import check_trace
+    g, n = mid
+    res, gamma = _norm_inputs(MID, 42)
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(MID, g, mode="dynamic", trace=trace, timeout_ms=3000, combine=combine)
+    y, yn, r = layer(g["x"], return_routing=True, check_errors=True, residual=res, norm_weight=gamma)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r, fused_norm=True)
+
+
 def test_trace_happens_before(mid):
     """Every task runs exactly once and starts after its producers ended."""
     from analysis_util import check_trace
@@ -451,6 +529,20 @@ def _full(cfg, layers=None):
 @pytest.mark.timeout(600)
 def test_full_decode():
     _full(2)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_fused_tail(cfg):
+    """The fused residual + RMSNorm tail at full size: decode (scatter-add
+    combine) and prefill (combine tasks), all three modes."""
+    from dynamic_task_scheduling_amd.synth import make_layer
+    wl = workload(cfg)
+    s = wl.layers[0]
+    t = make_layer(s, wl.name, 0, 0, "cuda")
+    n = host_inputs(t)
+    for mode, split in FULL_MODES:
+        check_fused_tail(s, t, n, mode, split, "auto", label=wl.name)
 
 
 @pytest.mark.timeout(900)
