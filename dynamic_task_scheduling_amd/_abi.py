@@ -18,10 +18,12 @@ FLAG_XCD_AFFINITY = 0x20
 ERRORS = {
     0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_WORKSPACE", 3: "MOE_ERR_UNSUPPORTED",
     4: "MOE_ERR_HIP", 5: "MOE_ERR_TIMEOUT", 6: "MOE_ERR_CAPACITY", 7: "MOE_ERR_NONFINITE",
+    8: "MOE_ERR_TOO_LARGE",
 }
+NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every function the header declares (checked by the CPU tests).
-EXPORTS = ["moe_workspace_size", "moe_query", "moe_layer", "moe_layer_norm",
+EXPORTS = ["moe_workspace_size", "moe_query", "moe_layer", "moe_layer_norm", "moe_layer_no_alloc",
            "moe_route_from_logits", "moe_last_device_error", "moe_last_schedule", "moe_strerror"]
 
 
@@ -93,6 +95,9 @@ def lib():
                                      ctypes.c_float, c_void_p, c_void_p, P(Routing), c_void_p,
                                      c_size_t, c_void_p]
         L.moe_layer_norm.restype = c_int
+        L.moe_layer_no_alloc.argtypes = [P(Desc), c_void_p, P(Weights), c_void_p, P(Routing),
+                                         c_void_p]
+        L.moe_layer_no_alloc.restype = c_int
         L.moe_route_from_logits.argtypes = [P(Desc), c_void_p, P(Routing), c_void_p,
                                             c_size_t, c_void_p]
         L.moe_route_from_logits.restype = c_int

@@ -429,9 +429,53 @@ int run_layer(const moe_desc* d, const void* x, const moe_weights* w, const floa
   return MOE_OK;
 }
 
+// ------------------------------------------- no-allocation entry point
+// The workspace of moe_layer_no_alloc: a fixed device array of this library,
+// one per GPU the library runs on, held until the process ends.  Host code
+// never uses the array's name as an address (it is only a host-side handle):
+// its device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and is kept per device.
+constexpr size_t kScratchBytes = MOE_NO_ALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % kAlign == 0, "scratch size");
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch[64] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_layer_no_alloc(const moe_desc* d, const void* x, const moe_weights* w, float* y,
+                       const moe_routing* routing, void* stream) {
+  const size_t need = moe_workspace_size(d);
+  if (need == 0) return MOE_ERR_ARG;
+  if (need > kScratchBytes) return MOE_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  return run_layer(d, x, w, nullptr, nullptr, 0.f, y, nullptr, routing, ws, need, stream);
+}
+
 
 size_t moe_workspace_size(const moe_desc* d) {
   if (validate(d) != MOE_OK) return 0;
@@ -543,6 +587,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_TIMEOUT: return "device watchdog timeout";
     case MOE_ERR_CAPACITY: return "device table capacity exceeded";
     case MOE_ERR_NONFINITE: return "non-finite router logit";
+    case MOE_ERR_TOO_LARGE: return "layer needs more workspace than the library's static scratch";
     default: return "unknown error";
   }
 }

@@ -125,7 +125,8 @@ class MoELayer:
                  max_workers: int = 0, fixed_mem_workers: int = 0, flags: int = 0,
                  trace: Optional[torch.Tensor] = None, timeout_ms: int = 0,
                  workspace: Optional[torch.Tensor] = None, row_tile: int = 0,
-                 combine: str = "auto", timeout_ticks: int = 0, bands: int = 0):
+                 combine: str = "auto", timeout_ticks: int = 0, bands: int = 0,
+                 no_alloc: bool = False):
         self.shape = shape
         dev = weights["w_gate"].device
         if dev.type != "cuda":
@@ -154,7 +155,12 @@ class MoELayer:
             setattr(w, name, None if t is None else t.data_ptr())
         self._w = w
         n = workspace_size(self.desc)
-        if workspace is None or workspace.numel() < n:
+        # no_alloc: calls go through moe_layer_no_alloc, whose workspace is the
+        # library's own static per-device scratch (no workspace tensor here)
+        self.no_alloc = no_alloc
+        if no_alloc:
+            workspace = None
+        elif workspace is None or workspace.numel() < n:
             workspace = torch.empty((n,), dtype=torch.uint8, device=dev)
         self.workspace = workspace
 
@@ -192,8 +198,14 @@ class MoELayer:
             _check_tensor("y_norm", y_norm, (s.T, s.d), _elem_dtype(s), self.device)
         elif residual is not None:
             raise ValueError("residual is fused only together with norm_weight")
+        if self.no_alloc and fused:
+            raise ValueError("the fused tail has no no-allocation entry point")
         with torch.cuda.device(self.device):
-            if fused:
+            if self.no_alloc:
+                rc = lib().moe_layer_no_alloc(ctypes.byref(desc), _ptr(x), ctypes.byref(self._w),
+                                              _ptr(y), _routing_struct(routing),
+                                              _stream(self.device))
+            elif fused:
                 rc = lib().moe_layer_norm(ctypes.byref(desc), _ptr(x), ctypes.byref(self._w),
                                           _ptr(residual), _ptr(norm_weight), float(norm_eps),
                                           _ptr(y), _ptr(y_norm), _routing_struct(routing),

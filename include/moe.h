@@ -106,6 +106,10 @@ typedef enum {
 #define MOE_ERR_TIMEOUT 5     /* device watchdog: a wait exceeded its limit */
 #define MOE_ERR_CAPACITY 6    /* a device table overflowed its capacity     */
 #define MOE_ERR_NONFINITE 7   /* a router logit was NaN or infinite         */
+#define MOE_ERR_TOO_LARGE 8   /* moe_layer_no_alloc: workspace > its scratch  */
+
+/* Size of the static per-device scratch moe_layer_no_alloc works in. */
+#define MOE_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef struct moe_desc {
   int T;              /* tokens (>= 0)                                      */
@@ -247,6 +251,18 @@ int moe_layer_norm(const moe_desc* desc, const void* x, const moe_weights* weigh
                    const float* residual, const float* norm_weight, float norm_eps,
                    float* y, void* y_norm, const moe_routing* routing, void* workspace,
                    size_t workspace_bytes, void* hip_stream);
+
+/* moe_layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * workspace is a fixed device array of this library, MOE_NO_ALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held until the process ends; nothing is allocated.  A
+ * layer whose moe_workspace_size exceeds it gets MOE_ERR_TOO_LARGE before
+ * any launch.  Every call on a GPU shares that GPU's scratch (each call
+ * re-initialises what must start at zero): calls that overlap in time on one
+ * GPU -- e.g. on two streams -- race and must not be issued.  Arguments,
+ * results and other errors as moe_layer. */
+int moe_layer_no_alloc(const moe_desc* desc, const void* x, const moe_weights* weights,
+                       float* y, const moe_routing* routing, void* hip_stream);
 
 /* Routing only, from caller-supplied fp32 logits [T, E] (device): top-k,
  * weights, counts, offsets, perm and slot_pos, with the same device code the
