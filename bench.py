@@ -250,6 +250,8 @@ def ablations(run, steps, warmup):
         ("dynamic/bands=1", "dynamic", "cost_model", 0, 1),
         ("dynamic/bands=2", "dynamic", "cost_model", 0, 2),
         ("dynamic/bands=4", "dynamic", "cost_model", 0, 4),
+        ("dynamic/fifo/bands=1", "dynamic", "cost_model", _abi.FLAG_FIFO, 1),
+        ("dynamic/fifo/bands=4", "dynamic", "cost_model", _abi.FLAG_FIFO, 4),
         ("static/sync=phase_barrier", "static", "fixed", 0, None),
         ("static/sync=ref_count", "static", "fixed", _abi.FLAG_REF_SYNC, None),
         ("multi_kernel", "multi_kernel", "none", 0, None),
@@ -263,6 +265,27 @@ def ablations(run, steps, warmup):
             out[name + ":mem_workers"] = L[0].last_schedule()["mem_workers"]
         del L
     return out
+
+
+def time_one_launch(run, steps, warmup):
+    """Every layer of the workload in one moe_layers call (one persistent
+    launch for dynamic-mode layers), timed like a step."""
+    from dynamic_task_scheduling_amd.moe import MoELayers
+    stack = MoELayers(run.layers("dynamic", "cost_model"))
+    torch = run.torch
+
+    xs = [t["x"] for t in run.tensors]
+    for _ in range(warmup):
+        stack(xs, run.ys)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        stack(xs, run.ys)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def summarize(run, ms, steps_note=None):
@@ -390,6 +413,12 @@ def main():
             r2 = Runner(cfg, dev, args.combine)
             ms2 = measure_modes(r2, max(5, args.steps // 2), max(2, args.warmup // 2))
             others[r2.wl.name] = summarize(r2, ms2)
+            if len(r2.wl.layers) > 1:
+                # the multi-layer persistent kernel: all layers in one launch
+                t1 = time_one_launch(r2, max(5, args.steps // 2), max(2, args.warmup // 2))
+                others[r2.wl.name]["ms_one_launch"] = round(t1, 4)
+                others[r2.wl.name]["gain_one_launch_vs_static"] = ms2["static"]["mean"] / t1
+                others[r2.wl.name]["gain_one_launch_vs_multi_kernel"] = ms2["multi_kernel"]["mean"] / t1
             del r2
             torch.cuda.empty_cache()
         out["other_workloads"] = others

@@ -14,6 +14,7 @@ SPLITS = {"cost_model": 0, "fixed": 1, "none": 2}
 COMBINES = {"auto": 0, "scatter": 1, "tasks": 2}
 FLAG_CHECK, FLAG_TRACE, FLAG_PHASE_SYNC, FLAG_REF_SYNC, FLAG_NO_STEAL = 0x1, 0x2, 0x4, 0x8, 0x10
 FLAG_XCD_AFFINITY = 0x20
+FLAG_FIFO = 0x40
 
 ERRORS = {
     0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_WORKSPACE", 3: "MOE_ERR_UNSUPPORTED",
@@ -24,6 +25,7 @@ NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every function the header declares (checked by the CPU tests).
 EXPORTS = ["moe_workspace_size", "moe_query", "moe_layer", "moe_layer_norm", "moe_layer_no_alloc",
+           "moe_layers_workspace_size", "moe_layers",
            "moe_route_from_logits", "moe_last_device_error", "moe_last_schedule", "moe_strerror"]
 
 
@@ -98,6 +100,11 @@ def lib():
         L.moe_layer_no_alloc.argtypes = [P(Desc), c_void_p, P(Weights), c_void_p, P(Routing),
                                          c_void_p]
         L.moe_layer_no_alloc.restype = c_int
+        L.moe_layers_workspace_size.argtypes = [P(Desc), c_int]
+        L.moe_layers_workspace_size.restype = c_size_t
+        L.moe_layers.argtypes = [P(Desc), c_int, P(c_void_p), P(Weights), P(c_void_p), P(Routing),
+                                 c_void_p, c_size_t, c_void_p]
+        L.moe_layers.restype = c_int
         L.moe_route_from_logits.argtypes = [P(Desc), c_void_p, P(Routing), c_void_p,
                                             c_size_t, c_void_p]
         L.moe_route_from_logits.restype = c_int

@@ -124,6 +124,19 @@ DEV int opaque_tid() {
 // persistent loop and kept (or spilled) across all task types.
 DEV int tidx() { return opaque_tid(); }
 
+// Cross-lane exchange inside a wave (ds_bpermute), with the lane index taken
+// from tidx() so that no lane-index arithmetic is hoisted out of the
+// persistent loop.  xor: the value of lane (lane ^ o); up: of lane (lane - o),
+// or the lane's own value for lanes below o.
+DEV float wave_xor(float v, int o) {
+  const int lane = tidx() & 63;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane ^ o) & 63) << 2, __float_as_int(v)));
+}
+DEV int wave_up(int v, int o) {
+  const int lane = tidx() & 63;
+  return __builtin_amdgcn_ds_bpermute((lane >= o ? lane - o : lane) << 2, v);
+}
+
 // A value every lane of the wave holds (a workgroup-wide result broadcast
 // through LDS), read from the first lane into a scalar register, so that the
 // branches and addresses that depend on it are scalar.

@@ -13,6 +13,15 @@ hipError_t launch_dynamic_f32(bool scatter, const Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_dynamic_layers_f32(bool scatter, const Params* layers, int n, int workers,
+                                     hipStream_t s) {
+  if (scatter)
+    hipLaunchKernelGGL((k_dynamic_layers<float, true>), dim3(workers), dim3(kThreads), 0, s, layers, n);
+  else
+    hipLaunchKernelGGL((k_dynamic_layers<float, false>), dim3(workers), dim3(kThreads), 0, s, layers, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_static_f32(bool scatter, const Params& p, hipStream_t s) {
   if (scatter)
     hipLaunchKernelGGL((k_static<float, true>), dim3(p.workers), dim3(kThreads), 0, s, p);

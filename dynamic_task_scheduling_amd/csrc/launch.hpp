@@ -17,6 +17,13 @@ hipError_t launch_dynamic_bf16_scatter(const Params& p, hipStream_t s);
 hipError_t launch_dynamic_bf16_rows(const Params& p, hipStream_t s);
 hipError_t launch_dynamic_f32(bool scatter, const Params& p, hipStream_t s);
 
+// Several layers in one persistent launch; `layers` is a device array of n
+// parameter blocks (all of one element type and combine mode).
+hipError_t launch_dynamic_layers_bf16(bool scatter, const Params* layers, int n, int workers,
+                                      hipStream_t s);
+hipError_t launch_dynamic_layers_f32(bool scatter, const Params* layers, int n, int workers,
+                                     hipStream_t s);
+
 // Persistent static-partition megakernel.
 hipError_t launch_static_bf16(bool scatter, const Params& p, hipStream_t s);
 hipError_t launch_static_f32(bool scatter, const Params& p, hipStream_t s);

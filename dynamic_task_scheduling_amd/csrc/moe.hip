@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "launch.hpp"
@@ -24,7 +25,7 @@ __host__ __device__ inline int ctrl_init(const Params& p, int w) {
   if (w == CW_TAIL + QA) return n_route;
   if (w == CW_TOTAL + QA) return n_route + p.n_rt;
   if (w == CW_TAIL + QC) return p.n_sup;
-  if (w == CW_TOTAL + QM || w == CW_TOTAL + QC) return 0x7fffffff;
+  if (w == CW_TOTAL + QM || w == CW_TOTAL + QC || w == CW_TOTAL + QH) return 0x7fffffff;
   if (w >= CW_UTOTAL && w < CW_UTOTAL + kXcds) return 0x7fffffff;
   return 0;
 }
@@ -32,9 +33,7 @@ __host__ __device__ inline int ctrl_init(const Params& p, int w) {
 // Control block reset + queue seeding, launched before every call.  Every
 // word of the control block has exactly one writer here (the thread whose
 // index it is), which stores the word's initial value directly.
-__global__ __launch_bounds__(kThreads) void k_reset(Params p) {
-  const int gid = blockIdx.x * kThreads + threadIdx.x;
-  const int stride = gridDim.x * kThreads;
+DEV void reset_body(const Params& p, int gid, int stride) {
   const int ncw = CW_COUNT * kCtrlStride;
   for (int i = gid; i < ncw; i += stride)
     p.ctrl[i] = (i % kCtrlStride == 0) ? ctrl_init(p, i / kCtrlStride) : 0;
@@ -61,12 +60,25 @@ __global__ __launch_bounds__(kThreads) void k_reset(Params p) {
   }
 }
 
+__global__ __launch_bounds__(kThreads) void k_reset(Params p) {
+  reset_body(p, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+}
+
+// The same for several layers at once (blockIdx.y = layer; parameter blocks
+// in device memory, read through the constant address space).
+__global__ __launch_bounds__(kThreads) void k_reset_layers(const Params* layers) {
+  ConstParams* lp = (ConstParams*)layers;
+  const Params& p = *(const Params*)(lp + blockIdx.y);
+  reset_body(p, blockIdx.x * kThreads + threadIdx.x, gridDim.x * kThreads);
+}
+
 }  // namespace moe
 
 namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxWorkersBound = 4096;  // queue slack for the largest grid
+constexpr int kMaxLayers = 1024;        // layers per moe_layers call
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -510,6 +522,109 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->cost_gather_bytes_per_worker = L.p.cm_cu_bw;
   info->cost_hbm_bytes = L.p.cm_hbm_bw;
   info->bands = L.p.bands;
+  return MOE_OK;
+}
+
+// Several layers: the parameter blocks first, then each layer's workspace.
+size_t layers_params_bytes(int n) { return align_up(sizeof(Params) * (size_t)n); }
+
+size_t moe_layers_workspace_size(const moe_desc* d, int n) {
+  if (!d || n < 1 || n > kMaxLayers) return 0;
+  size_t total = layers_params_bytes(n);
+  for (int l = 0; l < n; ++l) {
+    const size_t b = moe_workspace_size(d + l);
+    if (b == 0) return 0;
+    total += align_up(b);
+  }
+  return total;
+}
+
+int moe_layers(const moe_desc* d, int n, const void* const* x, const moe_weights* w,
+               float* const* y, const moe_routing* routing, void* workspace, size_t ws_bytes,
+               void* stream) {
+  if (!d || n < 1 || n > kMaxLayers || !x || !w || !y) return MOE_ERR_ARG;
+  const size_t need = moe_layers_workspace_size(d, n);
+  if (need == 0) return MOE_ERR_ARG;
+  if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  size_t off = layers_params_bytes(n);
+  std::vector<Params> ps;
+  std::vector<int> which;
+  ps.reserve(n);
+  which.reserve(n);
+  bool one_launch = true;
+  for (int l = 0; l < n; ++l) {
+    const size_t wl = align_up(moe_workspace_size(d + l));
+    Layout L;
+    int rc = fill_params(d + l, &L, base + off, wl);
+    if (rc) return rc;
+    off += wl;
+    if (d[l].T == 0) continue;
+    const moe_weights* wt = w + l;
+    if (!x[l] || !y[l] || !wt->w_router || !wt->w_gate || !wt->w_up || !wt->w_down)
+      return MOE_ERR_ARG;
+    if (d[l].n_shared > 0 && (!wt->ws_gate || !wt->ws_up || !wt->ws_down)) return MOE_ERR_ARG;
+    Params& p = L.p;
+    p.x = x[l];
+    p.wr = wt->w_router;
+    p.bias = wt->router_bias;
+    p.wg = wt->w_gate;
+    p.wu = wt->w_up;
+    p.wd = wt->w_down;
+    p.sg = wt->ws_gate;
+    p.su = wt->ws_up;
+    p.sd = wt->ws_down;
+    p.y = y[l];
+    if (d[l].mode != MOE_DYNAMIC || d[l].dtype != d[0].dtype) one_launch = false;
+    if (!ps.empty() && p.workers != ps[0].workers) one_launch = false;
+    ps.push_back(p);
+    which.push_back(l);
+  }
+  if (ps.empty()) return MOE_OK;
+  if (!one_launch) {
+    // the baselines (and mixed element types) run layer by layer
+    for (size_t i = 0; i < ps.size(); ++i) {
+      int rc = launch_layer(d + which[i], ps[i], s);
+      if (rc) return rc;
+    }
+  } else {
+    // parameter blocks to the device (pageable source: the copy is staged
+    // before the call returns), then one persistent launch per run of
+    // consecutive layers with the same combine mode
+    Params* dev_ps = reinterpret_cast<Params*>(base);
+    HIP_OK(hipMemcpyAsync(dev_ps, ps.data(), sizeof(Params) * ps.size(), hipMemcpyHostToDevice, s));
+    const bool bf16 = d[which[0]].dtype == MOE_BF16;
+    size_t a = 0;
+    while (a < ps.size()) {
+      size_t b = a + 1;
+      while (b < ps.size() && ps[b].comb_scatter == ps[a].comb_scatter) ++b;
+      long long qmax = 0;
+      for (size_t i = a; i < b; ++i) qmax = std::max<long long>(qmax, (long long)kNumQueues * ps[i].q_cap);
+      const int reset_blocks = (int)std::min<long long>(1024, (qmax + kThreads - 1) / kThreads + 1);
+      hipLaunchKernelGGL(k_reset_layers, dim3(reset_blocks, (unsigned)(b - a)), dim3(kThreads), 0, s,
+                         dev_ps + a);
+      HIP_OK(hipGetLastError());
+      const bool scat = ps[a].comb_scatter != 0;
+      HIP_OK(bf16 ? launch_dynamic_layers_bf16(scat, dev_ps + a, (int)(b - a), ps[a].workers, s)
+                  : launch_dynamic_layers_f32(scat, dev_ps + a, (int)(b - a), ps[a].workers, s));
+      a = b;
+    }
+  }
+  for (size_t i = 0; i < ps.size(); ++i) {
+    if (!routing) break;
+    int rc = copy_routing(d + which[i], ps[i], routing + which[i], s);
+    if (rc) return rc;
+  }
+  if (d[0].flags & MOE_FLAG_CHECK) {
+    HIP_OK(hipStreamSynchronize(s));
+    for (size_t i = 0; i < ps.size(); ++i) {
+      int err = 0;
+      HIP_OK(hipMemcpy(&err, reinterpret_cast<const char*>(ps[i].ctrl) + sizeof(int) * CW_ERROR * kCtrlStride,
+                       sizeof(int), hipMemcpyDeviceToHost));
+      if (err) return err;
+    }
+  }
   return MOE_OK;
 }
 

@@ -32,29 +32,33 @@ __host__ __device__ inline int task_kind(int id) { return id >> kKindShift; }
 __host__ __device__ inline int task_payload(int id) { return id & kPayloadMask; }
 
 // Ready queues.
-enum Queue : int { QA = 0, QM = 1, QC = 2, kNumQueues = 3 };
+// Ready queues.  QA: router and position tiles; QM: permute (gather) tasks;
+// QC: new expert work (UP tiles, shared-expert UP tiles); QH: continuation
+// work (DOWN tiles, shared DOWN tiles, combine and NORM tasks), taken before
+// QC so that started row tiles finish first.
+enum Queue : int { QA = 0, QM = 1, QC = 2, QH = 3, kNumQueues = 4 };
 
 // Control words; each sits on its own 128-byte line (index * kCtrlStride).
 enum CtrlWord : int {
   CW_HEAD = 0,         // + queue
-  CW_TAIL = 3,         // + queue
-  CW_TOTAL = 6,        // + queue: tasks that will ever enter the queue
-  CW_ROUTE_DONE = 9,
-  CW_POS_DONE = 10,
-  CW_SPLIT_READY = 11, // 1 once the task builder has published its tables
-  CW_WMEM = 12,        // memory-bound worker count chosen by the cost model
-  CW_ROLE = 13,        // role tickets handed out after the routing phase
-  CW_TICKET = 14,      // worker tickets (dynamic worker ids)
-  CW_ERROR = 15,       // first device error code
-  CW_NMT = 16,         // expert row tiles
-  CW_NPERM = 17,       // permute tasks
-  CW_BAR_COUNT = 18,   // grid barrier (static mode)
-  CW_BAR_GEN = 19,
-  CW_TRACE = 20,       // trace cursor
-  CW_UHEAD = 21,       // + XCD: per-XCD UP queues (XCD affinity)
-  CW_UTAIL = 29,       // + XCD
-  CW_UTOTAL = 37,      // + XCD
-  CW_COUNT = 45
+  CW_TAIL = 4,         // + queue
+  CW_TOTAL = 8,        // + queue: tasks that will ever enter the queue
+  CW_ROUTE_DONE = 12,
+  CW_POS_DONE = 13,
+  CW_SPLIT_READY = 14, // 1 once the task builder has published its tables
+  CW_WMEM = 15,        // memory-bound worker count chosen by the cost model
+  CW_ROLE = 16,        // role tickets handed out after the routing phase
+  CW_TICKET = 17,      // worker tickets (dynamic worker ids)
+  CW_ERROR = 18,       // first device error code
+  CW_NMT = 19,         // expert row tiles
+  CW_NPERM = 20,       // permute tasks
+  CW_BAR_COUNT = 21,   // grid barrier (static mode)
+  CW_BAR_GEN = 22,
+  CW_TRACE = 23,       // trace cursor
+  CW_UHEAD = 24,       // + XCD: per-XCD UP queues (XCD affinity)
+  CW_UTAIL = 32,       // + XCD
+  CW_UTOTAL = 40,      // + XCD
+  CW_COUNT = 48
 };
 constexpr int kXcds = 8;   // MI355X: 8 XCDs, each with its own L2
 constexpr int kMaxBands = 4;  // token bands of the row-tile order

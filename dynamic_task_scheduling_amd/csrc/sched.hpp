@@ -35,6 +35,11 @@ constexpr int kFlagPhaseSync = 0x4;
 constexpr int kFlagRefSync = 0x8;
 constexpr int kFlagNoSteal = 0x10;
 constexpr int kFlagXcdAffinity = 0x20;
+constexpr int kFlagFifo = 0x40;
+
+// The queue continuation work (DOWN, shared DOWN, combine, NORM) goes to:
+// its own priority queue, or -- MOE_FLAG_FIFO -- the one compute queue.
+DEV int qcont(const Params& p) { return (p.flags & kFlagFifo) ? QC : QH; }
 
 // XCD affinity: the UP task of column tile n goes to the ready queue of XCD
 // n % 8, so the workers of one XCD keep reading the same weight panels
@@ -93,35 +98,66 @@ DEV int take_up(const Params& p) {
   return kClaimExhausted;
 }
 
-DEV int claim(const Params& p, int q, int& pend, bool steal) {
-  if (pend < 0) pend = add_relaxed(cw(p, CW_HEAD + q), 1);
-  const int h = pend;
-  const int* sl = p.slots + (size_t)q * p.q_cap + (h < p.q_cap ? h : 0);
+// Thread 0: claim for queue q.  `pend` keeps a claimed but not yet filled
+// slot of q across calls.  For the compute queue (q == QC) the continuation
+// queue QH (DOWN, shared DOWN, combine, NORM work) comes first: a worker
+// that sees pushed QH work reserves the next QH slot (`pend_h`) by one
+// atomic increment before it takes new QC work, so started row tiles finish,
+// and their token tiles' combines become ready, before new UP work starts.
+// Reservations are never waited on while other work exists: a reserved
+// slot that is not yet filled stays pending while the worker runs its QC
+// work (every claim is an increment that always succeeds -- no
+// compare-and-swap retries on a hot word), and a filled reserved slot is
+// taken first at the next claim.  A worker leaves only when its QC index is
+// past QC's total and QH holds nothing more for it.
+DEV int claim(const Params& p, int q, int& pend, int& pend_h, bool steal) {
+  const bool cont = q == QC && !(p.flags & kFlagFifo);
   const uint64_t t0 = rtc();
   for (;;) {
-    const int v = h < p.q_cap ? ld_relaxed(sl) : 0;
-    const int total = ld_relaxed(cw(p, CW_TOTAL + q));
-    const int err = ld_relaxed(cw(p, CW_ERROR));
-    int mh = 0, mt = 0;
-    if (steal) {
-      mh = ld_relaxed(cw(p, CW_HEAD + QM));
-      mt = ld_relaxed(cw(p, CW_TAIL + QM));
+    int hh = 0, ht = 0, htot = 0, vh = 0;
+    if (cont) {
+      hh = ld_relaxed(cw(p, CW_HEAD + QH));
+      ht = ld_relaxed(cw(p, CW_TAIL + QH));
+      htot = ld_relaxed(cw(p, CW_TOTAL + QH));
+      if (pend_h >= 0) vh = ld_relaxed(p.slots + (size_t)QH * p.q_cap + pend_h);
     }
+    const int err = ld_relaxed(cw(p, CW_ERROR));
+    if (err != 0) return kClaimAbort;
+    if (vh != 0) {                     // the reserved continuation task is there
+      pend_h = -1;
+      return vh - 1;
+    }
+    if (cont && pend_h < 0 && hh < ht && hh < htot) {
+      const int i = add_relaxed(cw(p, CW_HEAD + QH), 1);
+      if (i < htot && i < p.q_cap) {
+        const int v = ld_relaxed(p.slots + (size_t)QH * p.q_cap + i);
+        if (v != 0) return v - 1;
+        pend_h = i;                    // pushed soon, or later: keep it
+      }
+    }
+    if (pend < 0) pend = add_relaxed(cw(p, CW_HEAD + q), 1);
+    const int h = pend;
+    const int v = h < p.q_cap ? ld_relaxed(p.slots + (size_t)q * p.q_cap + h) : 0;
+    const int total = ld_relaxed(cw(p, CW_TOTAL + q));
     if (v != 0) {            // a filled slot is always below the total
       pend = -1;
       return v - 1;
     }
-    if (h >= total) {
+    // no more QC work for this worker; QH: nothing reserved and nothing left
+    if (h >= total && (!cont || (pend_h < 0 && ld_relaxed(cw(p, CW_HEAD + QH)) >= htot))) {
       pend = -1;
       return kClaimExhausted;
     }
-    if (err != 0) return kClaimAbort;
-    if (steal && mh < mt) {
-      // pushed permute tasks are waiting: take one (the push is one burst,
-      // so a slot below the published total is filled now or very soon)
-      const int hm = add_relaxed(cw(p, CW_HEAD + QM), 1);
-      if (hm < ld_relaxed(cw(p, CW_TOTAL + QM)) && hm < p.q_cap)
-        return wait_slot(p, p.slots + (size_t)QM * p.q_cap + hm);
+    if (steal) {
+      const int mh = ld_relaxed(cw(p, CW_HEAD + QM));
+      const int mt = ld_relaxed(cw(p, CW_TAIL + QM));
+      if (mh < mt) {
+        // pushed permute tasks are waiting: take one (the push is one burst,
+        // so a slot below the published total is filled now or very soon)
+        const int hm = add_relaxed(cw(p, CW_HEAD + QM), 1);
+        if (hm < ld_relaxed(cw(p, CW_TOTAL + QM)) && hm < p.q_cap)
+          return wait_slot(p, p.slots + (size_t)QM * p.q_cap + hm);
+      }
     }
     if (q == QC && affinity(p)) {
       const int t = take_up(p);
@@ -234,12 +270,13 @@ DEV void trace_mark(const Params& p, int phase, int worker, uint64_t t0, uint64_
 // scatter-added into y themselves, its NORM task.
 DEV void push_tile_ready(const Params& p, int rt, bool scat) {
   const int n = scat ? 1 : p.n_cc;
-  const int base = add_relaxed(cw(p, CW_TAIL + QC), n);
+  const int q = qcont(p);
+  const int base = add_relaxed(cw(p, CW_TAIL + q), n);
   if (base + n > p.q_cap) {
     set_error(p, 6 /* MOE_ERR_CAPACITY */);
     return;
   }
-  int* sl = p.slots + (size_t)QC * p.q_cap + base;
+  int* sl = p.slots + (size_t)q * p.q_cap + base;
   if (scat) {
     st_relaxed(sl, make_task(TK_NORM, rt) + 1);
     return;
@@ -286,13 +323,16 @@ struct Sched {
     const int n_mt = ld_relaxed(cw(p, CW_NMT));
     const int n_perm = ld_relaxed(cw(p, CW_NPERM));
     const bool split = p.split_policy != 2;
+    const bool fifo = (p.flags & kFlagFifo) != 0;
     const int n_up_qc = affinity(p) ? 0 : n_mt * p.n_up_n;
-    const int n_comp = n_up_qc + n_mt * p.n_down_n * p.splitk + p.n_sup + p.n_sdown +
+    const int n_cont = n_mt * p.n_down_n * p.splitk + p.n_sdown +
                        (SCAT ? 0 : p.n_rt * p.n_cc) + (p.fuse_norm ? p.n_rt : 0);
+    const int n_comp = n_up_qc + p.n_sup + (fifo ? n_cont : 0);
     publish_fence();
     __syncthreads();
     if (tidx() == 0) {
       st_relaxed(cw(p, CW_TOTAL + QM), split ? n_perm : 0);
+      st_relaxed(cw(p, CW_TOTAL + QH), fifo ? 0 : n_cont);
       st_relaxed(cw(p, CW_TOTAL + QC), n_comp + (split ? 0 : n_perm));
       if (affinity(p))
         for (int x = 0; x < kXcds; ++x)
@@ -306,8 +346,9 @@ struct Sched {
     for (int i = tidx(); i < nsm; i += kThreads) {
       if (add_relaxed(p.cnt_sdown + i, -1) == 1) {
         int* sl = nullptr;
-        const int base = add_relaxed(cw(p, CW_TAIL + QC), p.n_down_n);
-        if (base + p.n_down_n <= p.q_cap) sl = p.slots + (size_t)QC * p.q_cap + base;
+        const int q = qcont(p);
+        const int base = add_relaxed(cw(p, CW_TAIL + q), p.n_down_n);
+        if (base + p.n_down_n <= p.q_cap) sl = p.slots + (size_t)q * p.q_cap + base;
         else set_error(p, 6);
         if (sl) {
           publish_fence();
@@ -406,7 +447,7 @@ struct Sched {
         *t_body = rtc();
         const int ks = slice_of(n, p.n_up_n, p.splitk);
         if (arrive_last(p.cnt_down + mt * p.splitk + ks, -1, 1, s_tmp) && dyn)
-          push_burst(p, QC, p.n_down_n, s_tmp, [&](int nn) {
+          push_burst(p, qcont(p), p.n_down_n, s_tmp, [&](int nn) {
             return make_task(TK_DOWN, (mt * p.n_down_n + nn) * p.splitk + ks);
           });
         break;
@@ -429,7 +470,7 @@ struct Sched {
         S::shared_up(p, sm / p.n_smt, sm % p.n_smt, n, smem);
         *t_body = rtc();
         if (arrive_last(p.cnt_sdown + sm, -1, 1, s_tmp) && dyn)
-          push_burst(p, QC, p.n_down_n, s_tmp,
+          push_burst(p, qcont(p), p.n_down_n, s_tmp,
                      [&](int nn) { return make_task(TK_SDOWN, sm * p.n_down_n + nn); });
         break;
       }
@@ -446,7 +487,7 @@ struct Sched {
         *t_body = rtc();
         // the last column chunk of a token tile releases its NORM task
         if (p.fuse_norm && arrive_last(p.cnt_norm + pl / p.n_cc, -1, 1, s_tmp) && dyn)
-          push_burst(p, QC, 1, s_tmp, [&](int) { return make_task(TK_NORM, pl / p.n_cc); });
+          push_burst(p, qcont(p), 1, s_tmp, [&](int) { return make_task(TK_NORM, pl / p.n_cc); });
         break;
       }
       case TK_NORM: {
@@ -508,29 +549,31 @@ DEV const Params& params_view(const Params& p) {
   return *reinterpret_cast<const Params*>(reinterpret_cast<const char*>(&p) + off);
 }
 
-// SCAT: the layer's combine mode as a compile-time constant, so each
-// instantiation holds only its own DOWN epilogue and combine code (the
-// persistent kernel's register allocation covers every task type at once).
-// The launch parameters stay in the kernel-argument segment (read-only,
-// loaded into scalar registers on use); the combine mode is passed down as a
-// template argument instead of being written into a private copy.
+// One worker's share of one layer: claim, run, publish, until the layer's
+// queues are exhausted (or a device error stops it).  The caller provides
+// the workgroup's LDS.  SCAT: the layer's combine mode as a compile-time
+// constant, so each instantiation holds only its own DOWN epilogue and
+// combine code (the persistent kernel's register allocation covers every
+// task type at once).  The launch parameters are read through params_view
+// on every pass; the combine mode is a template argument instead of being
+// written into a private copy of them.
 template <typename Elem, bool SCAT>
-__global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
-  __shared__ int s_tmp[4];
-  __shared__ int s_worker;
-  if (tidx() == 0) s_worker = add_relaxed(cw(p, CW_TICKET), 1);
+DEV void dynamic_worker(const Params& p, char* smem, int* s_tmp, int* s_worker) {
+  if (tidx() == 0) *s_worker = add_relaxed(cw(p, CW_TICKET), 1);
   int q = QA;
   int pend = -1;   // thread 0: claimed but not yet filled slot of queue q
-  const bool steal = p.split_policy != 2 && !(p.flags & kFlagNoSteal);
+  int pend_h = -1; // thread 0: reserved but not yet filled continuation slot
   for (;;) {
+    // every pass reads the parameters afresh (see params_view)
+    const Params& pv = params_view(p);
+    const bool steal = pv.split_policy != 2 && !(pv.flags & kFlagNoSteal);
     uint64_t t_req = rtc();
     if (tidx() == 0) {
-      int v = claim(p, q, pend, steal && q == QC);
+      int v = claim(pv, q, pend, pend_h, steal && q == QC);
       int role = q;
       // routing phase over for this worker: shared-expert tiles until the
       // split is published, then the role the split assigns
-      if (v == kClaimExhausted && q == QA) v = wait_split(p, &role);
+      if (v == kClaimExhausted && q == QA) v = wait_split(pv, &role);
       s_tmp[1] = v;
       s_tmp[2] = role;
     }
@@ -547,8 +590,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
     consume_fence();
     const uint64_t t_start = rtc();
     uint64_t t_body;
-    Sched<Elem, SCAT>::run(params_view(p), v, smem, s_tmp, true, &t_body, s_worker);
-    trace_record(p, v, s_worker, t_req, t_start, t_body);
+    const int worker = uniform(*s_worker);
+    Sched<Elem, SCAT>::run(pv, v, smem, s_tmp, true, &t_body, worker);
+    trace_record(pv, v, worker, t_req, t_start, t_body);
+  }
+}
+
+template <typename Elem, bool SCAT>
+__global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
+  __shared__ int s_tmp[4];
+  __shared__ int s_worker;
+  dynamic_worker<Elem, SCAT>(p, smem, s_tmp, &s_worker);
+}
+
+// Several independent layers in ONE persistent launch (layers[0..n), each
+// with its own control block and tables in its own workspace): a worker
+// that finds layer l's queues exhausted goes straight to layer l + 1's
+// router tiles while the other workers finish layer l's last tasks, so one
+// layer's routing overlaps the previous layer's expert tail instead of
+// waiting for a kernel boundary (the follow-up direction of
+// m.xxqk.cn/news/657744 section 6.3; the per-layer synchronisation windows
+// of xxqk.cn/news/665650 section 3.3).  The parameter blocks sit in device
+// memory; they are read through the constant address space (scalar loads).
+typedef const __attribute__((address_space(4))) Params ConstParams;
+
+template <typename Elem, bool SCAT>
+__global__ __launch_bounds__(kThreads, 1) void k_dynamic_layers(const Params* layers, int n) {
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
+  __shared__ int s_tmp[4];
+  __shared__ int s_worker;
+  ConstParams* lp = (ConstParams*)layers;
+  for (int l = 0; l < n; ++l) {
+    const Params& p = *(const Params*)(lp + l);
+    dynamic_worker<Elem, SCAT>(p, smem, s_tmp, &s_worker);
+    __syncthreads();
   }
 }
 

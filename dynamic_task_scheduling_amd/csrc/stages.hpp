@@ -43,7 +43,7 @@ DEV void set_error(const Params& p, int code) {
 DEV void trace_step(const Params& p, int phase, int worker, uint64_t t0, uint64_t t1) {
   if (p.trace == nullptr || tidx() != 0) return;
   asm volatile("" : "+s"(phase));
-  const int i = add_relaxed(p.ctrl + 20 /* CW_TRACE */ * kCtrlStride, 1);
+  const int i = add_relaxed(p.ctrl + CW_TRACE * kCtrlStride, 1);
   if (i < p.trace_cap) {
     uint64_t* r = p.trace + (size_t)i * 4;
     r[0] = t0;
@@ -376,7 +376,7 @@ struct Stages {
     int inc = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(inc, o);
+      const int u = wave_up(inc, o);
       if (lane >= o) inc += u;
     }
     if (lane == 63) s_w[wave] = inc;
@@ -397,7 +397,7 @@ struct Stages {
   static DEV float block_sum(float v, float* s_w) {
     const int lane = tidx() & 63, wave = tidx() >> 6;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    for (int o = 32; o >= 1; o >>= 1) v += wave_xor(v, o);
     if (lane == 0) s_w[wave] = v;
     __syncthreads();
     const float t = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
@@ -979,14 +979,17 @@ struct Stages {
     const int col0 = cc * p.comb_cols;
     const size_t slice = (size_t)p.T * k * p.d;
     const int n = rows * c4;
-    // two (token, float4) items per thread per pass, every load of both
-    // issued before any sum (a combine task is a latency-bound gather)
-    for (int i0 = tidx(); i0 < n; i0 += 2 * kThreads) {
-      float4 v[2][kMaxK];
-      float4 sh[2][4];
-      float4 rs[2];
+    // A combine task is a latency-bound gather and the persistent kernel runs
+    // one workgroup per CU, so each thread keeps many loads in flight: CU
+    // (token, float4) items per pass, the first K slice of every slot of all
+    // of them issued before any is used, then each further K slice as one
+    // burst, then the sums; the shared experts' rows and the residual follow
+    // as one more burst (the expert rows' registers are free by then).
+    constexpr int CU = 2;
+    for (int i0 = tidx(); i0 < n; i0 += CU * kThreads) {
+      float4 v[CU][kMaxK];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < CU; ++u) {
         const int i = i0 + u * kThreads;
         const int r = i / c4, col = col0 + (i % c4) * 4;
 #pragma unroll
@@ -994,55 +997,78 @@ struct Stages {
           v[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (i < n && j < k) {
             const int pos = s_pos[r * k + j];
+            if (pos >= 0) v[u][j] = *reinterpret_cast<const float4*>(p.O + (size_t)pos * p.d + col);
+          }
+        }
+      }
+      // further K slices (only layers with a DOWN split-K and combine tasks)
+      for (int ks = 1; ks < p.splitk; ++ks) {
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int i = i0 + u * kThreads;
+          const int r = i / c4, col = col0 + (i % c4) * 4;
+#pragma unroll
+          for (int j = 0; j < kMaxK; ++j) {
+            const int pos = (i < n && j < k) ? s_pos[r * k + j] : -1;
             if (pos >= 0) {
-              const float* o = p.O + (size_t)pos * p.d + col;
-              float4 a = *reinterpret_cast<const float4*>(o);
-              for (int ks = 1; ks < p.splitk; ++ks) {
-                const float4 b = *reinterpret_cast<const float4*>(o + ks * slice);
-                a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-              }
-              v[u][j] = a;
+              const float4 b = *reinterpret_cast<const float4*>(p.O + ks * slice + (size_t)pos * p.d + col);
+              v[u][j].x += b.x; v[u][j].y += b.y; v[u][j].z += b.z; v[u][j].w += b.w;
             }
           }
         }
+      }
+      // weighted sum over the token's kept slots, in slot order
+      float4 acc[CU];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          sh[u][s] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (i < n && s < p.n_shared)
-            sh[u][s] = *reinterpret_cast<const float4*>(p.Ys + ((size_t)s * p.T + t0 + r) * p.d + col);
+      for (int u = 0; u < CU; ++u) {
+        const int i = i0 + u * kThreads;
+        const int r = i / c4;
+        acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+          if (i < n && j < k && s_pos[r * k + j] >= 0) {
+            const float wj = s_w[r * k + j];
+            acc[u].x += wj * v[u][j].x;
+            acc[u].y += wj * v[u][j].y;
+            acc[u].z += wj * v[u][j].z;
+            acc[u].w += wj * v[u][j].w;
+          }
         }
-        rs[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < n && p.resid)
-          rs[u] = *reinterpret_cast<const float4*>(p.resid + (size_t)(t0 + r) * p.d + col);
+      }
+      // shared experts (weight 1), then the residual (h = residual + MoE(x))
+      if (p.n_shared > 0 || p.resid) {
+        float4 ex[CU][5];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int i = i0 + u * kThreads;
+          const int r = i / c4, col = col0 + (i % c4) * 4;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            ex[u][s] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (i < n && s < p.n_shared)
+              ex[u][s] = *reinterpret_cast<const float4*>(p.Ys + ((size_t)s * p.T + t0 + r) * p.d + col);
+          }
+          ex[u][4] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (i < n && p.resid)
+            ex[u][4] = *reinterpret_cast<const float4*>(p.resid + (size_t)(t0 + r) * p.d + col);
+        }
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+#pragma unroll
+          for (int s = 0; s < 5; ++s) {
+            acc[u].x += ex[u][s].x; acc[u].y += ex[u][s].y; acc[u].z += ex[u][s].z; acc[u].w += ex[u][s].w;
+          }
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < CU; ++u) {
         const int i = i0 + u * kThreads;
         if (i >= n) continue;
         const int r = i / c4, col = col0 + (i % c4) * 4;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-          if (j < k && s_pos[r * k + j] >= 0) {
-            const float wj = s_w[r * k + j];
-            acc.x += wj * v[u][j].x;
-            acc.y += wj * v[u][j].y;
-            acc.z += wj * v[u][j].z;
-            acc.w += wj * v[u][j].w;
-          }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s < p.n_shared) {
-            acc.x += sh[u][s].x; acc.y += sh[u][s].y; acc.z += sh[u][s].z; acc.w += sh[u][s].w;
-          }
-        }
-        // the residual last (the block output h = residual + MoE(x))
-        acc.x += rs[u].x; acc.y += rs[u].y; acc.z += rs[u].z; acc.w += rs[u].w;
         // write-through: a NORM task on another XCD reads these rows
         st_wt16(p.y + (size_t)(t0 + r) * p.d, (uint32_t)col * 4u,
-                make_uint4(__float_as_uint(acc.x), __float_as_uint(acc.y), __float_as_uint(acc.z),
-                           __float_as_uint(acc.w)));
+                make_uint4(__float_as_uint(acc[u].x), __float_as_uint(acc[u].y),
+                           __float_as_uint(acc[u].z), __float_as_uint(acc[u].w)));
       }
     }
     __syncthreads();
@@ -1073,7 +1099,7 @@ struct Stages {
         ss += v.w * v.w;
       }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      for (int o = 32; o >= 1; o >>= 1) ss += wave_xor(ss, o);
       const float scale = 1.0f / sqrtf(ss / (float)p.d + p.norm_eps);
       Elem* out = reinterpret_cast<Elem*>(p.y_norm) + (size_t)(t0 + r) * p.d;
       for (int c = lane * 4; c < p.d; c += 256) {

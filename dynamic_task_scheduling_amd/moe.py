@@ -235,6 +235,53 @@ class MoELayer:
                                                    _stream(self.device)))
 
 
+class MoELayers:
+    """Several independent MoE layers run by ONE call of moe_layers (one
+    persistent launch when all are dynamic-mode layers of one element type).
+    layers: MoELayer objects (their descriptors and weights are used; their
+    own workspaces are not)."""
+
+    def __init__(self, layers, workspace: Optional[torch.Tensor] = None):
+        self.layers = list(layers)
+        n = len(self.layers)
+        self.device = self.layers[0].device
+        self._descs = (Desc * n)(*[L.desc for L in self.layers])
+        self._w = (Weights * n)(*[L._w for L in self.layers])
+        size = int(lib().moe_layers_workspace_size(self._descs, n))
+        if size == 0:
+            raise MoEError(1, "invalid descriptors")
+        if workspace is None or workspace.numel() < size:
+            workspace = torch.empty((size,), dtype=torch.uint8, device=self.device)
+        self.workspace = workspace
+
+    def __call__(self, xs, ys=None, routings=None, check_errors: bool = False):
+        n = len(self.layers)
+        if ys is None:
+            ys = [torch.empty((L.shape.T, L.shape.d), dtype=torch.float32, device=self.device)
+                  for L in self.layers]
+        for L, x, y in zip(self.layers, xs, ys):
+            s = L.shape
+            _check_tensor("x", x, (s.T, s.d), _elem_dtype(s), self.device)
+            _check_tensor("y", y, (s.T, s.d), torch.float32, self.device)
+        descs = self._descs
+        if check_errors:
+            descs = (Desc * n)(*[Desc.from_buffer_copy(L.desc) for L in self.layers])
+            descs[0].flags |= _abi.FLAG_CHECK
+        xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+        yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+        rt = None
+        if routings is not None:
+            arr = (Routing * n)()
+            for i, r in enumerate(routings):
+                for name in RoutingResult._fields:
+                    setattr(arr[i], name, getattr(r, name).data_ptr())
+            rt = arr
+        with torch.cuda.device(self.device):
+            check(lib().moe_layers(descs, n, xp, self._w, yp, rt, _ptr(self.workspace),
+                                   self.workspace.numel(), _stream(self.device)))
+        return ys
+
+
 def route_from_logits(shape: LayerShape, logits: torch.Tensor,
                       workspace: Optional[torch.Tensor] = None,
                       check_errors: bool = False) -> RoutingResult:

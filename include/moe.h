@@ -96,6 +96,7 @@ typedef enum {
 #define MOE_FLAG_REF_SYNC 0x8u   /* static mode: per-task counter waits instead of barriers */
 #define MOE_FLAG_NO_STEAL 0x10u  /* dynamic split: compute workers never take permute tasks */
 #define MOE_FLAG_XCD_AFFINITY 0x20u /* dynamic: UP tasks of column tile n on XCD n % 8's queue */
+#define MOE_FLAG_FIFO 0x40u      /* dynamic: one compute queue, no priority for continuation work */
 
 /* Return codes. */
 #define MOE_OK 0
@@ -263,6 +264,29 @@ int moe_layer_norm(const moe_desc* desc, const void* x, const moe_weights* weigh
  * results and other errors as moe_layer. */
 int moe_layer_no_alloc(const moe_desc* desc, const void* x, const moe_weights* weights,
                        float* y, const moe_routing* routing, void* hip_stream);
+
+/* Bytes of workspace moe_layers needs for these n_layers descriptors (0 on
+ * a bad descriptor or n_layers outside 1..1024): the layers' parameter
+ * blocks, then each layer's moe_workspace_size, 256-byte aligned. */
+size_t moe_layers_workspace_size(const moe_desc* descs, int n_layers);
+
+/* Several independent MoE layers (descs[l], x[l], weights[l], y[l]; arrays of
+ * n_layers; routing: NULL or an array of n_layers, each entry as in
+ * moe_layer) in ONE persistent launch when every layer uses MOE_DYNAMIC and
+ * the same element type: a worker that runs out of layer l's work goes on to
+ * layer l + 1's router tiles while others finish layer l, so each layer's
+ * routing overlaps the previous layer's expert tail (the multi-layer
+ * follow-up of m.xxqk.cn/news/657744 section 6.3, against the per-layer
+ * synchronisation windows of xxqk.cn/news/665650 section 3.3).  Layers whose
+ * combine mode differs from the previous layer's start a new launch; the
+ * baseline modes run layer by layer.  Results equal n calls of moe_layer.
+ * The parameter blocks are copied from host memory with hipMemcpyAsync before
+ * the launch (so this call is not meant for graph capture).  Errors as
+ * moe_layer; with MOE_FLAG_CHECK in descs[0].flags the first layer's device
+ * error found is returned. */
+int moe_layers(const moe_desc* descs, int n_layers, const void* const* x,
+               const moe_weights* weights, float* const* y, const moe_routing* routing,
+               void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Routing only, from caller-supplied fp32 logits [T, E] (device): top-k,
  * weights, counts, offsets, perm and slot_pos, with the same device code the

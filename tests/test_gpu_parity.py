@@ -351,6 +351,94 @@ def test_xcd_affinity(big_tile, split):
                   flags=_abi.FLAG_XCD_AFFINITY)
 
 
+@pytest.mark.parametrize("fifo", [False, True])
+@pytest.mark.parametrize("bands", [1, 2, 4])
+def test_queue_policy_and_bands(big_tile, fifo, bands):
+    """Continuation-queue priority (default) or one FIFO compute queue, and
+    1, 2 or 4 token bands in the row-tile order: every task once, after its
+    producers, and y bit-identical to the static kernel's (same tiles, same
+    fixed-order combine), checked against the oracle once."""
+    from analysis_util import check_trace
+    from dynamic_task_scheduling_amd import _abi
+    g, n = big_tile
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(BIG_TILE, g, mode="dynamic", trace=trace, timeout_ms=3000, row_tile=256,
+                     combine="tasks", bands=bands, flags=_abi.FLAG_FIFO if fifo else 0)
+    assert layer.info["bands"] == bands
+    y, r = layer(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+    y2 = MoELayer(BIG_TILE, g, mode="static", split="fixed", row_tile=256, combine="tasks",
+                  bands=bands)(g["x"], check_errors=True)
+    assert torch.equal(y, y2)
+    if bands == 4 and not fifo:
+        run_and_check(BIG_TILE, g, n, "dynamic", "cost_model", label="rt256_b4", row_tile=256,
+                      combine="tasks")
+
+
+@pytest.mark.parametrize("combine", ["scatter", "tasks"])
+def test_layers_in_one_launch(combine):
+    """moe_layers: several independent layers of different shapes in one
+    persistent launch; each layer's y bit-identical to its own moe_layer call
+    with combine tasks (fixed-order combine; scatter-add: within fp32
+    summation order), routing tables identical, and every layer within the
+    bf16 tolerance of the oracle.  A T = 0 layer in the middle is skipped."""
+    from dynamic_task_scheduling_amd.moe import MoELayers, alloc_routing
+    shapes = [LayerShape(T=300, d=512, E=16, k=4, f=384, n_shared=1, f_shared=256, zipf_s=1.0),
+              LayerShape(T=1, d=256, E=8, k=2, f=256),
+              LayerShape(T=0, d=256, E=8, k=2, f=256),
+              LayerShape(T=129, d=256, E=32, k=6, f=512, e_begin=8, e_end=24, zipf_s=1.5),
+              LayerShape(T=77, d=512, E=16, k=4, f=384, zipf_s=0.5)]
+    gs = []
+    for i, s in enumerate(shapes):
+        g = gen_inputs(LayerShape(T=max(s.T, 1), d=s.d, E=s.E, k=s.k, f=s.f, e_begin=s.e_begin,
+                                  e_end=s.e_end, n_shared=s.n_shared, f_shared=s.f_shared,
+                                  zipf_s=s.zipf_s), "layers", 60 + i)
+        g["x"] = g["x"][:s.T].contiguous()
+        gs.append(g)
+    layers = [MoELayer(s, g, mode="dynamic", timeout_ms=3000, combine=combine)
+              for s, g in zip(shapes, gs)]
+    stack = MoELayers(layers)
+    routs = [alloc_routing(s, torch.device("cuda")) for s in shapes]
+    ys = stack([g["x"] for g in gs], routings=routs, check_errors=True)
+    torch.cuda.synchronize()
+    for s, g, L, y, r in zip(shapes, gs, layers, ys, routs):
+        if s.T == 0:
+            continue
+        y1, r1 = L(g["x"], return_routing=True, check_errors=True)
+        torch.cuda.synchronize()
+        for f in ("topk_idx", "expert_counts", "offsets", "slot_pos"):
+            assert torch.equal(getattr(r, f), getattr(r1, f))
+        if combine == "tasks":
+            assert torch.equal(y, y1)
+        else:
+            assert (y - y1).abs().max().item() <= 1e-5 * y1.abs().max().item()
+        n = host_inputs(g)
+        ro = oracle.route(r.logits.cpu().numpy(), s.k, s.e_begin, s.local_end)
+        check_routing(r, ro, s)
+        shared = (n["ws_gate"], n["ws_up"], n["ws_down"]) if s.n_shared else None
+        yo = oracle.moe_layer(n["x"], n["w_gate"], n["w_up"], n["w_down"], ro, s.e_begin, shared)
+        compare_y(y.cpu().numpy(), yo, "bf16")
+
+
+def test_layers_in_one_launch_traced():
+    """Each layer's own trace in a multi-layer launch: every task once, after
+    its producers."""
+    from analysis_util import check_trace
+    from dynamic_task_scheduling_amd.moe import MoELayers, alloc_routing
+    g, n = gen_and_host(MID, "mid", 1)
+    g2, _ = gen_and_host(BIG_TILE, "big_tile", 6)
+    traces = [torch.zeros(4 * 20000, dtype=torch.int64, device="cuda") for _ in range(2)]
+    layers = [MoELayer(MID, g, mode="dynamic", trace=traces[0], timeout_ms=3000, combine="tasks"),
+              MoELayer(BIG_TILE, g2, mode="dynamic", trace=traces[1], timeout_ms=3000, row_tile=256,
+                       combine="tasks")]
+    routs = [alloc_routing(MID, torch.device("cuda")), alloc_routing(BIG_TILE, torch.device("cuda"))]
+    MoELayers(layers)([g["x"], g2["x"]], routings=routs, check_errors=True)
+    torch.cuda.synchronize()
+    for t, L, r in zip(traces, layers, routs):
+        check_trace(t.cpu().numpy().reshape(-1, 4).view(np.uint64), L, r)
+
+
 def gen_and_host(shape, tag, seed):
     g = gen_inputs(shape, tag, seed)
     return g, host_inputs(g)
