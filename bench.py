@@ -250,8 +250,8 @@ def ablations(run, steps, warmup):
         ("dynamic/bands=1", "dynamic", "cost_model", 0, 1),
         ("dynamic/bands=2", "dynamic", "cost_model", 0, 2),
         ("dynamic/bands=4", "dynamic", "cost_model", 0, 4),
-        ("dynamic/fifo/bands=1", "dynamic", "cost_model", _abi.FLAG_FIFO, 1),
-        ("dynamic/fifo/bands=4", "dynamic", "cost_model", _abi.FLAG_FIFO, 4),
+        ("dynamic/cont_priority/bands=1", "dynamic", "cost_model", _abi.FLAG_CONT_PRIORITY, 1),
+        ("dynamic/cont_priority/bands=4", "dynamic", "cost_model", _abi.FLAG_CONT_PRIORITY, 4),
         ("static/sync=phase_barrier", "static", "fixed", 0, None),
         ("static/sync=ref_count", "static", "fixed", _abi.FLAG_REF_SYNC, None),
         ("multi_kernel", "multi_kernel", "none", 0, None),

@@ -15,6 +15,7 @@ COMBINES = {"auto": 0, "scatter": 1, "tasks": 2}
 FLAG_CHECK, FLAG_TRACE, FLAG_PHASE_SYNC, FLAG_REF_SYNC, FLAG_NO_STEAL = 0x1, 0x2, 0x4, 0x8, 0x10
 FLAG_XCD_AFFINITY = 0x20
 FLAG_FIFO = 0x40
+FLAG_CONT_PRIORITY = 0x80
 
 ERRORS = {
     0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_WORKSPACE", 3: "MOE_ERR_UNSUPPORTED",

@@ -36,10 +36,18 @@ constexpr int kFlagRefSync = 0x8;
 constexpr int kFlagNoSteal = 0x10;
 constexpr int kFlagXcdAffinity = 0x20;
 constexpr int kFlagFifo = 0x40;
+constexpr int kFlagContPriority = 0x80;
 
 // The queue continuation work (DOWN, shared DOWN, combine, NORM) goes to:
-// its own priority queue, or -- MOE_FLAG_FIFO -- the one compute queue.
-DEV int qcont(const Params& p) { return (p.flags & kFlagFifo) ? QC : QH; }
+// the one compute queue, in push order (default), or -- with
+// MOE_FLAG_CONT_PRIORITY and without MOE_FLAG_FIFO -- its own queue, which
+// workers serve before new compute-queue work.  Measured on the layer shapes
+// here, one FIFO queue is the faster policy (the priority queue holds the
+// UP tiles behind a long DOWN backlog), so it is the default.
+DEV bool cont_priority(const Params& p) {
+  return (p.flags & kFlagContPriority) != 0 && (p.flags & kFlagFifo) == 0;
+}
+DEV int qcont(const Params& p) { return cont_priority(p) ? QH : QC; }
 
 // XCD affinity: the UP task of column tile n goes to the ready queue of XCD
 // n % 8, so the workers of one XCD keep reading the same weight panels
@@ -111,7 +119,7 @@ DEV int take_up(const Params& p) {
 // taken first at the next claim.  A worker leaves only when its QC index is
 // past QC's total and QH holds nothing more for it.
 DEV int claim(const Params& p, int q, int& pend, int& pend_h, bool steal) {
-  const bool cont = q == QC && !(p.flags & kFlagFifo);
+  const bool cont = q == QC && cont_priority(p);
   const uint64_t t0 = rtc();
   for (;;) {
     int hh = 0, ht = 0, htot = 0, vh = 0;
@@ -323,7 +331,7 @@ struct Sched {
     const int n_mt = ld_relaxed(cw(p, CW_NMT));
     const int n_perm = ld_relaxed(cw(p, CW_NPERM));
     const bool split = p.split_policy != 2;
-    const bool fifo = (p.flags & kFlagFifo) != 0;
+    const bool fifo = !cont_priority(p);
     const int n_up_qc = affinity(p) ? 0 : n_mt * p.n_up_n;
     const int n_cont = n_mt * p.n_down_n * p.splitk + p.n_sdown +
                        (SCAT ? 0 : p.n_rt * p.n_cc) + (p.fuse_norm ? p.n_rt : 0);

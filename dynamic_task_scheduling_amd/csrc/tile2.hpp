@@ -63,11 +63,13 @@ DEV void wait_vmcnt() {
 // asm declares no memory clobber; ordering against LDS reads comes from the
 // barrier + compiler fence in the K loop.
 DEV void dma16(const void* gptr, uint32_t lds_base) {
-  // m0 is a reserved register: save and restore it around the load.
+  // m0 is a reserved register: save and restore it around the load.  s_nop 0
+  // is the one wait state an SALU write of M0 needs before an LDS DMA.
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -90,6 +92,7 @@ DEV void dma16s(uint32_t voff, uint64_t base, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)

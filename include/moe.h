@@ -96,7 +96,10 @@ typedef enum {
 #define MOE_FLAG_REF_SYNC 0x8u   /* static mode: per-task counter waits instead of barriers */
 #define MOE_FLAG_NO_STEAL 0x10u  /* dynamic split: compute workers never take permute tasks */
 #define MOE_FLAG_XCD_AFFINITY 0x20u /* dynamic: UP tasks of column tile n on XCD n % 8's queue */
-#define MOE_FLAG_FIFO 0x40u      /* dynamic: one compute queue, no priority for continuation work */
+#define MOE_FLAG_FIFO 0x40u      /* dynamic: one compute queue in push order (the default;
+                                    overrides MOE_FLAG_CONT_PRIORITY)       */
+#define MOE_FLAG_CONT_PRIORITY 0x80u /* dynamic: continuation work (DOWN, shared DOWN, combine,
+                                        NORM) in its own queue, served first */
 
 /* Return codes. */
 #define MOE_OK 0

@@ -354,16 +354,17 @@ def test_xcd_affinity(big_tile, split):
 @pytest.mark.parametrize("fifo", [False, True])
 @pytest.mark.parametrize("bands", [1, 2, 4])
 def test_queue_policy_and_bands(big_tile, fifo, bands):
-    """Continuation-queue priority (default) or one FIFO compute queue, and
-    1, 2 or 4 token bands in the row-tile order: every task once, after its
-    producers, and y bit-identical to the static kernel's (same tiles, same
-    fixed-order combine), checked against the oracle once."""
+    """One FIFO compute queue (default) or the continuation-priority queue,
+    and 1, 2 or 4 token bands in the row-tile order: every task once, after
+    its producers, and y bit-identical to the static kernel's (same tiles,
+    same fixed-order combine), checked against the oracle once."""
     from analysis_util import check_trace
     from dynamic_task_scheduling_amd import _abi
     g, n = big_tile
     trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
     layer = MoELayer(BIG_TILE, g, mode="dynamic", trace=trace, timeout_ms=3000, row_tile=256,
-                     combine="tasks", bands=bands, flags=_abi.FLAG_FIFO if fifo else 0)
+                     combine="tasks", bands=bands,
+                     flags=_abi.FLAG_FIFO if fifo else _abi.FLAG_CONT_PRIORITY)
     assert layer.info["bands"] == bands
     y, r = layer(g["x"], return_routing=True, check_errors=True)
     torch.cuda.synchronize()
