@@ -378,10 +378,9 @@ int copy_routing(const moe_desc* d, const Params& p, const moe_routing* r, hipSt
 // sustained per-CU MFMA rate in expert tiles, the bytes/s one worker moves in
 // a gather task, and the device HBM bandwidth a streaming tile sustains.
 void set_cost_model(const moe_desc* d, Params* p) {
-  p->cm_mfma_rate = (d->dtype == MOE_BF16 ? 4.9e12f : 0.3e12f);
-  p->cm_cu_bw = 16e9f;
+  p->cm_mfma_rate = (d->dtype == MOE_BF16 ? 4.3e12f : 0.3e12f);
+  p->cm_cu_bw = 26e9f;
   p->cm_hbm_bw = 6.0e12f;
-  p->cm_slack = 0.5f;
 }
 
 int fill_params(const moe_desc* d, Layout* L, void* ws, size_t ws_bytes) {

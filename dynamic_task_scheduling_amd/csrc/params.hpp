@@ -105,7 +105,6 @@ struct Params {
   float cm_mfma_rate;   // cost model: sustained MFMA flop/s per CU
   float cm_cu_bw;       // cost model: bytes/s one CU moves in a gather
   float cm_hbm_bw;      // cost model: device bytes/s
-  float cm_slack;       // cost model: permute must finish within slack * compute
   // inputs
   const void* x;
   const void* wr;

@@ -330,7 +330,8 @@ struct Sched {
   static DEV void publish_build(const Params& p, int* s_tmp) {
     const int n_mt = ld_relaxed(cw(p, CW_NMT));
     const int n_perm = ld_relaxed(cw(p, CW_NPERM));
-    const bool split = p.split_policy != 2;
+    // a split is in force when the builder chose memory workers (Wm > 0)
+    const bool split = ld_relaxed(cw(p, CW_WMEM)) > 0;
     const bool fifo = !cont_priority(p);
     const int n_up_qc = affinity(p) ? 0 : n_mt * p.n_up_n;
     const int n_cont = n_mt * p.n_down_n * p.splitk + p.n_sdown +
@@ -420,7 +421,7 @@ struct Sched {
         }
         if (arrive_last(cw(p, CW_POS_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
           const int n_perm = ld_relaxed(cw(p, CW_NPERM));
-          const int q = (p.split_policy != 2) ? QM : QC;
+          const int q = ld_relaxed(cw(p, CW_WMEM)) > 0 ? QM : QC;
           push_burst(p, q, n_perm, s_tmp, [&](int i) { return p.perm_list[i]; });
         }
         break;

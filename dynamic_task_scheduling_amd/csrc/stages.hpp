@@ -614,32 +614,41 @@ struct Stages {
       for (int c2 = 0; c2 < npt; ++c2) st_wt(p.perm_list + pbase + c2, make_task(TK_PERM, mt * p.pch + c2));
     }
     mark(3);
-    // 4. spatial split: the smallest memory group whose gather finishes
-    //    within `slack` x the compute group's time (cost model, per layer).
-    //    The gather time falls and the compute time rises with the memory
-    //    group's size, so the first size that passes is found by bisection.
+    // 4. spatial split (cost model, per layer).  With Wm memory workers the
+    //    gather takes t_mem(Wm) = bytes / min(Wm beta, B_hbm) and the expert
+    //    tiles t_mfma(Wm) = cost / (W - Wm); the split minimises their
+    //    maximum (t_mem falls and t_mfma rises with Wm, so the optimum is
+    //    where they cross: found by bisection, then the better neighbour).
+    //    Without a split every worker serves one queue: the gather, at the
+    //    device's bandwidth, then the tiles, t_none = bytes / min(W beta,
+    //    B_hbm) + cost / W.  The split is taken only when it is predicted at
+    //    least kSplitMargin faster than that (a split costs the role
+    //    hand-over and a second queue); otherwise Wm = 0.
     if (tid == 0) {
       const int W = p.workers;
       int wm_choice = 0;
       if (p.split_policy == 0 /* cost model */ && W >= 2) {
+        constexpr float kSplitMargin = 0.03f;
         const float bytes = 2.f * (float)total * (float)p.d * esz;
-        auto ok = [&](int wm) {
-          const float tm = bytes / fminf((float)wm * p.cm_cu_bw, p.cm_hbm_bw);
-          const float tc = tot_cost / (float)(W - wm);
-          return tm <= p.cm_slack * tc;
-        };
-        int lo = 1, hi = W - 1;        // answer in [lo, hi]; hi if none passes
+        auto t_mem = [&](int wm) { return bytes / fminf((float)wm * p.cm_cu_bw, p.cm_hbm_bw); };
+        auto t_mfma = [&](int wm) { return tot_cost / (float)(W - wm); };
+        int lo = 1, hi = W - 1;        // first wm with t_mem <= t_mfma (hi if none)
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
-          if (ok(mid)) hi = mid;
+          if (t_mem(mid) <= t_mfma(mid)) hi = mid;
           else lo = mid + 1;
         }
-        wm_choice = lo;
+        int best = lo;
+        float t_best = fmaxf(t_mem(lo), t_mfma(lo));
+        if (lo > 1 && fmaxf(t_mem(lo - 1), t_mfma(lo - 1)) < t_best) {
+          best = lo - 1;
+          t_best = fmaxf(t_mem(lo - 1), t_mfma(lo - 1));
+        }
+        const float t_none = t_mem(W) + tot_cost / (float)W;
+        wm_choice = (t_best < (1.f - kSplitMargin) * t_none) ? best : 0;
       } else if (p.split_policy == 1 /* fixed */) {
-        wm_choice = p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8;
+        wm_choice = max(1, p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8);
       }
-      // with a split, at least one worker drains the permute queue
-      if (p.split_policy != 2) wm_choice = max(1, wm_choice);
       int* cw = p.ctrl;
       st_relaxed(cw + CW_NMT * kCtrlStride, n_mt);
       st_relaxed(cw + CW_NPERM * kCtrlStride, n_perm);
