@@ -130,11 +130,11 @@ class Runner:
         self.bands = bands
         torch.cuda.synchronize()
 
-    def layers(self, mode, split, flags=0, trace=None, bands=None):
+    def layers(self, mode, split, flags=0, trace=None, bands=None, claim_batch=0):
         from dynamic_task_scheduling_amd.moe import MoELayer
         b = self.bands if bands is None else bands
         return [MoELayer(s, t, mode=mode, split=split, trace=trace, combine=self.combine, flags=flags,
-                         bands=b)
+                         bands=b, claim_batch=claim_batch)
                 for s, t in zip(self.wl.layers, self.tensors)]
 
     def step(self, layers):
@@ -238,30 +238,37 @@ def measure_modes(run, steps, warmup, modes=("dynamic", "static", "multi_kernel"
 
 def ablations(run, steps, warmup):
     """Scheduler ablations on one workload: the split policy, compute workers
-    stealing permute tasks, per-XCD UP queues, and the static baseline's
-    synchronisation (grid barriers vs per-task counter waits)."""
+    stealing permute tasks, per-XCD UP queues, XCD-local continuation queues,
+    batched claims, the continuation-priority queue, token bands, and the
+    static baseline's synchronisation (grid barriers vs per-task counter
+    waits)."""
     from dynamic_task_scheduling_amd import _abi
+    D, S, M = "dynamic", "static", "multi_kernel"
     variants = [
-        ("dynamic/split=cost_model", "dynamic", "cost_model", 0, None),
-        ("dynamic/split=fixed", "dynamic", "fixed", 0, None),
-        ("dynamic/split=none", "dynamic", "none", 0, None),
-        ("dynamic/steal=0", "dynamic", "cost_model", _abi.FLAG_NO_STEAL, None),
-        ("dynamic/xcd_affinity", "dynamic", "cost_model", _abi.FLAG_XCD_AFFINITY, None),
-        ("dynamic/bands=1", "dynamic", "cost_model", 0, 1),
-        ("dynamic/bands=2", "dynamic", "cost_model", 0, 2),
-        ("dynamic/bands=4", "dynamic", "cost_model", 0, 4),
-        ("dynamic/cont_priority/bands=1", "dynamic", "cost_model", _abi.FLAG_CONT_PRIORITY, 1),
-        ("dynamic/cont_priority/bands=4", "dynamic", "cost_model", _abi.FLAG_CONT_PRIORITY, 4),
-        ("static/sync=phase_barrier", "static", "fixed", 0, None),
-        ("static/sync=ref_count", "static", "fixed", _abi.FLAG_REF_SYNC, None),
-        ("multi_kernel", "multi_kernel", "none", 0, None),
+        # name, mode, split, flags, bands, claim_batch
+        ("dynamic/split=cost_model", D, "cost_model", 0, None, 0),
+        ("dynamic/split=fixed", D, "fixed", 0, None, 0),
+        ("dynamic/split=none", D, "none", 0, None, 0),
+        ("dynamic/steal=0", D, "fixed", _abi.FLAG_NO_STEAL, None, 0),
+        ("dynamic/xcd_affinity", D, "cost_model", _abi.FLAG_XCD_AFFINITY, None, 0),
+        ("dynamic/local_queues", D, "cost_model", _abi.FLAG_LOCAL_QUEUES, None, 0),
+        ("dynamic/claim_batch=2", D, "cost_model", 0, None, 2),
+        ("dynamic/claim_batch=4", D, "cost_model", 0, None, 4),
+        ("dynamic/claim_batch=8", D, "cost_model", 0, None, 8),
+        ("dynamic/local_queues/claim_batch=4", D, "cost_model", _abi.FLAG_LOCAL_QUEUES, None, 4),
+        ("dynamic/cont_priority", D, "cost_model", _abi.FLAG_CONT_PRIORITY, None, 0),
+        ("dynamic/bands=2", D, "cost_model", 0, 2, 0),
+        ("dynamic/bands=4", D, "cost_model", 0, 4, 0),
+        ("static/sync=phase_barrier", S, "fixed", 0, None, 0),
+        ("static/sync=ref_count", S, "fixed", _abi.FLAG_REF_SYNC, None, 0),
+        ("multi_kernel", M, "none", 0, None, 0),
     ]
     out = {}
-    for name, mode, split, fl, bands in variants:
-        L = run.layers(mode, split, flags=fl, bands=bands)
+    for name, mode, split, fl, bands, cb in variants:
+        L = run.layers(mode, split, flags=fl, bands=bands, claim_batch=cb)
         run.timed(L, 1, warmup)
         out[name] = round(run.timed(L, steps, warmup)["mean"], 4)
-        if mode == "dynamic":
+        if mode == D:
             out[name + ":mem_workers"] = L[0].last_schedule()["mem_workers"]
         del L
     return out
@@ -413,6 +420,17 @@ def main():
             r2 = Runner(cfg, dev, args.combine)
             ms2 = measure_modes(r2, max(5, args.steps // 2), max(2, args.warmup // 2))
             others[r2.wl.name] = summarize(r2, ms2)
+            if not args.no_ablations:
+                # the spatial split on this workload: the cost model's choice
+                # (Wm per layer above) against a fixed group and no split
+                sp = {}
+                for split in ("fixed", "none"):
+                    L = r2.layers("dynamic", split)
+                    r2.timed(L, 1, 2)
+                    sp[split] = round(r2.timed(L, max(5, args.steps // 2), 2)["mean"], 4)
+                    del L
+                sp["cost_model"] = others[r2.wl.name]["ms"]["dynamic"]
+                others[r2.wl.name]["split_ablation_ms"] = sp
             if len(r2.wl.layers) > 1:
                 # the multi-layer persistent kernel: all layers in one launch
                 t1 = time_one_launch(r2, max(5, args.steps // 2), max(2, args.warmup // 2))

@@ -16,6 +16,7 @@ FLAG_CHECK, FLAG_TRACE, FLAG_PHASE_SYNC, FLAG_REF_SYNC, FLAG_NO_STEAL = 0x1, 0x2
 FLAG_XCD_AFFINITY = 0x20
 FLAG_FIFO = 0x40
 FLAG_CONT_PRIORITY = 0x80
+FLAG_LOCAL_QUEUES = 0x100
 
 ERRORS = {
     0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_WORKSPACE", 3: "MOE_ERR_UNSUPPORTED",
@@ -38,6 +39,7 @@ class Desc(ctypes.Structure):
         ("fixed_mem_workers", c_int), ("split_k", c_int), ("max_workers", c_int),
         ("flags", c_uint), ("trace", c_void_p), ("trace_cap", c_int), ("timeout_ms", c_int),
         ("row_tile", c_int), ("combine", c_int), ("bands", c_int), ("timeout_ticks", c_int),
+        ("claim_batch", c_int),
     ]
 
 

@@ -27,6 +27,7 @@ __host__ __device__ inline int ctrl_init(const Params& p, int w) {
   if (w == CW_TAIL + QC) return p.n_sup;
   if (w == CW_TOTAL + QM || w == CW_TOTAL + QC || w == CW_TOTAL + QH) return 0x7fffffff;
   if (w >= CW_UTOTAL && w < CW_UTOTAL + kXcds) return 0x7fffffff;
+  if (w == CW_LTOTAL) return 0x7fffffff;
   return 0;
 }
 
@@ -54,7 +55,7 @@ DEV void reset_body(const Params& p, int gid, int stride) {
   for (int i = gid; i < p.n_rt; i += stride) p.cnt_comb[i] = 1 + p.n_shared * p.n_down_n;
   // a token tile's NORM task waits for its combine column chunks
   for (int i = gid; i < p.n_rt; i += stride) p.cnt_norm[i] = p.n_cc;
-  if (p.flags & MOE_FLAG_XCD_AFFINITY) {
+  if (p.flags & (MOE_FLAG_XCD_AFFINITY | MOE_FLAG_LOCAL_QUEUES)) {
     const size_t nu = (size_t)kXcds * p.q_cap;
     for (size_t i = gid; i < nu; i += stride) p.uslots[i] = 0;
   }
@@ -116,6 +117,12 @@ int validate(const moe_desc* d) {
   if (d->row_tile == 256 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->combine < MOE_COMBINE_AUTO || d->combine > MOE_COMBINE_TASKS) return MOE_ERR_ARG;
   if (d->bands < 0 || d->bands > kMaxBands) return MOE_ERR_ARG;
+  if (d->claim_batch < 0 || d->claim_batch > 8) return MOE_ERR_ARG;
+  // local continuation queues take the place of the per-XCD UP queues and
+  // of the continuation-priority queue
+  if ((d->flags & MOE_FLAG_LOCAL_QUEUES) &&
+      (d->flags & (MOE_FLAG_XCD_AFFINITY | MOE_FLAG_CONT_PRIORITY)))
+    return MOE_ERR_ARG;
   return MOE_OK;
 }
 
@@ -400,6 +407,7 @@ int fill_params(const moe_desc* d, Layout* L, void* ws, size_t ws_bytes) {
   const long long ms = d->timeout_ms > 0 ? d->timeout_ms : 2000;
   p.timeout_ticks = ms * 100000ll;  // 100 MHz constant clock
   if (d->timeout_ticks > 0) p.timeout_ticks = d->timeout_ticks;
+  p.claim_batch = d->claim_batch > 0 ? d->claim_batch : 1;
   set_cost_model(d, &p);
   p.trace = (d->flags & MOE_FLAG_TRACE) ? d->trace : nullptr;
   p.trace_cap = d->trace_cap;

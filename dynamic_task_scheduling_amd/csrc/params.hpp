@@ -58,7 +58,9 @@ enum CtrlWord : int {
   CW_UHEAD = 24,       // + XCD: per-XCD UP queues (XCD affinity)
   CW_UTAIL = 32,       // + XCD
   CW_UTOTAL = 40,      // + XCD
-  CW_COUNT = 48
+  CW_LTOTAL = 48,      // local queues: continuation tasks that will be pushed
+  CW_LCLAIMED = 49,    // local queues: continuation tasks claimed so far
+  CW_COUNT = 50
 };
 constexpr int kXcds = 8;   // MI355X: 8 XCDs, each with its own L2
 constexpr int kMaxBands = 4;  // token bands of the row-tile order
@@ -101,6 +103,7 @@ struct Params {
   int workers;
   int mode, split_policy, fixed_mem;
   unsigned flags;
+  int claim_batch;      // compute-queue slots one claim reserves (1..8)
   long long timeout_ticks;
   float cm_mfma_rate;   // cost model: sustained MFMA flop/s per CU
   float cm_cu_bw;       // cost model: bytes/s one CU moves in a gather
@@ -119,7 +122,7 @@ struct Params {
   // workspace
   int* ctrl;
   int* slots;      // [kNumQueues][q_cap]
-  int* uslots;     // [kXcds][q_cap] per-XCD UP queues (XCD affinity)
+  int* uslots;     // [kXcds][q_cap] per-XCD queues (XCD affinity, local queues)
   float* logits;   // [T][E]
   float* route_part;  // [rsk][T][E] router partial sums (rsk > 1)
   int* cnt_route;  // [n_rt] router slices still running

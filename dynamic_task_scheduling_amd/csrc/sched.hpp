@@ -37,6 +37,9 @@ constexpr int kFlagNoSteal = 0x10;
 constexpr int kFlagXcdAffinity = 0x20;
 constexpr int kFlagFifo = 0x40;
 constexpr int kFlagContPriority = 0x80;
+constexpr int kFlagLocalQueues = 0x100;
+// Push target meaning "the local queue of the pushing worker's XCD".
+constexpr int QL = kNumQueues;
 
 // The queue continuation work (DOWN, shared DOWN, combine, NORM) goes to:
 // the one compute queue, in push order (default), or -- with
@@ -47,7 +50,16 @@ constexpr int kFlagContPriority = 0x80;
 DEV bool cont_priority(const Params& p) {
   return (p.flags & kFlagContPriority) != 0 && (p.flags & kFlagFifo) == 0;
 }
-DEV int qcont(const Params& p) { return cont_priority(p) ? QH : QC; }
+// MOE_FLAG_LOCAL_QUEUES: continuation work goes to the local queue of the
+// XCD whose worker made it ready (its inputs were just written through that
+// XCD's L2); workers serve their own XCD's local queue first, then the
+// global compute queue, then steal from other XCDs' local queues (the
+// per-CU-queue-with-global-fallback pattern of xxqk.cn/news/665650 s4.4,
+// with the XCD as the locality domain).
+DEV bool local_queues(const Params& p) { return (p.flags & kFlagLocalQueues) != 0; }
+DEV int qcont(const Params& p) {
+  return local_queues(p) ? QL : cont_priority(p) ? QH : QC;
+}
 
 // XCD affinity: the UP task of column tile n goes to the ready queue of XCD
 // n % 8, so the workers of one XCD keep reading the same weight panels
@@ -87,26 +99,56 @@ DEV int wait_slot(const Params& p, const int* sl) {
   }
 }
 
-// Thread 0: take an already-pushed UP task from the XCD queues, own first.
-// A slot is claimed (by compare-and-swap on the head) only while it lies
-// below the queue's tail, so the claimed slot has been pushed (its store is
-// at most one instruction behind the tail increment): a worker never waits
-// here on a slot that may never be filled.
-DEV int take_up(const Params& p) {
+// Thread 0: take an already-pushed task from the per-XCD queues of this
+// XCD and the next nx - 1 XCDs, in that order.  One poll reads every
+// queue's head and tail in a single round trip (the loads are independent);
+// a slot is then claimed by compare-and-swap on the head only while it lies
+// below the observed tail, so the claimed slot has been pushed (its store is
+// at most a few instructions behind the tail increment): a worker never
+// waits here on a slot that may never be filled.  `count`: add the take to
+// the local-queue claim counter.
+DEV int take_xcd(const Params& p, int nx, bool count) {
   const int x0 = xcc_id() & (kXcds - 1);
+  int hd[kXcds], tl[kXcds];
+#pragma unroll
   for (int i = 0; i < kXcds; ++i) {
     const int x = (x0 + i) & (kXcds - 1);
-    int h = ld_relaxed(ucw(p, CW_UHEAD, x));
-    while (h < ld_relaxed(ucw(p, CW_UTAIL, x)) && h < p.q_cap) {
+    hd[i] = i < nx ? ld_relaxed(ucw(p, CW_UHEAD, x)) : 0;
+    tl[i] = i < nx ? ld_relaxed(ucw(p, CW_UTAIL, x)) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kXcds; ++i) {
+    const int x = (x0 + i) & (kXcds - 1);
+    int h = hd[i];
+    while (h < tl[i] && h < p.q_cap) {
       const int seen = cas_relaxed(ucw(p, CW_UHEAD, x), h, h + 1);
-      if (seen == h) return wait_slot(p, p.uslots + (size_t)x * p.q_cap + h);
+      if (seen == h) {
+        if (count) add_relaxed(cw(p, CW_LCLAIMED), 1);
+        return wait_slot(p, p.uslots + (size_t)x * p.q_cap + h);
+      }
       h = seen;
+      tl[i] = ld_relaxed(ucw(p, CW_UTAIL, x));
     }
   }
   return kClaimExhausted;
 }
 
-// Thread 0: claim for queue q.  `pend` keeps a claimed but not yet filled
+// XCD affinity: an UP task from the XCD queues, own first.
+DEV int take_up(const Params& p) { return take_xcd(p, kXcds, false); }
+
+// Local queues: continuation work from this XCD's queue and, nx = 8, from
+// the other XCDs' (stealing); every take is counted, so a worker knows when
+// all continuation tasks have been claimed.
+DEV int take_local(const Params& p, int nx) { return take_xcd(p, nx, true); }
+
+// Thread 0's reservations across claims: slots [pb, pe) of its current
+// queue (taken claim_batch at a time with one atomic increment on the
+// compute queue, one at a time elsewhere) and one continuation slot h.
+struct Reserve {
+  int pb, pe, h;
+};
+
+// Thread 0: claim for queue q.  `r` keeps claimed but not yet filled
 // slot of q across calls.  For the compute queue (q == QC) the continuation
 // queue QH (DOWN, shared DOWN, combine, NORM work) comes first: a worker
 // that sees pushed QH work reserves the next QH slot (`pend_h`) by one
@@ -118,43 +160,65 @@ DEV int take_up(const Params& p) {
 // compare-and-swap retries on a hot word), and a filled reserved slot is
 // taken first at the next claim.  A worker leaves only when its QC index is
 // past QC's total and QH holds nothing more for it.
-DEV int claim(const Params& p, int q, int& pend, int& pend_h, bool steal) {
+// Batched claims (claim_batch > 1, xxqk.cn/news/665650 s4.2): one atomic
+// increment reserves that many consecutive compute-queue slots, which the
+// worker then runs in order, so the hot head word sees a fraction of the
+// atomics; the reserved slots are this worker's, filled or not.
+DEV int claim(const Params& p, int q, Reserve& r, bool steal) {
   const bool cont = q == QC && cont_priority(p);
+  const bool local = q == QC && local_queues(p);
+  const int batch = q == QC ? p.claim_batch : 1;
   const uint64_t t0 = rtc();
+  int nx = 1;        // local queues polled: this XCD's, then (after one
+                     // empty pass over the global queue) every XCD's
   for (;;) {
     int hh = 0, ht = 0, htot = 0, vh = 0;
     if (cont) {
       hh = ld_relaxed(cw(p, CW_HEAD + QH));
       ht = ld_relaxed(cw(p, CW_TAIL + QH));
       htot = ld_relaxed(cw(p, CW_TOTAL + QH));
-      if (pend_h >= 0) vh = ld_relaxed(p.slots + (size_t)QH * p.q_cap + pend_h);
+      if (r.h >= 0) vh = ld_relaxed(p.slots + (size_t)QH * p.q_cap + r.h);
     }
     const int err = ld_relaxed(cw(p, CW_ERROR));
     if (err != 0) return kClaimAbort;
     if (vh != 0) {                     // the reserved continuation task is there
-      pend_h = -1;
+      r.h = -1;
       return vh - 1;
     }
-    if (cont && pend_h < 0 && hh < ht && hh < htot) {
+    if (cont && r.h < 0 && hh < ht && hh < htot) {
       const int i = add_relaxed(cw(p, CW_HEAD + QH), 1);
       if (i < htot && i < p.q_cap) {
         const int v = ld_relaxed(p.slots + (size_t)QH * p.q_cap + i);
         if (v != 0) return v - 1;
-        pend_h = i;                    // pushed soon, or later: keep it
+        r.h = i;                       // pushed soon, or later: keep it
       }
     }
-    if (pend < 0) pend = add_relaxed(cw(p, CW_HEAD + q), 1);
-    const int h = pend;
+    if (local) {                       // this XCD's continuation work first
+      const int t = take_local(p, nx);
+      if (t != kClaimExhausted) return t;
+    }
+    if (r.pb >= r.pe) {
+      r.pb = add_relaxed(cw(p, CW_HEAD + q), batch);
+      r.pe = r.pb + batch;
+    }
+    const int h = r.pb;
     const int v = h < p.q_cap ? ld_relaxed(p.slots + (size_t)q * p.q_cap + h) : 0;
     const int total = ld_relaxed(cw(p, CW_TOTAL + q));
     if (v != 0) {            // a filled slot is always below the total
-      pend = -1;
+      ++r.pb;
       return v - 1;
     }
-    // no more QC work for this worker; QH: nothing reserved and nothing left
-    if (h >= total && (!cont || (pend_h < 0 && ld_relaxed(cw(p, CW_HEAD + QH)) >= htot))) {
-      pend = -1;
-      return kClaimExhausted;
+    // past q's total (so are the later reservations): nothing more from q;
+    // leave unless continuation work is still owed to this worker or to the
+    // local queues
+    if (h >= total) {
+      const bool cont_left = cont && (r.h >= 0 || ld_relaxed(cw(p, CW_HEAD + QH)) < htot);
+      const bool local_left =
+          local && ld_relaxed(cw(p, CW_LCLAIMED)) < ld_relaxed(cw(p, CW_LTOTAL));
+      if (!cont_left && !local_left) {
+        r.pb = r.pe = -1;
+        return kClaimExhausted;
+      }
     }
     if (steal) {
       const int mh = ld_relaxed(cw(p, CW_HEAD + QM));
@@ -171,6 +235,7 @@ DEV int claim(const Params& p, int q, int& pend, int& pend_h, bool steal) {
       const int t = take_up(p);
       if (t != kClaimExhausted) return t;
     }
+    nx = kXcds;                        // next pass: steal local work too
     if (timed_out(p, t0)) {
       set_error(p, 5 /* MOE_ERR_TIMEOUT */);
       return kClaimAbort;
@@ -193,6 +258,16 @@ DEV bool wait_zero(const Params& p, const int* c) {
   return true;
 }
 
+// Tail word and slot array of push target q: a queue, or QL, the local
+// queue of the calling workgroup's XCD.
+DEV int* push_tail(const Params& p, int q) {
+  return q == QL ? ucw(p, CW_UTAIL, xcc_id() & (kXcds - 1)) : cw(p, CW_TAIL + q);
+}
+DEV int* push_slots(const Params& p, int q) {
+  return q == QL ? p.uslots + (size_t)(xcc_id() & (kXcds - 1)) * p.q_cap
+                 : p.slots + (size_t)q * p.q_cap;
+}
+
 // All threads: push n task ids (id_of(i)) into queue q.  The slot stores are
 // agent-coherent; everything the new tasks read was written through and
 // drained by its producers before they published.
@@ -200,7 +275,7 @@ template <typename F>
 DEV void push_burst(const Params& p, int q, int n, int* s_tmp, F&& id_of) {
   if (n <= 0) return;
   publish_fence();
-  if (tidx() == 0) s_tmp[0] = add_relaxed(cw(p, CW_TAIL + q), n);
+  if (tidx() == 0) s_tmp[0] = add_relaxed(push_tail(p, q), n);
   __syncthreads();
   const int base = uniform(s_tmp[0]);
   __syncthreads();
@@ -208,7 +283,7 @@ DEV void push_burst(const Params& p, int q, int n, int* s_tmp, F&& id_of) {
     if (tidx() == 0) set_error(p, 6 /* MOE_ERR_CAPACITY */);
     return;
   }
-  int* slots = p.slots + (size_t)q * p.q_cap + base;
+  int* slots = push_slots(p, q) + base;
   for (int i = tidx(); i < n; i += kThreads) st_relaxed(slots + i, id_of(i) + 1);
 }
 
@@ -279,12 +354,12 @@ DEV void trace_mark(const Params& p, int phase, int worker, uint64_t t0, uint64_
 DEV void push_tile_ready(const Params& p, int rt, bool scat) {
   const int n = scat ? 1 : p.n_cc;
   const int q = qcont(p);
-  const int base = add_relaxed(cw(p, CW_TAIL + q), n);
+  const int base = add_relaxed(push_tail(p, q), n);
   if (base + n > p.q_cap) {
     set_error(p, 6 /* MOE_ERR_CAPACITY */);
     return;
   }
-  int* sl = p.slots + (size_t)q * p.q_cap + base;
+  int* sl = push_slots(p, q) + base;
   if (scat) {
     st_relaxed(sl, make_task(TK_NORM, rt) + 1);
     return;
@@ -332,16 +407,17 @@ struct Sched {
     const int n_perm = ld_relaxed(cw(p, CW_NPERM));
     // a split is in force when the builder chose memory workers (Wm > 0)
     const bool split = ld_relaxed(cw(p, CW_WMEM)) > 0;
-    const bool fifo = !cont_priority(p);
+    const int qc = qcont(p);
     const int n_up_qc = affinity(p) ? 0 : n_mt * p.n_up_n;
     const int n_cont = n_mt * p.n_down_n * p.splitk + p.n_sdown +
                        (SCAT ? 0 : p.n_rt * p.n_cc) + (p.fuse_norm ? p.n_rt : 0);
-    const int n_comp = n_up_qc + p.n_sup + (fifo ? n_cont : 0);
+    const int n_comp = n_up_qc + p.n_sup + (qc == QC ? n_cont : 0);
     publish_fence();
     __syncthreads();
     if (tidx() == 0) {
       st_relaxed(cw(p, CW_TOTAL + QM), split ? n_perm : 0);
-      st_relaxed(cw(p, CW_TOTAL + QH), fifo ? 0 : n_cont);
+      st_relaxed(cw(p, CW_TOTAL + QH), qc == QH ? n_cont : 0);
+      st_relaxed(cw(p, CW_LTOTAL), qc == QL ? n_cont : 0);
       st_relaxed(cw(p, CW_TOTAL + QC), n_comp + (split ? 0 : n_perm));
       if (affinity(p))
         for (int x = 0; x < kXcds; ++x)
@@ -356,8 +432,8 @@ struct Sched {
       if (add_relaxed(p.cnt_sdown + i, -1) == 1) {
         int* sl = nullptr;
         const int q = qcont(p);
-        const int base = add_relaxed(cw(p, CW_TAIL + q), p.n_down_n);
-        if (base + p.n_down_n <= p.q_cap) sl = p.slots + (size_t)q * p.q_cap + base;
+        const int base = add_relaxed(push_tail(p, q), p.n_down_n);
+        if (base + p.n_down_n <= p.q_cap) sl = push_slots(p, q) + base;
         else set_error(p, 6);
         if (sl) {
           publish_fence();
@@ -570,15 +646,26 @@ template <typename Elem, bool SCAT>
 DEV void dynamic_worker(const Params& p, char* smem, int* s_tmp, int* s_worker) {
   if (tidx() == 0) *s_worker = add_relaxed(cw(p, CW_TICKET), 1);
   int q = QA;
-  int pend = -1;   // thread 0: claimed but not yet filled slot of queue q
-  int pend_h = -1; // thread 0: reserved but not yet filled continuation slot
+  // thread 0's reserved, not yet taken slots live in LDS (s_tmp[4..6])
+  // between claims, not in registers held across every task body
+  // (the -1 is laundered so that no vector of it is hoisted out of the
+  // multi-layer loop and held across every task)
+  if (tidx() == 0) {
+    int none = -1;
+    asm volatile("" : "+v"(none));
+    s_tmp[4] = s_tmp[5] = s_tmp[6] = none;
+  }
   for (;;) {
     // every pass reads the parameters afresh (see params_view)
     const Params& pv = params_view(p);
     const bool steal = pv.split_policy != 2 && !(pv.flags & kFlagNoSteal);
     uint64_t t_req = rtc();
     if (tidx() == 0) {
-      int v = claim(pv, q, pend, pend_h, steal && q == QC);
+      Reserve r{s_tmp[4], s_tmp[5], s_tmp[6]};
+      int v = claim(pv, q, r, steal && q == QC);
+      s_tmp[4] = r.pb;
+      s_tmp[5] = r.pe;
+      s_tmp[6] = r.h;
       int role = q;
       // routing phase over for this worker: shared-expert tiles until the
       // split is published, then the role the split assigns
@@ -608,7 +695,7 @@ DEV void dynamic_worker(const Params& p, char* smem, int* s_tmp, int* s_worker) 
 template <typename Elem, bool SCAT>
 __global__ __launch_bounds__(kThreads, 1) void k_dynamic(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
-  __shared__ int s_tmp[4];
+  __shared__ int s_tmp[8];
   __shared__ int s_worker;
   dynamic_worker<Elem, SCAT>(p, smem, s_tmp, &s_worker);
 }
@@ -627,7 +714,7 @@ typedef const __attribute__((address_space(4))) Params ConstParams;
 template <typename Elem, bool SCAT>
 __global__ __launch_bounds__(kThreads, 1) void k_dynamic_layers(const Params* layers, int n) {
   __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
-  __shared__ int s_tmp[4];
+  __shared__ int s_tmp[8];
   __shared__ int s_worker;
   ConstParams* lp = (ConstParams*)layers;
   for (int l = 0; l < n; ++l) {
@@ -647,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dynamic_layers(const Params* la
 template <typename Elem, bool SCAT>
 __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
-  __shared__ int s_tmp[4];
+  __shared__ int s_tmp[8];
   if (tidx() == 0) s_tmp[3] = add_relaxed(cw(p, CW_TICKET), 1);
   __syncthreads();
   const int w = uniform(s_tmp[3]);
@@ -783,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_route(Params p) {
   const int rt = blockIdx.x / p.rsk;
   Stages<Elem>::route(p, rt, blockIdx.x % p.rsk, smem, p.comb_scatter != 0);
   if (p.rsk > 1) {
-    __shared__ int s_tmp[4];
+    __shared__ int s_tmp[8];
     if (!arrive_last(p.cnt_route + rt, -1, 1, s_tmp)) return;
     Stages<Elem>::route_finish(p, rt, smem);
   }

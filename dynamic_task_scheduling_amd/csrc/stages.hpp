@@ -973,6 +973,17 @@ struct Stages {
   // abstract): a token's output needs every one of its experts, so the task
   // becomes ready only when all DOWN tiles holding its rows have finished.
   // Fixed summation order: y does not depend on the schedule.
+  // A combined y row chunk: written through to memory when a NORM task (on
+  // any XCD) reads it in this launch; otherwise a plain store, left in this
+  // XCD's L2 until the kernel's end-of-launch release writes it back.
+  static DEV void st_y16(const Params& p, float* row, uint32_t byte_off, uint4 v) {
+    if (p.fuse_norm) {
+      st_wt16(row, byte_off, v);
+    } else {
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(row) + byte_off) = v;
+    }
+  }
+
   static TASKFN void combine(const Params& p, int rt, int cc, char* smem) {
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
@@ -1074,10 +1085,9 @@ struct Stages {
         const int i = i0 + u * kThreads;
         if (i >= n) continue;
         const int r = i / c4, col = col0 + (i % c4) * 4;
-        // write-through: a NORM task on another XCD reads these rows
-        st_wt16(p.y + (size_t)(t0 + r) * p.d, (uint32_t)col * 4u,
-                make_uint4(__float_as_uint(acc[u].x), __float_as_uint(acc[u].y),
-                           __float_as_uint(acc[u].z), __float_as_uint(acc[u].w)));
+        st_y16(p, p.y + (size_t)(t0 + r) * p.d, (uint32_t)col * 4u,
+               make_uint4(__float_as_uint(acc[u].x), __float_as_uint(acc[u].y),
+                          __float_as_uint(acc[u].z), __float_as_uint(acc[u].w)));
       }
     }
     __syncthreads();

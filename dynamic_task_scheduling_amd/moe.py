@@ -37,7 +37,7 @@ def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model
               split_k: int = 0, max_workers: int = 0, fixed_mem_workers: int = 0,
               flags: int = 0, trace: Optional[torch.Tensor] = None,
               timeout_ms: int = 0, row_tile: int = 0, combine: str = "auto",
-              timeout_ticks: int = 0, bands: int = 0) -> Desc:
+              timeout_ticks: int = 0, bands: int = 0, claim_batch: int = 0) -> Desc:
     d = Desc()
     d.T, d.d, d.E, d.k, d.f = shape.T, shape.d, shape.E, shape.k, shape.f
     d.e_begin, d.e_end = shape.e_begin, shape.local_end
@@ -59,6 +59,7 @@ def make_desc(shape: LayerShape, mode: str = "dynamic", split: str = "cost_model
     d.combine = _abi.COMBINES[combine]
     d.timeout_ticks = timeout_ticks
     d.bands = bands
+    d.claim_batch = claim_batch
     return d
 
 
@@ -126,6 +127,7 @@ class MoELayer:
                  trace: Optional[torch.Tensor] = None, timeout_ms: int = 0,
                  workspace: Optional[torch.Tensor] = None, row_tile: int = 0,
                  combine: str = "auto", timeout_ticks: int = 0, bands: int = 0,
+                 claim_batch: int = 0,
                  no_alloc: bool = False):
         self.shape = shape
         dev = weights["w_gate"].device
@@ -133,7 +135,8 @@ class MoELayer:
             raise ValueError("weights must be on a GPU")
         self.device = dev
         self.desc = make_desc(shape, mode, split, split_k, max_workers, fixed_mem_workers,
-                              flags, trace, timeout_ms, row_tile, combine, timeout_ticks, bands)
+                              flags, trace, timeout_ms, row_tile, combine, timeout_ticks, bands,
+                              claim_batch)
         self._trace = trace
         et = _elem_dtype(shape)
         d, E, f, El = shape.d, shape.E, shape.f, shape.E_loc

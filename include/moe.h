@@ -100,6 +100,11 @@ typedef enum {
                                     overrides MOE_FLAG_CONT_PRIORITY)       */
 #define MOE_FLAG_CONT_PRIORITY 0x80u /* dynamic: continuation work (DOWN, shared DOWN, combine,
                                         NORM) in its own queue, served first */
+#define MOE_FLAG_LOCAL_QUEUES 0x100u /* dynamic: continuation work in the local queue of the
+                                        XCD that made it ready; workers take their own XCD's
+                                        first, then the global queue, then steal from other
+                                        XCDs (xxqk.cn/news/665650 s4.4).  Not combinable
+                                        with XCD_AFFINITY or CONT_PRIORITY (MOE_ERR_ARG) */
 
 /* Return codes. */
 #define MOE_OK 0
@@ -144,6 +149,9 @@ typedef struct moe_desc {
                          device clock, overriding timeout_ms (lets a test
                          force the watchdog; every wait then gives up and the
                          call reports MOE_ERR_TIMEOUT)                      */
+  int claim_batch;    /* dynamic: compute-queue slots one atomic claim
+                         reserves, 1..8 (xxqk.cn/news/665650 s4.2, batched
+                         fetch); 0 = 1                                      */
 } moe_desc;
 
 /* Weights.  E_loc = e_end - e_begin.  Element type = desc.dtype.

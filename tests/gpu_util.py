@@ -84,7 +84,8 @@ def check_logits(lg, n, shape):
 
 
 def run_and_check(shape, g, n=None, mode="dynamic", split="cost_model", sample=None,
-                  split_k=0, max_workers=0, label="", row_tile=0, combine="auto", flags=0):
+                  split_k=0, max_workers=0, label="", row_tile=0, combine="auto", flags=0,
+                  claim_batch=0):
     """Run one layer on the GPU and check it against the oracle.
     sample: None = every token; int = that many sampled tokens."""
     t0 = time.time()
@@ -94,7 +95,7 @@ def run_and_check(shape, g, n=None, mode="dynamic", split="cost_model", sample=N
                                    row_tile, combine))
     layer = MoELayer(shape, g, mode=mode, split=split, split_k=split_k,
                      max_workers=max_workers, timeout_ms=3000, row_tile=row_tile,
-                     combine=combine, flags=flags)
+                     combine=combine, flags=flags, claim_batch=claim_batch)
     y, r = layer(g["x"], return_routing=True, check_errors=True)
     torch.cuda.synchronize()
     if n is None:

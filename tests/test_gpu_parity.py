@@ -377,6 +377,33 @@ def test_queue_policy_and_bands(big_tile, fifo, bands):
                       combine="tasks")
 
 
+@pytest.mark.parametrize("local", [False, True])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_claim_batch_and_local_queues(big_tile, local, batch):
+    """Batched claims (one atomic increment reserves `batch` compute-queue
+    slots) and XCD-local continuation queues with a global fallback and
+    stealing: every task once, after its producers, y bit-identical to the
+    static kernel's (same tiles, fixed-order combine); the largest batch of
+    each queue layout is also checked against the oracle, with the scatter
+    combine and a local expert range."""
+    from analysis_util import check_trace
+    from dynamic_task_scheduling_amd import _abi
+    g, n = big_tile
+    fl = _abi.FLAG_LOCAL_QUEUES if local else 0
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(BIG_TILE, g, mode="dynamic", trace=trace, timeout_ms=3000, row_tile=256,
+                     combine="tasks", claim_batch=batch, flags=fl)
+    y, r = layer(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+    y2 = MoELayer(BIG_TILE, g, mode="static", split="fixed", row_tile=256,
+                  combine="tasks")(g["x"], check_errors=True)
+    assert torch.equal(y, y2)
+    if batch == 8:
+        run_and_check(MID_LOCAL, *gen_and_host(MID_LOCAL, "mid_local", 2), "dynamic", "none",
+                      label="batch8_local%d" % local, flags=fl, claim_batch=8)
+
+
 @pytest.mark.parametrize("combine", ["scatter", "tasks"])
 def test_layers_in_one_launch(combine):
     """moe_layers: several independent layers of different shapes in one

@@ -82,7 +82,9 @@ def test_workspace_size_and_validation(abi):
     assert ok >= 2 * 256 * (4096 + 14336)
     bad = [dict(k=9), dict(k=3, E=2), dict(d=100), dict(f=200), dict(E=300), dict(T=-1),
            dict(e_begin=5, e_end=3), dict(n_shared=1, f_shared=100), dict(dtype=7),
-           dict(mode=5), dict(split_k=9)]
+           dict(mode=5), dict(split_k=9), dict(claim_batch=9), dict(claim_batch=-1),
+           dict(flags=abi.FLAG_LOCAL_QUEUES | abi.FLAG_XCD_AFFINITY),
+           dict(flags=abi.FLAG_LOCAL_QUEUES | abi.FLAG_CONT_PRIORITY)]
     for b in bad:
         assert L.moe_workspace_size(ctypes.byref(_desc(abi, **b))) == 0, b
     # bigger problems need more workspace
