@@ -17,6 +17,7 @@ FLAG_XCD_AFFINITY = 0x20
 FLAG_FIFO = 0x40
 FLAG_CONT_PRIORITY = 0x80
 FLAG_LOCAL_QUEUES = 0x100
+FLAG_PERTURB = 0x200
 
 ERRORS = {
     0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_WORKSPACE", 3: "MOE_ERR_UNSUPPORTED",

@@ -38,6 +38,7 @@ constexpr int kFlagXcdAffinity = 0x20;
 constexpr int kFlagFifo = 0x40;
 constexpr int kFlagContPriority = 0x80;
 constexpr int kFlagLocalQueues = 0x100;
+constexpr int kFlagPerturb = 0x200;
 // Push target meaning "the local queue of the pushing worker's XCD".
 constexpr int QL = kNumQueues;
 
@@ -71,6 +72,21 @@ DEV bool affinity(const Params& p) { return (p.flags & kFlagXcdAffinity) != 0; }
 DEV int* ucw(const Params& p, int word, int x) { return p.ctrl + (word + x) * kCtrlStride; }
 
 DEV int* cw(const Params& p, int word) { return p.ctrl + word * kCtrlStride; }
+
+// Race perturbation (MOE_FLAG_PERTURB; m.xxqk.cn/news/657744 s3.3 on
+// hunting scheduler races): thread 0 sleeps a pseudo-random 0 .. 63 x 128
+// clocks before every claim and every dependency decrement, and pushed
+// bursts land in reverse order, so the interleavings a test sees are far
+// from the usual ones.  The hash of the clock and a per-site salt is
+// splitmix-style mixing; only timing depends on it, never a result.
+DEV void perturb(const Params& p, uint32_t salt) {
+  if (!(p.flags & kFlagPerturb)) return;
+  uint32_t h = (uint32_t)__builtin_amdgcn_s_memrealtime() * 0x9e3779b9u ^ salt;
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  for (uint32_t i = 0, n = h & 63u; i < n; ++i) __builtin_amdgcn_s_sleep(2);
+}
 
 DEV bool timed_out(const Params& p, uint64_t t0) {
   return (long long)(rtc() - t0) > p.timeout_ticks;
@@ -165,6 +181,7 @@ struct Reserve {
 // worker then runs in order, so the hot head word sees a fraction of the
 // atomics; the reserved slots are this worker's, filled or not.
 DEV int claim(const Params& p, int q, Reserve& r, bool steal) {
+  perturb(p, 0x1000u + q);
   const bool cont = q == QC && cont_priority(p);
   const bool local = q == QC && local_queues(p);
   const int batch = q == QC ? p.claim_batch : 1;
@@ -284,14 +301,18 @@ DEV void push_burst(const Params& p, int q, int n, int* s_tmp, F&& id_of) {
     return;
   }
   int* slots = push_slots(p, q) + base;
-  for (int i = tidx(); i < n; i += kThreads) st_relaxed(slots + i, id_of(i) + 1);
+  const bool rev = (p.flags & kFlagPerturb) != 0;
+  for (int i = tidx(); i < n; i += kThreads) st_relaxed(slots + i, id_of(rev ? n - 1 - i : i) + 1);
 }
 
 // All threads: the last of `target` arrivals on counter c returns true.
-DEV bool arrive_last(int* c, int delta, int last_old, int* s_tmp) {
+DEV bool arrive_last(const Params& p, int* c, int delta, int last_old, int* s_tmp) {
   publish_fence();
   __syncthreads();
-  if (tidx() == 0) s_tmp[0] = (add_relaxed(c, delta) == last_old);
+  if (tidx() == 0) {
+    perturb(p, 0x2000u);
+    s_tmp[0] = (add_relaxed(c, delta) == last_old);
+  }
   __syncthreads();
   const bool last = uniform(s_tmp[0]) != 0;
   __syncthreads();
@@ -379,7 +400,10 @@ DEV void combine_arrive_rows(const Params& p, int row0, int rows, bool dyn, bool
   if (r < rows) {
     const int blk = p.perm[row0 + r] / kTB;
     const int prev = r > 0 ? p.perm[row0 + r - 1] / kTB : -1;
-    if (blk != prev && add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn) push_tile_ready(p, blk, scat);
+    if (blk != prev) {
+      perturb(p, 0x3000u + blk);
+      if (add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn) push_tile_ready(p, blk, scat);
+    }
   }
   __syncthreads();
 }
@@ -459,12 +483,12 @@ struct Sched {
         *t_body = rtc();
         if (p.rsk > 1) {
           // the last K slice of this tile reduces the partials and routes
-          if (!arrive_last(p.cnt_route + rt, -1, 1, s_tmp)) break;
+          if (!arrive_last(p, p.cnt_route + rt, -1, 1, s_tmp)) break;
           const uint64_t tf = rtc();
           S::route_finish(p, rt, smem);
           trace_mark(p, kPhaseRouteFinish + rt, worker, tf, rtc());
         }
-        if (arrive_last(cw(p, CW_ROUTE_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
+        if (arrive_last(p, cw(p, CW_ROUTE_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
           const uint64_t tb = rtc();
           S::build(p, smem, worker);
           __syncthreads();
@@ -495,7 +519,7 @@ struct Sched {
           if (tidx() == 0) push_tile_ready(p, pl, SCAT);
           __syncthreads();
         }
-        if (arrive_last(cw(p, CW_POS_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
+        if (arrive_last(p, cw(p, CW_POS_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
           const int n_perm = ld_relaxed(cw(p, CW_NPERM));
           const int q = ld_relaxed(cw(p, CW_WMEM)) > 0 ? QM : QC;
           push_burst(p, q, n_perm, s_tmp, [&](int i) { return p.perm_list[i]; });
@@ -506,7 +530,7 @@ struct Sched {
         const int mt = pl / p.pch, c = pl % p.pch;
         S::permute(p, mt, c);
         *t_body = rtc();
-        if (arrive_last(p.cnt_perm + mt, -1, 1, s_tmp) && dyn) {
+        if (arrive_last(p, p.cnt_perm + mt, -1, 1, s_tmp) && dyn) {
           if (affinity(p)) {
             // one thread per column tile, into XCD n % 8's queue
             const int n = tidx();
@@ -531,7 +555,7 @@ struct Sched {
         S::up(p, mt, n, smem);
         *t_body = rtc();
         const int ks = slice_of(n, p.n_up_n, p.splitk);
-        if (arrive_last(p.cnt_down + mt * p.splitk + ks, -1, 1, s_tmp) && dyn)
+        if (arrive_last(p, p.cnt_down + mt * p.splitk + ks, -1, 1, s_tmp) && dyn)
           push_burst(p, qcont(p), p.n_down_n, s_tmp, [&](int nn) {
             return make_task(TK_DOWN, (mt * p.n_down_n + nn) * p.splitk + ks);
           });
@@ -554,7 +578,7 @@ struct Sched {
         const int sm = pl / p.n_s_up_n;          // s * n_smt + m
         S::shared_up(p, sm / p.n_smt, sm % p.n_smt, n, smem);
         *t_body = rtc();
-        if (arrive_last(p.cnt_sdown + sm, -1, 1, s_tmp) && dyn)
+        if (arrive_last(p, p.cnt_sdown + sm, -1, 1, s_tmp) && dyn)
           push_burst(p, qcont(p), p.n_down_n, s_tmp,
                      [&](int nn) { return make_task(TK_SDOWN, sm * p.n_down_n + nn); });
         break;
@@ -571,7 +595,7 @@ struct Sched {
         S::combine(p, pl / p.n_cc, pl % p.n_cc, smem);
         *t_body = rtc();
         // the last column chunk of a token tile releases its NORM task
-        if (p.fuse_norm && arrive_last(p.cnt_norm + pl / p.n_cc, -1, 1, s_tmp) && dyn)
+        if (p.fuse_norm && arrive_last(p, p.cnt_norm + pl / p.n_cc, -1, 1, s_tmp) && dyn)
           push_burst(p, qcont(p), 1, s_tmp, [&](int) { return make_task(TK_NORM, pl / p.n_cc); });
         break;
       }
@@ -871,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_route(Params p) {
   Stages<Elem>::route(p, rt, blockIdx.x % p.rsk, smem, p.comb_scatter != 0);
   if (p.rsk > 1) {
     __shared__ int s_tmp[8];
-    if (!arrive_last(p.cnt_route + rt, -1, 1, s_tmp)) return;
+    if (!arrive_last(p, p.cnt_route + rt, -1, 1, s_tmp)) return;
     Stages<Elem>::route_finish(p, rt, smem);
   }
 }

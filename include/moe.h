@@ -105,6 +105,10 @@ typedef enum {
                                         first, then the global queue, then steal from other
                                         XCDs (xxqk.cn/news/665650 s4.4).  Not combinable
                                         with XCD_AFFINITY or CONT_PRIORITY (MOE_ERR_ARG) */
+#define MOE_FLAG_PERTURB 0x200u  /* dynamic: race perturbation for tests -- pseudo-random
+                                    sleeps before claims and dependency decrements,
+                                    pushed bursts in reverse order (m.xxqk.cn/news/657744
+                                    s3.3); changes timing only, never results */
 
 /* Return codes. */
 #define MOE_OK 0

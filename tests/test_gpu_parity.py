@@ -404,6 +404,32 @@ def test_claim_batch_and_local_queues(big_tile, local, batch):
                       label="batch8_local%d" % local, flags=fl, claim_batch=8)
 
 
+@pytest.mark.parametrize("variant", ["fifo", "cont_priority", "local_queues", "xcd_affinity"])
+def test_perturbed_schedule(big_tile, variant):
+    """Race perturbation (random sleeps before every claim and dependency
+    decrement, pushed bursts reversed) under each queue policy: the trace
+    still shows every task once and after its producers, and y is
+    bit-identical to the static kernel's (fixed-order combine); the scatter
+    combine with a local expert range is checked against the oracle."""
+    from analysis_util import check_trace
+    from dynamic_task_scheduling_amd import _abi
+    g, n = big_tile
+    fl = _abi.FLAG_PERTURB | {"fifo": 0, "cont_priority": _abi.FLAG_CONT_PRIORITY,
+                              "local_queues": _abi.FLAG_LOCAL_QUEUES,
+                              "xcd_affinity": _abi.FLAG_XCD_AFFINITY}[variant]
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(BIG_TILE, g, mode="dynamic", trace=trace, timeout_ms=3000, row_tile=256,
+                     combine="tasks", flags=fl)
+    y, r = layer(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+    y2 = MoELayer(BIG_TILE, g, mode="static", split="fixed", row_tile=256,
+                  combine="tasks")(g["x"], check_errors=True)
+    assert torch.equal(y, y2)
+    run_and_check(MID_LOCAL, *gen_and_host(MID_LOCAL, "mid_local", 2), "dynamic", "fixed",
+                  label="perturb_" + variant, flags=fl)
+
+
 @pytest.mark.parametrize("combine", ["scatter", "tasks"])
 def test_layers_in_one_launch(combine):
     """moe_layers: several independent layers of different shapes in one
