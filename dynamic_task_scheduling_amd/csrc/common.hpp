@@ -76,8 +76,20 @@ DEV void st_wt(int* p, int v) {
 DEV void st_wt(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A pointer the caller knows is the same in every lane, moved into scalar
+// registers (so buffer descriptors built from it need no per-lane loop).
+template <typename T>
+DEV T* uniform_ptr(T* ptr) {
+  const uint64_t b = (uint64_t)(uintptr_t)ptr;
+  return (T*)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b));
+}
+
 typedef unsigned int u32x4_t __attribute__((__vector_size__(16)));
 // 16 bytes at base + byte_off; base must be 16-byte aligned, byte_off < 2^31.
+// base must be the same in every lane of the wave (the buffer descriptor is
+// scalar): a per-lane base makes the compiler loop over its distinct values.
+// Per-lane addressing goes into byte_off.
 DEV void st_wt16(void* base, uint32_t byte_off, uint4 v) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
   const u32x4_t d = {v.x, v.y, v.z, v.w};

@@ -479,11 +479,22 @@ struct Stages {
           }
         }
         __syncthreads();
-        // exclusive bases out, spread over every thread
-        const int n = El * nr;
+        // exclusive bases out, spread over every thread, four per 16-byte
+        // store (rows of rt_base are 16-byte aligned: hist_ld and r0 are
+        // multiples of 4); a row's last partial quad is stored word by word
+        const int nq4 = (nr + 3) / 4;
+        const int n = El * nq4;
         for (int i = tid; i < n; i += kThreads) {
-          const int e = i / nr, r = i % nr;
-          st_wt(p.rt_base + (size_t)e * p.hist_ld + r0 + r, s_h[e * cwp + r]);
+          const int e = i / nq4, r = (i % nq4) * 4;
+          const int* src = s_h + e * cwp + r;
+          if (r + 4 <= nr) {
+            st_wt16(p.rt_base + r0, (uint32_t)((e * p.hist_ld + r) * 4),
+                    make_uint4((unsigned)src[0], (unsigned)src[1], (unsigned)src[2],
+                               (unsigned)src[3]));
+          } else {
+            int* dst = p.rt_base + (size_t)e * p.hist_ld + r0 + r;
+            for (int u = 0; r + u < nr; ++u) st_wt(dst + u, src[u]);
+          }
         }
         __syncthreads();
       }
@@ -722,9 +733,16 @@ struct Stages {
   // coalesced copies; the local stand-in for expert-parallel dispatch).
   // The chunk's token ids go to LDS first, so every row load of a batch is
   // issued together (one round trip per 64 KB batch).
+  // A row-tile record, every field in scalar registers (the record is the
+  // same for the whole workgroup; derived addresses then stay uniform).
+  static DEV MTile load_mtile(const Params& p, int mt) {
+    const MTile t = p.mtiles[mt];
+    return MTile{uniform(t.e), uniform(t.row0), uniform(t.rows), uniform(t.bm)};
+  }
+
   static TASKFN void permute(const Params& p, int mt, int c) {
     __shared__ int s_tok[128];
-    const MTile t = p.mtiles[mt];
+    const MTile t = load_mtile(p, mt);
     const int r0 = t.row0 + c * p.perm_rows;
     const int r1 = min(t.row0 + t.rows, r0 + p.perm_rows);
     if (tidx() < r1 - r0) s_tok[tidx()] = p.perm[r0 + tidx()];
@@ -747,7 +765,9 @@ struct Stages {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int ii = i0 + u * kThreads;
-        if (ii < total) st_wt16(xp + (size_t)(r0 + ii / cpr) * row_bytes, (ii % cpr) * 16, v[u]);
+        if (ii < total)
+          st_wt16(uniform_ptr(xp + (size_t)r0 * row_bytes),
+                  (uint32_t)((ii / cpr) * row_bytes + (ii % cpr) * 16), v[u]);
       }
     }
     __syncthreads();
@@ -790,7 +810,7 @@ struct Stages {
     constexpr int CPR = kBN * (int)sizeof(Elem) / 16;
     for (int i = tidx(); i < rows * CPR; i += kThreads) {
       const int r = i / CPR, c = i % CPR;
-      st_wt16(Hout + (size_t)r * ldh, c * 16,
+      st_wt16(Hout, (uint32_t)(r * ldh * (int)sizeof(Elem) + c * 16),
               *reinterpret_cast<const uint4*>(st + r * SLD + c * (16 / (int)sizeof(Elem))));
     }
     __syncthreads();
@@ -849,7 +869,7 @@ struct Stages {
       } else {
         for (int i = tidx(); i < rows * CPR; i += kThreads) {
           const int r = i / CPR, c = i % CPR;
-          st_wt16(out + (size_t)r * ldo + m * kBN, c * 16,
+          st_wt16(uniform_ptr(out + m * kBN), (uint32_t)(r * ldo * 4 + c * 16),
                   *reinterpret_cast<const uint4*>(st + r * SLD + c * 4));
         }
       }
@@ -905,7 +925,7 @@ struct Stages {
   }
 
   static TASKFN void up(const Params& p, int mt, int n, char* smem) {
-    const MTile t = p.mtiles[mt];
+    const MTile t = load_mtile(p, mt);
     const Elem* A = reinterpret_cast<const Elem*>(p.Xp) + (size_t)t.row0 * p.d;
     const size_t eo = (size_t)t.e * p.d * p.f + (size_t)n * kBN;
     const Elem* wg = reinterpret_cast<const Elem*>(p.wg) + eo;
@@ -915,7 +935,7 @@ struct Stages {
   }
 
   static TASKFN void down(const Params& p, int mt, int n, int ks, char* smem, bool scat) {
-    const MTile t = p.mtiles[mt];
+    const MTile t = load_mtile(p, mt);
     const int k_lo = slice_lo(ks, p.n_up_n, p.splitk) * kBN;
     const int K = slice_lo(ks + 1, p.n_up_n, p.splitk) * kBN - k_lo;
     const Elem* A = reinterpret_cast<const Elem*>(p.H) + (size_t)t.row0 * p.f + k_lo;
@@ -973,14 +993,15 @@ struct Stages {
   // abstract): a token's output needs every one of its experts, so the task
   // becomes ready only when all DOWN tiles holding its rows have finished.
   // Fixed summation order: y does not depend on the schedule.
-  // A combined y row chunk: written through to memory when a NORM task (on
-  // any XCD) reads it in this launch; otherwise a plain store, left in this
-  // XCD's L2 until the kernel's end-of-launch release writes it back.
-  static DEV void st_y16(const Params& p, float* row, uint32_t byte_off, uint4 v) {
+  // 16 bytes of combined y at base + byte_off (base uniform over the
+  // workgroup): written through to memory when a NORM task (on any XCD)
+  // reads them in this launch; otherwise a plain store, left in this XCD's
+  // L2 until the kernel's end-of-launch release writes it back.
+  static DEV void st_y16(const Params& p, float* base, uint32_t byte_off, uint4 v) {
     if (p.fuse_norm) {
-      st_wt16(row, byte_off, v);
+      st_wt16(base, byte_off, v);
     } else {
-      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(row) + byte_off) = v;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(base) + byte_off) = v;
     }
   }
 
@@ -1085,7 +1106,7 @@ struct Stages {
         const int i = i0 + u * kThreads;
         if (i >= n) continue;
         const int r = i / c4, col = col0 + (i % c4) * 4;
-        st_y16(p, p.y + (size_t)(t0 + r) * p.d, (uint32_t)col * 4u,
+        st_y16(p, uniform_ptr(p.y + (size_t)t0 * p.d), (uint32_t)((r * p.d + col) * 4),
                make_uint4(__float_as_uint(acc[u].x), __float_as_uint(acc[u].y),
                           __float_as_uint(acc[u].z), __float_as_uint(acc[u].w)));
       }
