@@ -754,13 +754,21 @@ struct Stages {
     const size_t row_bytes = (size_t)cpr * 16;
     // 16 loads in flight per thread (64 KB per workgroup): a gather is a
     // latency-bound copy, so bytes in flight set its rate.
+    // (the token of every load is read from LDS first, with one wait, so no
+    // load waits on an LDS read of its own)
     constexpr int U = 16;
     for (int i0 = tidx(); i0 < total; i0 += U * kThreads) {
+      int tok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ii = i0 + u * kThreads;
+        tok[u] = ii < total ? s_tok[ii / cpr] : 0;
+      }
       uint4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int ii = i0 + u * kThreads;
-        if (ii < total) v[u] = x[(size_t)s_tok[ii / cpr] * cpr + ii % cpr];
+        if (ii < total) v[u] = x[(size_t)tok[u] * cpr + ii % cpr];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -1022,24 +1030,37 @@ struct Stages {
     const int n = rows * c4;
     // A combine task is a latency-bound gather and the persistent kernel runs
     // one workgroup per CU, so each thread keeps many loads in flight: CU
-    // (token, float4) items per pass, the first K slice of every slot of all
-    // of them issued before any is used, then each further K slice as one
-    // burst, then the sums; the shared experts' rows and the residual follow
-    // as one more burst (the expert rows' registers are free by then).
+    // (token, float4) items per pass.  Every slot row index of the pass is
+    // read from LDS first (one wait), so no load waits on an LDS read of its
+    // own; then the first K slice of every kept slot of all items is issued
+    // before any is used, then each further K slice as one burst, then the
+    // sums; the shared experts' rows and the residual follow as one more
+    // burst (the expert rows' registers are free by then).
     constexpr int CU = 2;
     for (int i0 = tidx(); i0 < n; i0 += CU * kThreads) {
+      int pos[CU][kMaxK];
+      float wt[CU][kMaxK];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const int i = i0 + u * kThreads;
+        const int r = i / c4;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+          const bool ok = i < n && j < k;
+          pos[u][j] = ok ? s_pos[r * k + j] : -1;
+          wt[u][j] = ok ? s_w[r * k + j] : 0.f;
+        }
+      }
       float4 v[CU][kMaxK];
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const int i = i0 + u * kThreads;
-        const int r = i / c4, col = col0 + (i % c4) * 4;
+        const int col = col0 + (i % c4) * 4;
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
           v[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (i < n && j < k) {
-            const int pos = s_pos[r * k + j];
-            if (pos >= 0) v[u][j] = *reinterpret_cast<const float4*>(p.O + (size_t)pos * p.d + col);
-          }
+          if (pos[u][j] >= 0)
+            v[u][j] = *reinterpret_cast<const float4*>(p.O + (size_t)pos[u][j] * p.d + col);
         }
       }
       // further K slices (only layers with a DOWN split-K and combine tasks)
@@ -1047,12 +1068,12 @@ struct Stages {
 #pragma unroll
         for (int u = 0; u < CU; ++u) {
           const int i = i0 + u * kThreads;
-          const int r = i / c4, col = col0 + (i % c4) * 4;
+          const int col = col0 + (i % c4) * 4;
 #pragma unroll
           for (int j = 0; j < kMaxK; ++j) {
-            const int pos = (i < n && j < k) ? s_pos[r * k + j] : -1;
-            if (pos >= 0) {
-              const float4 b = *reinterpret_cast<const float4*>(p.O + ks * slice + (size_t)pos * p.d + col);
+            if (pos[u][j] >= 0) {
+              const float4 b =
+                  *reinterpret_cast<const float4*>(p.O + ks * slice + (size_t)pos[u][j] * p.d + col);
               v[u][j].x += b.x; v[u][j].y += b.y; v[u][j].z += b.z; v[u][j].w += b.w;
             }
           }
@@ -1062,13 +1083,11 @@ struct Stages {
       float4 acc[CU];
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
-        const int i = i0 + u * kThreads;
-        const int r = i / c4;
         acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
-          if (i < n && j < k && s_pos[r * k + j] >= 0) {
-            const float wj = s_w[r * k + j];
+          if (pos[u][j] >= 0) {
+            const float wj = wt[u][j];
             acc[u].x += wj * v[u][j].x;
             acc[u].y += wj * v[u][j].y;
             acc[u].z += wj * v[u][j].z;
