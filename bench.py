@@ -237,19 +237,21 @@ def measure_modes(run, steps, warmup, modes=("dynamic", "static", "multi_kernel"
 
 
 def ablations(run, steps, warmup):
-    """Scheduler ablations on one workload: the split policy, compute workers
-    stealing permute tasks, per-XCD UP queues, XCD-local continuation queues,
+    """Scheduler ablations on one workload: the permute as separate tasks
+    (the default fuses it into the UP tiles) under each split policy, compute
+    workers stealing permute tasks, per-XCD UP queues, XCD-local continuation queues,
     batched claims, the continuation-priority queue, token bands, and the
     static baseline's synchronisation (grid barriers vs per-task counter
     waits)."""
     from dynamic_task_scheduling_amd import _abi
     D, S, M = "dynamic", "static", "multi_kernel"
+    EP = _abi.FLAG_EXPLICIT_PERMUTE
     variants = [
         # name, mode, split, flags, bands, claim_batch
-        ("dynamic/split=cost_model", D, "cost_model", 0, None, 0),
-        ("dynamic/split=fixed", D, "fixed", 0, None, 0),
-        ("dynamic/split=none", D, "none", 0, None, 0),
-        ("dynamic/steal=0", D, "fixed", _abi.FLAG_NO_STEAL, None, 0),
+        ("dynamic/explicit_permute/split=cost_model", D, "cost_model", EP, None, 0),
+        ("dynamic/explicit_permute/split=fixed", D, "fixed", EP, None, 0),
+        ("dynamic/explicit_permute/split=none", D, "none", EP, None, 0),
+        ("dynamic/explicit_permute/steal=0", D, "fixed", EP | _abi.FLAG_NO_STEAL, None, 0),
         ("dynamic/xcd_affinity", D, "cost_model", _abi.FLAG_XCD_AFFINITY, None, 0),
         ("dynamic/local_queues", D, "cost_model", _abi.FLAG_LOCAL_QUEUES, None, 0),
         ("dynamic/claim_batch=2", D, "cost_model", 0, None, 2),
@@ -413,6 +415,7 @@ def main():
     del run
     torch.cuda.empty_cache()
     if not args.no_others and not args.no_baselines:
+        from dynamic_task_scheduling_amd import _abi
         others = {}
         for cfg in (2, 3, 5):
             if cfg == args.config:
@@ -425,12 +428,17 @@ def main():
                 # (Wm per layer above) against a fixed group and no split
                 sp = {}
                 for split in ("fixed", "none"):
-                    L = r2.layers("dynamic", split)
+                    L = r2.layers("dynamic", split, flags=_abi.FLAG_EXPLICIT_PERMUTE)
                     r2.timed(L, 1, 2)
                     sp[split] = round(r2.timed(L, max(5, args.steps // 2), 2)["mean"], 4)
                     del L
-                sp["cost_model"] = others[r2.wl.name]["ms"]["dynamic"]
-                others[r2.wl.name]["split_ablation_ms"] = sp
+                L = r2.layers("dynamic", "cost_model", flags=_abi.FLAG_EXPLICIT_PERMUTE)
+                r2.timed(L, 1, 2)
+                sp["cost_model"] = round(r2.timed(L, max(5, args.steps // 2), 2)["mean"], 4)
+                sp["mem_workers"] = L[0].last_schedule()["mem_workers"]
+                del L
+                sp["fused_gather"] = others[r2.wl.name]["ms"]["dynamic"]
+                others[r2.wl.name]["explicit_permute_split_ablation_ms"] = sp
             if len(r2.wl.layers) > 1:
                 # the multi-layer persistent kernel: all layers in one launch
                 t1 = time_one_launch(r2, max(5, args.steps // 2), max(2, args.warmup // 2))

@@ -18,6 +18,7 @@ FLAG_FIFO = 0x40
 FLAG_CONT_PRIORITY = 0x80
 FLAG_LOCAL_QUEUES = 0x100
 FLAG_PERTURB = 0x200
+FLAG_EXPLICIT_PERMUTE = 0x400
 
 ERRORS = {
     0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_WORKSPACE", 3: "MOE_ERR_UNSUPPORTED",
@@ -63,7 +64,8 @@ class Info(ctypes.Structure):
                 ("workspace_bytes", c_size_t),
                 ("cost_mfma_flops_per_cu", ctypes.c_float),
                 ("cost_gather_bytes_per_worker", ctypes.c_float),
-                ("cost_hbm_bytes", ctypes.c_float), ("bands", c_int)]
+                ("cost_hbm_bytes", ctypes.c_float), ("bands", c_int),
+                ("gather_fused", c_int)]
 
 
 class Schedule(ctypes.Structure):

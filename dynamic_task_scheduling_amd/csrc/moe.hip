@@ -141,6 +141,11 @@ void make_layout(const moe_desc* d, Layout* L) {
   p.fs = d->n_shared > 0 ? d->f_shared : kBN;
   p.dtype = d->dtype;
   L->esz = d->dtype == MOE_BF16 ? 2 : 4;
+  // the permute is fused into the UP tiles' row loads (x rows gathered
+  // through perm) unless asked for as separate tasks; the bf16 tiles address
+  // x with 32-bit per-lane byte offsets
+  p.gather_a = !(d->flags & MOE_FLAG_EXPLICIT_PERMUTE) &&
+               (d->dtype != MOE_BF16 || (long long)d->T * d->d * 2 + 65536 < (1ll << 32));
   p.n_rt = (d->T + kTB - 1) / kTB;
   p.hist_ld = std::max(4, (p.n_rt + 3) / 4 * 4);
   // router K slices: enough router tasks to occupy the device (~256), each
@@ -245,7 +250,7 @@ void make_layout(const moe_desc* d, Layout* L) {
   L->off_perm_list = take(sizeof(int) * p.max_perm);
   L->off_cnt_comb = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
   L->off_cnt_norm = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
-  L->off_xp = take((size_t)L->esz * Tk * d->d);
+  L->off_xp = take(p.gather_a ? 0 : (size_t)L->esz * Tk * d->d);
   L->off_h = take((size_t)L->esz * Tk * d->f);
   L->off_hs = take((size_t)L->esz * d->n_shared * d->T * (d->n_shared ? d->f_shared : 0));
   L->off_o = take(sizeof(float) * (size_t)p.splitk * Tk * d->d);
@@ -529,6 +534,7 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->cost_gather_bytes_per_worker = L.p.cm_cu_bw;
   info->cost_hbm_bytes = L.p.cm_hbm_bw;
   info->bands = L.p.bands;
+  info->gather_fused = L.p.gather_a;
   return MOE_OK;
 }
 

@@ -94,6 +94,8 @@ struct Params {
   int max_perm;    // capacity of the permute list
   int bands;       // token bands of the row-tile order (1..kMaxBands)
   int n_sup, n_sdown;
+  int gather_a;     // 1: UP tiles gather their rows from x through perm (no
+                    //    permute tasks, no Xp); 0: permute tasks fill Xp
   int comb_scatter; // 1: DOWN tiles scatter-add w * (H Wd) into y (small layers);
                     // 0: DOWN tiles write O rows, combine tasks sum them
   int comb_cols;   // y columns per combine task (divides d)

@@ -468,6 +468,33 @@ struct Sched {
     }
   }
 
+  // All threads, once every POS task is done, with the gather fused into
+  // the UP tiles: push every UP task -- as one burst into the compute
+  // queue, or (XCD affinity) column tile n into XCD n % 8's queue, each
+  // XCD's share written below a tail raised once (bases staged in LDS).
+  static DEV void push_all_up(const Params& p, char* smem, int* s_tmp) {
+    const int n_mt = ld_relaxed(cw(p, CW_NMT));
+    if (!affinity(p)) {
+      push_burst(p, QC, n_mt * p.n_up_n, s_tmp, [&](int i) { return make_task(TK_UP, i); });
+      return;
+    }
+    int* s_base = reinterpret_cast<int*>(smem);
+    publish_fence();
+    if (tidx() < kXcds) {
+      const int x = tidx();
+      s_base[x] = add_relaxed(ucw(p, CW_UTAIL, x), n_mt * ((p.n_up_n - x + kXcds - 1) / kXcds));
+    }
+    __syncthreads();
+    for (int i = tidx(); i < n_mt * p.n_up_n; i += kThreads) {
+      const int mt = i / p.n_up_n, n = i % p.n_up_n, x = n % kXcds;
+      const int per = (p.n_up_n - x + kXcds - 1) / kXcds;   // column tiles of XCD x
+      const int slot = s_base[x] + mt * per + n / kXcds;
+      if (slot < p.q_cap) st_relaxed(p.uslots + (size_t)x * p.q_cap + slot, make_task(TK_UP, i) + 1);
+      else set_error(p, 6 /* MOE_ERR_CAPACITY */);
+    }
+    __syncthreads();
+  }
+
   // Run one task; in dynamic mode also publish it and push what it enables.
   // *t_body receives the clock at the end of the task body, before any
   // publication, so a trace can check producer-end <= consumer-start.
@@ -520,9 +547,14 @@ struct Sched {
           __syncthreads();
         }
         if (arrive_last(p, cw(p, CW_POS_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
-          const int n_perm = ld_relaxed(cw(p, CW_NPERM));
-          const int q = ld_relaxed(cw(p, CW_WMEM)) > 0 ? QM : QC;
-          push_burst(p, q, n_perm, s_tmp, [&](int i) { return p.perm_list[i]; });
+          if (p.gather_a) {
+            // every row's token is known: all UP tiles are ready at once
+            push_all_up(p, smem, s_tmp);
+          } else {
+            const int n_perm = ld_relaxed(cw(p, CW_NPERM));
+            const int q = ld_relaxed(cw(p, CW_WMEM)) > 0 ? QM : QC;
+            push_burst(p, q, n_perm, s_tmp, [&](int i) { return p.perm_list[i]; });
+          }
         }
         break;
       }
@@ -809,6 +841,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
         n_down = n_mt * p.n_down_n * p.splitk;
         st = ST_PERM;
         i = !ref ? w : (w < wm ? w : n_perm);
+        if (n_perm == 0) {      // gather fused into UP: no memory group
+          st = ST_UP;
+          i = w;
+        }
       } else if (st == ST_PERM) {
         if (i < n_perm) {
           task = p.perm_list[i];
@@ -822,7 +858,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
         if (i < n_up) {
           task = make_task(TK_UP, i);
           if (ref) dep = p.cnt_perm + i / p.n_up_n;
-          i += ref ? W - wm : W;
+          i += (ref && n_perm > 0) ? W - wm : W;
           break;
         }
         if (!ref && !grid_barrier(p, gen, s_tmp)) return;
@@ -972,7 +1008,8 @@ hipError_t launch_stage_sequence(const Params& p, hipStream_t s) {
   hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt * p.rsk), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(k_stage_build<Elem>, dim3(1), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(k_stage_pos<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
-  hipLaunchKernelGGL(k_stage_perm<Elem>, dim3(p.max_perm), dim3(kThreads), 0, s, p);
+  if (!p.gather_a)
+    hipLaunchKernelGGL(k_stage_perm<Elem>, dim3(p.max_perm), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(k_stage_up<Elem>, dim3(p.max_mt * p.n_up_n + p.n_sup), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(k_stage_down<Elem>, dim3(p.max_mt * p.n_down_n * p.splitk + p.n_sdown),
                      dim3(kThreads), 0, s, p);

@@ -568,7 +568,7 @@ struct Stages {
       if (tid < El) {
         const int m0 = lo_of(nt, b), m1 = lo_of(nt, b + 1);
         bt = m1 - m0;
-        if (bt > 0) {
+        if (bt > 0 && !p.gather_a) {   // a fused gather has no permute tasks
           const int lastrows = min(p.th, c_r - p.th * (m1 - 1));
           bp = (bt - 1) * p.pch + (lastrows + p.perm_rows - 1) / p.perm_rows;
         }
@@ -616,7 +616,7 @@ struct Stages {
       static_assert(sizeof(MTile) == 16, "MTile is one 16-byte store");
       st_wt16(p.mtiles, (uint32_t)mt * 16u,
               make_uint4((unsigned)e, (unsigned)(s_off[e] + p.th * m), (unsigned)rows, (unsigned)bm));
-      const int npt = (rows + p.perm_rows - 1) / p.perm_rows;
+      const int npt = p.gather_a ? 0 : (rows + p.perm_rows - 1) / p.perm_rows;
       st_wt(p.cnt_perm + mt, npt);
       for (int ks = 0; ks < p.splitk; ++ks)
         st_wt(p.cnt_down + mt * p.splitk + ks,
@@ -640,7 +640,8 @@ struct Stages {
       int wm_choice = 0;
       if (p.split_policy == 0 /* cost model */ && W >= 2) {
         constexpr float kSplitMargin = 0.03f;
-        const float bytes = 2.f * (float)total * (float)p.d * esz;
+        // (a gather fused into the UP tiles leaves no memory-bound tasks)
+        const float bytes = p.gather_a ? 0.f : 2.f * (float)total * (float)p.d * esz;
         auto t_mem = [&](int wm) { return bytes / fminf((float)wm * p.cm_cu_bw, p.cm_hbm_bw); };
         auto t_mfma = [&](int wm) { return tot_cost / (float)(W - wm); };
         int lo = 1, hi = W - 1;        // first wm with t_mem <= t_mfma (hi if none)
@@ -788,15 +789,17 @@ struct Stages {
   }
 
   // UP tile: H[rows, n0:n0+128] = silu(A Wg) * (A Wu), rounded to Elem.
+  // a_idx: row gather (tile row m reads A row a_idx[m]), or nullptr.
   template <int BM>
   static DEV void up_tile(const Elem* A, int lda, int rows, const Elem* wg, const Elem* wu,
-                          int ldb, int K, Elem* Hout, int ldh, char* smem) {
+                          int ldb, int K, Elem* Hout, int ldh, char* smem, const int* a_idx) {
     using TL = typename GemmSel<Elem, BM, 2>::T;
     static_assert(TL::LDS_BYTES <= kSmemTile, "UP tile fits the tile LDS");
     typename TL::Args g;
     g.A = A;
     g.lda = lda;
     g.a_rows = rows;
+    g.a_idx = a_idx;
     g.B[0] = wg;
     g.B[1] = wu;
     g.ldb = ldb;
@@ -926,20 +929,27 @@ struct Stages {
     });
   }
   static DEV void up_any(int bm, const Elem* A, int lda, int rows, const Elem* wg, const Elem* wu,
-                         int ldb, int K, Elem* Hout, int ldh, char* smem) {
+                         int ldb, int K, Elem* Hout, int ldh, char* smem,
+                         const int* a_idx = nullptr) {
     by_class(bm, [&](auto c) __attribute__((always_inline)) {
-      up_tile<decltype(c)::value>(A, lda, rows, wg, wu, ldb, K, Hout, ldh, smem);
+      up_tile<decltype(c)::value>(A, lda, rows, wg, wu, ldb, K, Hout, ldh, smem, a_idx);
     });
   }
 
+  // UP(mt, n).  With the gather fused (p.gather_a) the tile reads its rows
+  // straight from x through the permutation (row r of the expert-contiguous
+  // order is token perm[r]), so no permuted copy Xp is written or read;
+  // otherwise from Xp, which the permute tasks filled.
   static TASKFN void up(const Params& p, int mt, int n, char* smem) {
     const MTile t = load_mtile(p, mt);
-    const Elem* A = reinterpret_cast<const Elem*>(p.Xp) + (size_t)t.row0 * p.d;
+    const Elem* A = p.gather_a ? reinterpret_cast<const Elem*>(p.x)
+                               : reinterpret_cast<const Elem*>(p.Xp) + (size_t)t.row0 * p.d;
+    const int* a_idx = p.gather_a ? p.perm + t.row0 : nullptr;
     const size_t eo = (size_t)t.e * p.d * p.f + (size_t)n * kBN;
     const Elem* wg = reinterpret_cast<const Elem*>(p.wg) + eo;
     const Elem* wu = reinterpret_cast<const Elem*>(p.wu) + eo;
     Elem* H = reinterpret_cast<Elem*>(p.H) + (size_t)t.row0 * p.f + (size_t)n * kBN;
-    up_any(t.bm, A, p.d, t.rows, wg, wu, p.f, p.d, H, p.f, smem);
+    up_any(t.bm, A, p.d, t.rows, wg, wu, p.f, p.d, H, p.f, smem, a_idx);
   }
 
   static TASKFN void down(const Params& p, int mt, int n, int ks, char* smem, bool scat) {

@@ -56,6 +56,8 @@ struct Tile {
     int ldb;
     int n_valid;        // valid columns in [0, 128)
     int K;              // multiple of BK
+    // row gather: tile row m is A row a_idx[m]; nullptr: row m is A row m
+    const int* a_idx = nullptr;
   };
 
   struct Regs {
@@ -73,7 +75,8 @@ struct Tile {
       const int row = (tid >> 3) + 32 * p;
       const int c = tid & 7;
       if (row < g.a_rows)
-        r.a[p] = *reinterpret_cast<const uint4*>(g.A + (size_t)row * g.lda + k0 + c * EPC);
+        r.a[p] = *reinterpret_cast<const uint4*>(g.A + (size_t)(g.a_idx ? g.a_idx[row] : row) * g.lda +
+                                                 k0 + c * EPC);
       else
         r.a[p] = make_uint4(0, 0, 0, 0);
     }

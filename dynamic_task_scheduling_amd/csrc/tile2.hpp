@@ -150,6 +150,9 @@ struct Tile2 {
     int ldb;
     int K;              // multiple of 64
     int b_cols;         // CLAMP_B only: valid columns of B (multiple of 8)
+    // row gather: tile row m is A row a_idx[m] (a_idx[m] * lda * 2 < 2^32
+    // bytes); nullptr: row m is A row m
+    const int* a_idx = nullptr;
   };
 
   // Per-lane constants of one tile run.
@@ -175,7 +178,8 @@ struct Tile2 {
       const int m = 8 * i + (lane >> 3);
       const int c = (lane & 7) ^ swz_a128(m);
       const int mr = m < g.a_rows ? m : g.a_rows - 1;
-      L.a_src[ii] = (uint32_t)mr * (uint32_t)g.lda * 2u + (uint32_t)c * 16u;
+      const int sr = g.a_idx ? g.a_idx[mr] : mr;
+      L.a_src[ii] = (uint32_t)sr * (uint32_t)g.lda * 2u + (uint32_t)c * 16u;
     }
     // B: K rows 4i..4i+3, chunk c of row k at c ^ swz_b(k).
 #pragma unroll

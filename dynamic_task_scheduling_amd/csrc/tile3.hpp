@@ -118,6 +118,9 @@ struct Tile3 {
     const bf16_t* B[NB];
     int ldb;
     int K;              // multiple of 32
+    // row gather: tile row m is A row a_idx[m] (a_idx[m] * lda * 2 < 2^32
+    // bytes); nullptr: row m is A row m
+    const int* a_idx = nullptr;
   };
 
   // Instruction offset of load j: its slice of the region, relative to M0.
@@ -150,7 +153,8 @@ struct Tile3 {
       const int m = 16 * i + (lane >> 2);
       const int c = (lane & 3) ^ swz_a64(m);
       const int mr = m < g.a_rows ? m : g.a_rows - 1;
-      L.a_src[ii] = (uint32_t)mr * (uint32_t)g.lda * 2u + (uint32_t)c * 16u +
+      const int sr = g.a_idx ? g.a_idx[mr] : mr;
+      L.a_src[ii] = (uint32_t)sr * (uint32_t)g.lda * 2u + (uint32_t)c * 16u +
                     (uint32_t)(kBaseBias - load_off(ii));
     }
     // B: instruction i covers K rows 4 i .. 4 i + 3.  The offset of matrix

@@ -105,6 +105,11 @@ typedef enum {
                                         first, then the global queue, then steal from other
                                         XCDs (xxqk.cn/news/665650 s4.4).  Not combinable
                                         with XCD_AFFINITY or CONT_PRIORITY (MOE_ERR_ARG) */
+#define MOE_FLAG_EXPLICIT_PERMUTE 0x400u /* permute (dispatch) as separate memory-bound tasks
+                                           writing Xp, the stage the pages schedule on
+                                           memory workers; default: the gather is fused
+                                           into the UP tiles' row loads (x rows read through
+                                           perm), with no Xp and no permute tasks */
 #define MOE_FLAG_PERTURB 0x200u  /* dynamic: race perturbation for tests -- pseudo-random
                                     sleeps before claims and dependency decrements,
                                     pushed bursts in reverse order (m.xxqk.cn/news/657744
@@ -218,6 +223,8 @@ typedef struct moe_info {
   float cost_gather_bytes_per_worker; /* bytes/s one worker moves in a gather task */
   float cost_hbm_bytes;              /* device bytes/s a streaming tile sustains */
   int bands;            /* token bands of the row-tile order               */
+  int gather_fused;     /* 1: the UP tiles gather x rows themselves (no
+                           permute tasks, no Xp); 0: explicit permute    */
 } moe_info;
 
 /* Bytes of workspace a call with this descriptor needs (0 on a bad

@@ -33,6 +33,9 @@ def check_trace(raw, layer, routing, fused_norm=False):
               SUP: s.n_shared * n_smt * n_sup_n, SDOWN: s.n_shared * n_smt * n_down,
               COMB: 0 if info["combine"] == 1 else n_rt * n_cc,
               NORM: n_rt if fused_norm else 0}
+    fused = bool(info.get("gather_fused", 0))
+    if fused:
+        expect[PERM] = 0
     for k, n in expect.items():
         assert int((kinds == k).sum()) == n, "kind %d ran %d times, expected %d" % (
             k, int((kinds == k).sum()), n)
@@ -94,7 +97,11 @@ def check_trace(raw, layer, routing, fused_norm=False):
         elif k == PERM:
             assert st >= pos_end
         elif k == UP:
+            # the fused gather reads perm (all POS tiles); else its row
+            # tile's permute tasks
             assert st >= perm_end[p // n_up]
+            if fused:
+                assert st >= pos_end, "UP before every POS tile (fused gather)"
         elif k == DOWN:
             ks = p % sk
             mt = p // sk // n_down

@@ -332,23 +332,26 @@ def test_consecutive_calls_new_inputs(mode, split, combine):
         compare_y(y.cpu().numpy(), yo, "bf16")
 
 
+@pytest.mark.parametrize("explicit", [False, True])
 @pytest.mark.parametrize("split", ["cost_model", "none"])
-def test_xcd_affinity(big_tile, split):
-    """Per-XCD UP queues: same results bit for bit, every task once, every
-    task after its producers."""
+def test_xcd_affinity(big_tile, split, explicit):
+    """Per-XCD UP queues (filled all at once after the positions with the
+    fused gather, per row tile by its last permute task otherwise): same
+    results bit for bit, every task once, every task after its producers."""
     from analysis_util import check_trace
     from dynamic_task_scheduling_amd import _abi
     g, n = big_tile
+    fl = _abi.FLAG_XCD_AFFINITY | (_abi.FLAG_EXPLICIT_PERMUTE if explicit else 0)
     trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
     layer = MoELayer(BIG_TILE, g, mode="dynamic", split=split, trace=trace, timeout_ms=3000,
-                     row_tile=256, combine="tasks", flags=_abi.FLAG_XCD_AFFINITY)
+                     row_tile=256, combine="tasks", flags=fl)
     y, r = layer(g["x"], return_routing=True, check_errors=True)
     torch.cuda.synchronize()
     check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
     y2 = MoELayer(BIG_TILE, g, mode="dynamic", row_tile=256, combine="tasks")(g["x"], check_errors=True)
     assert torch.equal(y, y2)
     run_and_check(MID, *gen_and_host(MID, "mid", 1), "dynamic", split, label="mid_aff",
-                  flags=_abi.FLAG_XCD_AFFINITY)
+                  flags=fl)
 
 
 @pytest.mark.parametrize("fifo", [False, True])
@@ -375,6 +378,36 @@ def test_queue_policy_and_bands(big_tile, fifo, bands):
     if bands == 4 and not fifo:
         run_and_check(BIG_TILE, g, n, "dynamic", "cost_model", label="rt256_b4", row_tile=256,
                       combine="tasks")
+
+
+@pytest.mark.parametrize("mode,split", MODES)
+def test_explicit_permute_all_modes(mid, big_tile, mode, split):
+    """The permute (dispatch) as separate memory-bound tasks writing Xp, the
+    stage the pages schedule on memory workers (the default fuses the gather
+    into the UP tiles' row loads): y bit-identical to the fused gather's
+    (the same rows feed the same tiles, summed in the same order) and within
+    tolerance of the oracle; with 256-row tiles the dynamic trace shows every
+    UP tile after its row tile's permute tasks."""
+    from analysis_util import check_trace
+    from dynamic_task_scheduling_amd import _abi
+    fl = _abi.FLAG_EXPLICIT_PERMUTE
+    g, n = mid
+    y_e = run_and_check(MID, g, n, mode, split, label="mid_explicit", combine="tasks", flags=fl)[0]
+    fused = MoELayer(MID, g, mode=mode, split=split, timeout_ms=3000, combine="tasks")
+    assert fused.info["gather_fused"] == 1
+    assert torch.equal(y_e, fused(g["x"], check_errors=True))
+    if mode == "dynamic":
+        gb, _ = big_tile
+        trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+        layer = MoELayer(BIG_TILE, gb, mode="dynamic", split=split, trace=trace, timeout_ms=3000,
+                         row_tile=256, combine="tasks", flags=fl)
+        assert layer.info["gather_fused"] == 0
+        y, r = layer(gb["x"], return_routing=True, check_errors=True)
+        torch.cuda.synchronize()
+        tr = check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+        assert int((tr["kind"] == 3).sum()) > 0, "no permute tasks ran"
+        y2 = MoELayer(BIG_TILE, gb, mode="dynamic", row_tile=256, combine="tasks")(gb["x"])
+        assert torch.equal(y, y2)
 
 
 @pytest.mark.parametrize("local", [False, True])
