@@ -52,7 +52,7 @@ def _rows(path):
 def kernel_stats(args):
     rows = _rows(args.csv)
     total = sum(float(r["TotalDurationNs"]) for r in rows)
-    out = ["# %s on the %s workload: rocprofv3 kernel stats" % (args.kernel, args.workload), "",
+    out = ["# %s on the %s workload: rocprofv3 kernel stats" % (args.kernel.rstrip("<"), args.workload), "",
            "Command (from the repository root, on one MI355X):", "", "    " + args.command, "",
            "Source hash of the kernels profiled: `%s` (sha256 of csrc/*.hip + *.hpp, first 16 hex)."
            % source_sha(), "",
@@ -88,7 +88,7 @@ def traffic(args):
     fs = cbytes / 1024.0 / cf_kib
     ws = cbytes / 1024.0 / cw_kib
     t = (f_kib * fs + w_kib * ws) * 1024.0
-    d = {"workload": args.workload, "kernel": args.kernel, "source_sha": source_sha(),
+    d = {"workload": args.workload, "kernel": args.kernel.rstrip("<"), "source_sha": source_sha(),
          "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
          "dispatches": [len(f), len(w)],
          "copy_calibration": {"bytes": cbytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
@@ -108,7 +108,7 @@ def counters(args):
         n[r["Counter_Name"]].add(r["Dispatch_Id"])
     avg = {c: sum(v.values()) / len(v) for c, v in per.items()}
     out = ["# %s on the %s workload: rocprofv3 counters (per dispatch, averaged)" % (
-        args.kernel, args.workload), "", "Command (from the repository root, on one MI355X):", "",
+        args.kernel.rstrip("<"), args.workload), "", "Command (from the repository root, on one MI355X):", "",
         "    " + args.command, "", "Source hash: `%s`." % source_sha(), "",
         "| Counter | Value |", "|---|---|"]
     for c in sorted(avg):
