@@ -144,6 +144,10 @@ DEV float wave_xor(float v, int o) {
   const int lane = tidx() & 63;
   return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane ^ o) & 63) << 2, __float_as_int(v)));
 }
+DEV int wave_xor_i(int v, int o) {
+  const int lane = tidx() & 63;
+  return __builtin_amdgcn_ds_bpermute(((lane ^ o) & 63) << 2, v);
+}
 DEV int wave_up(int v, int o) {
   const int lane = tidx() & 63;
   return __builtin_amdgcn_ds_bpermute((lane >= o ? lane - o : lane) << 2, v);

@@ -86,7 +86,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   Params p;          // geometry only (pointers filled by carve)
   int esz;
-  size_t off_ctrl, off_slots, off_uslots, off_logits, off_idx, off_w, off_hist, off_rtb, off_counts,
+  size_t off_ctrl, off_slots, off_uslots, off_logits, off_idx, off_w, off_hist, off_counts,
       off_offsets, off_eorder, off_route_part, off_cnt_route, off_perm, off_rw, off_slotpos, off_mtiles, off_cnt_perm,
       off_cnt_down, off_cnt_sdown, off_perm_list, off_cnt_comb, off_cnt_norm, off_xp,
       off_h, off_hs,
@@ -236,7 +236,6 @@ void make_layout(const moe_desc* d, Layout* L) {
   L->off_idx = take(sizeof(int) * Tk);
   L->off_w = take(sizeof(float) * Tk);
   L->off_hist = take(sizeof(int) * (size_t)p.E_loc * p.hist_ld);
-  L->off_rtb = take(sizeof(int) * (size_t)p.E_loc * p.hist_ld);
   L->off_counts = take(sizeof(int) * p.E_loc);
   L->off_offsets = take(sizeof(int) * (p.E_loc + 1));
   L->off_eorder = take(sizeof(int) * p.E_loc);
@@ -270,7 +269,6 @@ void carve(Layout* L, void* ws) {
   p.idx = reinterpret_cast<int*>(b + L->off_idx);
   p.w = reinterpret_cast<float*>(b + L->off_w);
   p.hist = reinterpret_cast<int*>(b + L->off_hist);
-  p.rt_base = reinterpret_cast<int*>(b + L->off_rtb);
   p.counts = reinterpret_cast<int*>(b + L->off_counts);
   p.offsets = reinterpret_cast<int*>(b + L->off_offsets);
   p.eorder = reinterpret_cast<int*>(b + L->off_eorder);

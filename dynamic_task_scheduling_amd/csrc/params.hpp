@@ -80,7 +80,7 @@ struct Params {
   // derived geometry
   int n_rt;        // router / position tiles of 32 tokens
   int rsk;         // router K slices (divides d / 64)
-  int hist_ld;     // row stride of hist / rt_base (n_rt rounded up to 4)
+  int hist_ld;     // row stride of hist (n_rt rounded up to 4)
   int th;          // expert row-tile height: 128 or 256 rows
   int n_up_n;      // f / 128
   int down_nb;     // 128-column blocks per DOWN task: 1 or 2
@@ -131,7 +131,6 @@ struct Params {
   int* idx;        // [T][k]
   float* w;        // [T][k]
   int* hist;       // [E_loc][hist_ld]
-  int* rt_base;    // [E_loc][hist_ld]
   int* counts;     // [E_loc]
   int* offsets;    // [E_loc + 1]
   int* eorder;     // [E_loc] local experts by descending count

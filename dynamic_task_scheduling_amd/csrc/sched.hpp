@@ -944,7 +944,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_build(Params p) {
 
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void k_stage_pos(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[(2 * kThreads + 4) * 4];
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kPosSmem];
   Stages<Elem>::position(p, blockIdx.x, smem);
 }
 

@@ -125,10 +125,10 @@ struct Stages {
   static constexpr int kRouteSmem = kRouteTile + 32 * kMaxE * 4 + 2 * kMaxE * 4;
   static constexpr int kRouteStage = kRouteTile;
   static_assert(kRouteSmem <= kSmemTile, "route LDS");
-  // build(): small tables first, then a histogram staging area
-  static constexpr int kBuildScratch = 16384;
-  static constexpr int kBuildStage = 65536;
-  static constexpr int kBuildSmem = kBuildScratch + kBuildStage;
+  // build(): its tables; position(): its per-expert tables
+  static constexpr int kBuildSmem = 16384;
+  static constexpr int kPosSmem = (7 * kMaxE + 4) * 4;
+  static_assert(kPosSmem <= kBuildSmem, "position LDS");
   static_assert(kBuildSmem <= kSmemTile, "build LDS");
 
   // --------------------------------------------------------------- router
@@ -430,77 +430,47 @@ struct Stages {
     int* s_bp = s_bt + kMaxBands * 257;         // [kMaxBands][257] permute base of (band, rank)
     int* s_w = s_bp + kMaxBands * 257;          // [8] scan / reduction scratch
     float* s_wf = reinterpret_cast<float*>(s_w + 4);
-    int* s_h = reinterpret_cast<int*>(smem + kBuildScratch);   // histogram staging
     const int tid = tidx();
     const int El = p.E_loc;
-    // 1. per-expert counts and per-tile exclusive bases, in column chunks of
-    //    the [El][n_rt] histogram (row stride cwp = cw + 1: the per-expert
-    //    scan reads a column per wave without bank conflicts).
+    // 1. per-expert counts: the row sums of the [El][n_rt] tile histogram,
+    //    tpe consecutive threads per expert, every load of a thread issued
+    //    before any is used (a memory round trip or two in all).  The
+    //    per-tile bases inside an expert's segment are prefix sums of the
+    //    same rows, which each position task takes for its own tile.
     int run = 0;
     {
-      const int C = max(4, min(p.hist_ld, ((kBuildStage / 4) / max(El, 1) - 1) & ~3));
-      for (int r0 = 0; r0 < p.n_rt; r0 += C) {
-        const int cw = min(C, p.hist_ld - r0);
-        const int cwp = cw + 1;
-        const int q4 = cw / 4;
-        const int nq = El * q4;
-        // all loads of the chunk in flight, then into LDS
-        for (int i0 = tid; i0 < nq; i0 += 8 * kThreads) {
-          int4 v[8];
+      int tpe = 64;
+      while (tpe > 1 && tpe * El > kThreads) tpe >>= 1;
+      const int e = tid / tpe, sub = tid % tpe;
+      const int nq = (p.n_rt + 3) / 4;                   // int4 per row (hist_ld % 4 == 0)
+      int sum = 0;
+      if (e < El) {
+        const int4* row = reinterpret_cast<const int4*>(p.hist + (size_t)e * p.hist_ld);
+        for (int q0 = sub; q0 < nq; q0 += 16 * tpe) {
+          int4 v[16];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * kThreads;
-            if (i < nq)
-              v[u] = *reinterpret_cast<const int4*>(p.hist + (size_t)(i / q4) * p.hist_ld + r0 +
-                                                   (i % q4) * 4);
+          for (int u = 0; u < 16; ++u) {
+            const int q = q0 + u * tpe;
+            if (q < nq) v[u] = row[q];
           }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * kThreads;
-            if (i < nq) {
-              int* d = s_h + (i / q4) * cwp + (i % q4) * 4;
-              d[0] = v[u].x; d[1] = v[u].y; d[2] = v[u].z; d[3] = v[u].w;
-            }
+          for (int u = 0; u < 16; ++u) {
+            const int q = q0 + u * tpe, r = 4 * q;
+            if (q < nq)    // columns past n_rt are padding and never written
+              sum += v[u].x + (r + 1 < p.n_rt ? v[u].y : 0) + (r + 2 < p.n_rt ? v[u].z : 0) +
+                     (r + 3 < p.n_rt ? v[u].w : 0);
           }
         }
-        __syncthreads();
-        const int nr = min(cw, p.n_rt - r0);
-        if (tid < El) {
-          int* row = s_h + tid * cwp;
-          for (int r = 0; r < nr; r += 16) {
-            int v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = (r + u < nr) ? row[r + u] : 0;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-              if (r + u < nr) row[r + u] = run;
-              run += v[u];
-            }
-          }
-        }
-        __syncthreads();
-        // exclusive bases out, spread over every thread, four per 16-byte
-        // store (rows of rt_base are 16-byte aligned: hist_ld and r0 are
-        // multiples of 4); a row's last partial quad is stored word by word
-        const int nq4 = (nr + 3) / 4;
-        const int n = El * nq4;
-        for (int i = tid; i < n; i += kThreads) {
-          const int e = i / nq4, r = (i % nq4) * 4;
-          const int* src = s_h + e * cwp + r;
-          if (r + 4 <= nr) {
-            st_wt16(p.rt_base + r0, (uint32_t)((e * p.hist_ld + r) * 4),
-                    make_uint4((unsigned)src[0], (unsigned)src[1], (unsigned)src[2],
-                               (unsigned)src[3]));
-          } else {
-            int* dst = p.rt_base + (size_t)e * p.hist_ld + r0 + r;
-            for (int u = 0; r + u < nr; ++u) st_wt(dst + u, src[u]);
-          }
-        }
-        __syncthreads();
       }
+      for (int o = 1; o < tpe; o <<= 1) sum += wave_xor_i(sum, o);
+      if (e < El && sub == 0) s_cnt[e] = sum;
+      __syncthreads();
+      if (tid < El) run = s_cnt[tid];
+      __syncthreads();
     }
     // 2. offsets (exclusive scan) and expert order by descending count
     if (tid < El) s_cnt[tid] = run;
+    else if (tid < ((El + 7) & ~7)) s_cnt[tid] = -1;   // padding: never outranks an expert
     int total = 0;
     const int off = block_exscan(tid < El ? run : 0, s_w, &total);
     if (tid < El) {
@@ -516,9 +486,14 @@ struct Stages {
     if (tid < El) {
       const int c = run;
       int rank = 0;
-      for (int e = 0; e < El; ++e) {
-        const int ce = s_cnt[e];
-        rank += (ce > c) || (ce == c && e < tid);
+      // eight counts per pass (two 16-byte LDS reads, the same address in
+      // every lane); the padding up to a multiple of 8 holds -1
+      for (int e0 = 0; e0 < El; e0 += 8) {
+        const int4 a = *reinterpret_cast<const int4*>(s_cnt + e0);
+        const int4 b = *reinterpret_cast<const int4*>(s_cnt + e0 + 4);
+        const int ce[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += (ce[u] > c) || (ce[u] == c && e0 + u < tid);
       }
       s_ord[rank] = tid;
       st_wt(p.eorder + rank, tid);
@@ -670,64 +645,113 @@ struct Stages {
   }
 
   // POS(rt): rows of this tile's kept slots, ascending (token, slot) order
-  // inside every expert: row = offsets[e] + rt_base[e][rt] + rank in tile.
-  // One thread per slot (32 tokens x k <= 256 slots): its rank is the number
-  // of earlier slots of the tile with the same expert.
+  // inside every expert: row = offsets[e] + (rows of expert e in tiles
+  // before rt) + rank of the slot among the tile's slots of expert e.
+  // One thread per slot (32 tokens x k <= 256 slots).  The rank inside a
+  // wave comes from the lanes holding the same expert (nine ballots over
+  // the expert id's bits), plus the slots of that expert in earlier waves.
+  // The rows before the tile are the prefix of the expert's histogram row,
+  // read for the experts present in the tile only.
   // Returns (to every thread) how many distinct expert row tiles hold the
   // tile's kept slots: the combine of these tokens waits for exactly those
-  // tiles' DOWN tasks.
+  // tiles' DOWN tasks.  An expert's slots here take the consecutive rows
+  // [pre, pre + count) of its segment, so they meet the row tiles
+  // pre / th .. (pre + count - 1) / th.
   static TASKFN int position(const Params& p, int rt, char* smem) {
     static_assert(kTB * kMaxK <= kThreads, "one thread per slot");
+    static_assert(kMaxE <= 256, "expert id + 1 in nine bits");
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     const int k = p.k;
     const int ns = rows * k;
-    int* s_e = reinterpret_cast<int*>(smem);             // [256]
-    int* s_mt = s_e + kThreads;                          // [256] row tile of each slot
-    int* s_nd = s_mt + kThreads;                         // distinct row tiles
+    const int El = p.E_loc;
+    int* s_wc = reinterpret_cast<int*>(smem);            // [4][kMaxE] slots of e in wave w
+    int* s_pre = s_wc + 4 * kMaxE;                       // [kMaxE] rows of e before the tile
+    int* s_off = s_pre + kMaxE;                          // [kMaxE] segment offset of e
+    int* s_list = s_off + kMaxE;                         // [kMaxE] experts present in the tile
+    int* s_w = s_list + kMaxE;                           // [4] scan scratch
     const int i = tidx();
-    if (i == 0) *s_nd = 0;
+    const int wave = i >> 6, lane = i & 63;
     int e = -1;
     float w = 0.f;
     if (i < ns) {
       e = p.idx[(size_t)t0 * k + i] - p.e_begin;
       w = p.w[(size_t)t0 * k + i];
-      if (e >= p.E_loc) e = -1;
-      if (e < 0) e = -1;
+      if (e >= El || e < 0) e = -1;
     }
-    s_e[i] = e;
-    // this slot's segment base, loaded while the ranks are counted
-    int base = 0, eoff = 0;
-    if (e >= 0) {
-      eoff = p.offsets[e];
-      base = eoff + p.rt_base[(size_t)e * p.hist_ld + rt];
+    const int eoff_i = i < El ? p.offsets[i] : 0;      // in flight with the slot loads
+    for (int j = i; j < 5 * kMaxE; j += kThreads) s_wc[j] = 0;   // s_wc and s_pre
+    __syncthreads();
+    // lanes of this wave holding the same expert (lanes past the tile's
+    // slots hold -1 and match only each other and non-local slots)
+    const int key = e + 1;
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const uint64_t bal = __ballot((key >> b) & 1);
+      same &= ((key >> b) & 1) ? bal : ~bal;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int rank_w = __popcll(same & below);
+    if (e >= 0 && rank_w == 0) s_wc[wave * kMaxE + e] = __popcll(same);
+    if (i < El) s_off[i] = eoff_i;
+    __syncthreads();
+    // experts present: a compact list, then their histogram prefixes
+    int cnt = 0;
+    if (i < El) cnt = s_wc[i] + s_wc[kMaxE + i] + s_wc[2 * kMaxE + i] + s_wc[3 * kMaxE + i];
+    int n_pres = 0;
+    const int li = block_exscan(cnt > 0 ? 1 : 0, s_w, &n_pres);
+    if (cnt > 0) s_list[li] = i;
+    __syncthreads();
+    const int nq = (rt + 3) / 4;                          // int4 of a row prefix
+    const int npairs = n_pres * nq;
+    for (int j0 = i; j0 < npairs; j0 += 8 * kThreads) {
+      int4 v[8];
+      int ee[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * kThreads;
+        ee[u] = j < npairs ? s_list[j / nq] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * kThreads;
+        if (j < npairs)
+          v[u] = *reinterpret_cast<const int4*>(p.hist + (size_t)ee[u] * p.hist_ld + 4 * (j % nq));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * kThreads;
+        if (j < npairs) {
+          const int r = 4 * (j % nq);    // columns rt and later do not count
+          const int s = v[u].x + (r + 1 < rt ? v[u].y : 0) + (r + 2 < rt ? v[u].z : 0) +
+                        (r + 3 < rt ? v[u].w : 0);
+          if (s) atomicAdd(s_pre + ee[u], s);
+        }
+      }
     }
     __syncthreads();
-    int mt = -1;
     if (i < ns) {
       if (e < 0) {
         st_wt(p.slot_pos + (size_t)t0 * k + i, -1);
       } else {
-        int rank = 0;
-        for (int j = 0; j < i; ++j) rank += (s_e[j] == e);
-        const int pos = base + rank;
+        int rank = rank_w;
+        for (int v2 = 0; v2 < wave; ++v2) rank += s_wc[v2 * kMaxE + e];
+        const int pos = s_off[e] + s_pre[e] + rank;
         st_wt(p.perm + pos, t0 + i / k);
         st_wt(p.rw + pos, w);
         st_wt(p.slot_pos + (size_t)t0 * k + i, pos);
-        mt = (e << 16) | ((pos - eoff) / p.th);   // the row tile: (expert, tile of the expert)
       }
     }
-    s_mt[i] = mt;
-    __syncthreads();
-    if (mt >= 0) {
-      bool first = true;
-      for (int j = 0; j < i; ++j) first = first && (s_mt[j] != mt);
-      if (first) atomicAdd(s_nd, 1);
+    // distinct row tiles, summed over the experts present
+    int nd_e = 0;
+    if (cnt > 0) {
+      const int pre = s_pre[i];
+      nd_e = (pre + cnt - 1) / p.th - pre / p.th + 1;
     }
-    __syncthreads();
-    const int nd = uniform(*s_nd);
-    __syncthreads();
-    return nd;
+    int nd = 0;
+    block_exscan(nd_e, s_w, &nd);
+    return uniform(nd);
   }
 
   // PERM(mt, c): Xp[r] = x[perm[r]] for rows chunk c of tile mt (16-byte
