@@ -240,9 +240,9 @@ def ablations(run, steps, warmup):
     """Scheduler ablations on one workload: the permute as separate tasks
     (the default fuses it into the UP tiles) under each split policy, compute
     workers stealing permute tasks, per-XCD UP queues, XCD-local continuation queues,
-    batched claims, the continuation-priority queue, token bands, and the
-    static baseline's synchronisation (grid barriers vs per-task counter
-    waits)."""
+    batched claims, the continuation-priority queue, token bands, router
+    tasks over 32-token tiles instead of 256-token groups, and the static
+    baseline's synchronisation (grid barriers vs per-task counter waits)."""
     from dynamic_task_scheduling_amd import _abi
     D, S, M = "dynamic", "static", "multi_kernel"
     EP = _abi.FLAG_EXPLICIT_PERMUTE
@@ -261,6 +261,7 @@ def ablations(run, steps, warmup):
         ("dynamic/cont_priority", D, "cost_model", _abi.FLAG_CONT_PRIORITY, None, 0),
         ("dynamic/bands=2", D, "cost_model", 0, 2, 0),
         ("dynamic/bands=4", D, "cost_model", 0, 4, 0),
+        ("dynamic/router=32_token_tiles", D, "cost_model", _abi.FLAG_NARROW_ROUTER, None, 0),
         ("static/sync=phase_barrier", S, "fixed", 0, None, 0),
         ("static/sync=ref_count", S, "fixed", _abi.FLAG_REF_SYNC, None, 0),
         ("multi_kernel", M, "none", 0, None, 0),

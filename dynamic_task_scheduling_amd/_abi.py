@@ -19,6 +19,7 @@ FLAG_CONT_PRIORITY = 0x80
 FLAG_LOCAL_QUEUES = 0x100
 FLAG_PERTURB = 0x200
 FLAG_EXPLICIT_PERMUTE = 0x400
+FLAG_NARROW_ROUTER = 0x800
 
 ERRORS = {
     0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_WORKSPACE", 3: "MOE_ERR_UNSUPPORTED",
@@ -65,7 +66,7 @@ class Info(ctypes.Structure):
                 ("cost_mfma_flops_per_cu", ctypes.c_float),
                 ("cost_gather_bytes_per_worker", ctypes.c_float),
                 ("cost_hbm_bytes", ctypes.c_float), ("bands", c_int),
-                ("gather_fused", c_int)]
+                ("gather_fused", c_int), ("route_groups", c_int)]
 
 
 class Schedule(ctypes.Structure):

@@ -11,7 +11,9 @@ import numpy as np
 
 KIND_SHIFT = 27
 KINDS = {1: "ROUTE", 2: "POS", 3: "PERM", 4: "UP", 5: "DOWN", 6: "SUP", 7: "SDOWN",
-         8: "PHASE", 9: "COMB", 10: "NORM"}   # PHASE: scheduler phases (builder steps, router reduction)
+         8: "PHASE", 9: "COMB", 10: "NORM", 11: "RFIN"}
+# PHASE: scheduler phases (builder steps, router reduction); RFIN: the sum of
+# a 256-token router group's K slices and the top-k of one 32-token tile
 CLOCK_HZ = 100e6   # s_memrealtime rate
 
 

@@ -21,9 +21,9 @@ namespace moe {
 // slots, QC with the shared-expert UP tiles; queue totals other than QA's are
 // unknown until the builder publishes them.
 __host__ __device__ inline int ctrl_init(const Params& p, int w) {
-  const int n_route = p.n_rt * p.rsk;
-  if (w == CW_TAIL + QA) return n_route;
-  if (w == CW_TOTAL + QA) return n_route + p.n_rt;
+  const int seeded = p.n_route + (p.route_wide ? p.n_rt : 0);   // router (+ finish) tasks
+  if (w == CW_TAIL + QA) return seeded;
+  if (w == CW_TOTAL + QA) return seeded + p.n_rt;
   if (w == CW_TAIL + QC) return p.n_sup;
   if (w == CW_TOTAL + QM || w == CW_TOTAL + QC || w == CW_TOTAL + QH) return 0x7fffffff;
   if (w >= CW_UTOTAL && w < CW_UTOTAL + kXcds) return 0x7fffffff;
@@ -39,15 +39,19 @@ DEV void reset_body(const Params& p, int gid, int stride) {
   for (int i = gid; i < ncw; i += stride)
     p.ctrl[i] = (i % kCtrlStride == 0) ? ctrl_init(p, i / kCtrlStride) : 0;
   const size_t ns = (size_t)kNumQueues * p.q_cap;
-  const int n_route = p.n_rt * p.rsk;
+  const int n_route = p.n_route;
+  const int n_fin = p.route_wide ? p.n_rt : 0;
   for (size_t i = gid; i < ns; i += stride) {
     const size_t q = i / p.q_cap, j = i % p.q_cap;
     int v = 0;
     if (q == QA && j < (size_t)n_route) v = make_task(TK_ROUTE, (int)j) + 1;
+    else if (q == QA && j < (size_t)(n_route + n_fin)) v = make_task(TK_RFIN, (int)j - n_route) + 1;
     else if (q == QC && j < (size_t)p.n_sup) v = make_task(TK_SUP, (int)j) + 1;
     p.slots[i] = v;
   }
-  for (int i = gid; i < p.n_rt; i += stride) p.cnt_route[i] = p.rsk;
+  // K slices outstanding per router tile (per 256-token group with route_wide)
+  const int n_rc = p.route_wide ? p.n_rg : p.n_rt;
+  for (int i = gid; i < n_rc; i += stride) p.cnt_route[i] = p.rsk;
   const int nsm = p.n_shared * p.n_smt;
   for (int i = gid; i < nsm; i += stride) p.cnt_sdown[i] = p.n_s_up_n + 1;
   // combine tiles: the shared DOWN tiles over their tokens, plus one unit
@@ -148,10 +152,22 @@ void make_layout(const moe_desc* d, Layout* L) {
                (d->dtype != MOE_BF16 || (long long)d->T * d->d * 2 + 65536 < (1ll << 32));
   p.n_rt = (d->T + kTB - 1) / kTB;
   p.hist_ld = std::max(4, (p.n_rt + 3) / 4 * 4);
-  // router K slices: enough router tasks to occupy the device (~256), each
-  // slice at least 256 deep, slices a divisor of d/64, and one tile's
-  // partials small enough to be staged in LDS at once by its reduction
-  {
+  // Router tasks over 256-token groups on the 256-row tile (bf16, E = 128
+  // or 256, at least 8 groups): K slices of a multiple of 32, at most 8,
+  // about 256 tasks in all.  Otherwise over 32-token tiles: K slices enough
+  // for ~256 router tasks, each slice at least 256 deep, slices a divisor of
+  // d/64, and one tile's partials small enough to be staged in LDS at once
+  // by its reduction.
+  p.route_wide = d->dtype == MOE_BF16 && (d->E == 128 || d->E == 256) && d->T >= 2048 &&
+                 !(d->flags & MOE_FLAG_NARROW_ROUTER);
+  p.n_rg = (d->T + 255) / 256;
+  if (p.route_wide) {
+    const int ksteps = d->d / 32;
+    const int want = std::max(1, (256 + p.n_rg - 1) / p.n_rg);
+    p.rsk = 1;
+    for (int sl = 1; sl <= std::min(ksteps, Stages<bf16_t>::kMaxRouteSlicesWide); ++sl)
+      if (ksteps % sl == 0 && sl <= want) p.rsk = sl;
+  } else {
     const int ksteps = d->d / 64;
     const int want = std::max(1, (256 + std::max(p.n_rt, 1) - 1) / std::max(p.n_rt, 1));
     const int stage = d->dtype == MOE_BF16 ? Stages<bf16_t>::kRouteStage : Stages<float>::kRouteStage;
@@ -160,6 +176,7 @@ void make_layout(const moe_desc* d, Layout* L) {
     for (int sl = 1; sl <= ksteps; ++sl)
       if (ksteps % sl == 0 && sl <= want && sl <= max_rsk && d->d / sl >= 256) p.rsk = sl;
   }
+  p.n_route = (p.route_wide ? p.n_rg : p.n_rt) * p.rsk;
   // Expert row tiles: 256 rows for large bf16 layers (the 256 x 256 task
   // reads half the LDS bytes per MFMA flop of a 128-row one), 128 otherwise
   // (small layers need many tasks, and their experts hold few rows).
@@ -215,7 +232,7 @@ void make_layout(const moe_desc* d, Layout* L) {
       break;
     }
   p.n_cc = d->d / p.comb_cols;
-  const long long qa = (long long)p.n_rt * (p.rsk + 1);
+  const long long qa = (long long)p.n_route + (long long)p.n_rt * (p.route_wide ? 2 : 1);
   const long long qc = (long long)p.max_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup +
                        p.n_sdown + p.max_perm + (long long)p.n_rt * p.n_cc;
   p.q_cap = (int)(std::max(qa, qc) + kMaxWorkersBound);
@@ -231,7 +248,9 @@ void make_layout(const moe_desc* d, Layout* L) {
   L->off_slots = take(sizeof(int) * (size_t)kNumQueues * p.q_cap);
   L->off_uslots = take(sizeof(int) * (size_t)kXcds * p.q_cap);
   L->off_logits = take(sizeof(float) * (size_t)d->T * d->E);
-  L->off_route_part = take(p.rsk > 1 ? sizeof(float) * (size_t)p.rsk * p.n_rt * kTB * d->E : 0);
+  L->off_route_part = take(p.route_wide ? sizeof(float) * (size_t)p.rsk * d->T * d->E
+                           : p.rsk > 1  ? sizeof(float) * (size_t)p.rsk * p.n_rt * kTB * d->E
+                                        : 0);
   L->off_cnt_route = take(sizeof(int) * (size_t)std::max(1, p.n_rt));
   L->off_idx = take(sizeof(int) * Tk);
   L->off_w = take(sizeof(float) * Tk);
@@ -523,6 +542,7 @@ int moe_query(const moe_desc* d, moe_info* info) {
   info->max_mtiles = L.p.max_mt;
   info->max_tasks = L.p.q_cap;
   info->route_splits = L.p.rsk;
+  info->route_groups = L.p.route_wide ? L.p.n_rg : 0;
   info->combine_chunks = L.p.n_cc;
   info->row_tile = L.p.th;
   info->combine = L.p.comb_scatter ? MOE_COMBINE_SCATTER : MOE_COMBINE_TASKS;

@@ -7,7 +7,8 @@ namespace moe {
 
 // Task kinds.  A task id packs the kind in bits [30:27] and a payload below.
 enum TaskKind : int {
-  TK_ROUTE = 1,  // payload rt * rsk + ks: router K slice ks of tokens [32 rt, 32 rt + 32)
+  TK_ROUTE = 1,  // payload rt * rsk + ks: router K slice ks of tokens [32 rt, 32 rt + 32);
+                 // with 256-token router groups, g * rsk + ks: of tokens [256 g, 256 g + 256)
   TK_POS = 2,    // payload rt: stable positions of those tokens' slots
   TK_PERM = 3,   // payload mt * pch + c: gather rows chunk c of row-tile mt
   TK_UP = 4,     // payload mt * n_up_n + n: gate/up GEMM + SiLU-gate epilogue
@@ -17,6 +18,7 @@ enum TaskKind : int {
   TK_BUILD = 8,  // (trace only) scheduler phases: payload = kPhase* id
   TK_COMB = 9,   // payload rt * n_cc + cc: y rows of tokens [32 rt, 32 rt + 32), column chunk cc
   TK_NORM = 10,  // payload rt: RMSNorm of the (residual-added) y rows of tokens [32 rt, 32 rt + 32)
+  TK_RFIN = 11,  // payload rt: sum of the router K slices of tokens [32 rt, 32 rt + 32), then top-k
 };
 // Trace phase ids (payload of TK_BUILD records).
 constexpr int kPhaseBuild = 0;          // the whole post-routing builder
@@ -80,6 +82,10 @@ struct Params {
   // derived geometry
   int n_rt;        // router / position tiles of 32 tokens
   int rsk;         // router K slices (divides d / 64)
+  int route_wide;  // 1: router tasks are 256-token groups x K slices on the 256-row
+                  //    tile, each 32-token tile then summed and routed by a TK_RFIN task
+  int n_rg;        // router groups of 256 tokens (route_wide)
+  int n_route;     // router GEMM tasks: n_rt * rsk, or n_rg * rsk (route_wide)
   int hist_ld;     // row stride of hist (n_rt rounded up to 4)
   int th;          // expert row-tile height: 128 or 256 rows
   int n_up_n;      // f / 128
@@ -126,7 +132,8 @@ struct Params {
   int* slots;      // [kNumQueues][q_cap]
   int* uslots;     // [kXcds][q_cap] per-XCD queues (XCD affinity, local queues)
   float* logits;   // [T][E]
-  float* route_part;  // [rsk][T][E] router partial sums (rsk > 1)
+  float* route_part;  // router partial sums (rsk > 1): [n_rt][rsk][32][E], or
+                      // [rsk][T][E] with route_wide
   int* cnt_route;  // [n_rt] router slices still running
   int* idx;        // [T][k]
   float* w;        // [T][k]

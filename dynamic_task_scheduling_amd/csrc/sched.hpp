@@ -495,35 +495,69 @@ struct Sched {
     __syncthreads();
   }
 
+  // A 32-token tile is routed: the last one to finish runs the builder
+  // (dynamic mode; static mode runs it between its stage barriers).
+  static DEV void tile_routed(const Params& p, char* smem, int* s_tmp, bool dyn, int worker) {
+    if (arrive_last(p, cw(p, CW_ROUTE_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
+      const uint64_t tb = rtc();
+      S::build(p, smem, worker);
+      __syncthreads();
+      const uint64_t tp = rtc();
+      publish_build(p, s_tmp);
+      trace_mark(p, kPhaseBuild, worker, tb, tp);
+      trace_mark(p, kPhasePublish, worker, tp, rtc());
+    }
+  }
+
   // Run one task; in dynamic mode also publish it and push what it enables.
   // *t_body receives the clock at the end of the task body, before any
-  // publication, so a trace can check producer-end <= consumer-start.
+  // publication, so a trace can check producer-end <= consumer-start; a
+  // task that first waits for its producers moves *t_start past the wait.
   static DEV void run(const Params& p, int task, char* smem, int* s_tmp, bool dyn,
-                      uint64_t* t_body, int worker) {
+                      uint64_t* t_start, uint64_t* t_body, int worker) {
     const int kind = task_kind(task);
     const int pl = task_payload(task);
     *t_body = 0;
     switch (kind) {
-      case TK_ROUTE: {
-        const int rt = pl / p.rsk;
-        S::route(p, rt, pl % p.rsk, smem, SCAT);
-        *t_body = rtc();
-        if (p.rsk > 1) {
-          // the last K slice of this tile reduces the partials and routes
-          if (!arrive_last(p, p.cnt_route + rt, -1, 1, s_tmp)) break;
-          const uint64_t tf = rtc();
-          S::route_finish(p, rt, smem);
-          trace_mark(p, kPhaseRouteFinish + rt, worker, tf, rtc());
-        }
-        if (arrive_last(p, cw(p, CW_ROUTE_DONE), 1, p.n_rt - 1, s_tmp) && dyn) {
-          const uint64_t tb = rtc();
-          S::build(p, smem, worker);
+      case TK_ROUTE:
+      case TK_RFIN: {
+        // one call site of the builder (tile_routed) for every router path
+        bool routed = true;
+        if (kind == TK_RFIN) {
+          // every router task precedes the finish tasks (in the router
+          // queue and in the static order), so the group's K slices are all
+          // claimed or done by the time this waits for them
+          if (tidx() == 0) s_tmp[0] = wait_zero(p, p.cnt_route + pl / (256 / kTB));
           __syncthreads();
-          const uint64_t tp = rtc();
-          publish_build(p, s_tmp);
-          trace_mark(p, kPhaseBuild, worker, tb, tp);
-          trace_mark(p, kPhasePublish, worker, tp, rtc());
+          const bool ok = uniform(s_tmp[0]) != 0;
+          __syncthreads();
+          if (!ok) break;
+          consume_fence();
+          *t_start = rtc();
+          S::route_finish_wide(p, pl, smem);
+          *t_body = rtc();
+        } else if (p.route_wide) {
+          // a K slice of a 256-token group: its partial is published by the
+          // group's count; the group's TK_RFIN tasks wait for it to reach 0
+          S::route_wide(p, pl / p.rsk, pl % p.rsk, smem, SCAT);
+          *t_body = rtc();
+          arrive_last(p, p.cnt_route + pl / p.rsk, -1, 1, s_tmp);
+          routed = false;
+        } else {
+          const int rt = pl / p.rsk;
+          S::route(p, rt, pl % p.rsk, smem, SCAT);
+          *t_body = rtc();
+          if (p.rsk > 1) {
+            // the last K slice of this tile reduces the partials and routes
+            routed = arrive_last(p, p.cnt_route + rt, -1, 1, s_tmp);
+            if (routed) {
+              const uint64_t tf = rtc();
+              S::route_finish(p, rt, smem);
+              trace_mark(p, kPhaseRouteFinish + rt, worker, tf, rtc());
+            }
+          }
         }
+        if (routed) tile_routed(p, smem, s_tmp, dyn, worker);
         break;
       }
       case TK_POS: {
@@ -743,8 +777,9 @@ DEV void dynamic_worker(const Params& p, char* smem, int* s_tmp, int* s_worker) 
     const uint64_t t_start = rtc();
     uint64_t t_body;
     const int worker = uniform(*s_worker);
-    Sched<Elem, SCAT>::run(pv, v, smem, s_tmp, true, &t_body, worker);
-    trace_record(pv, v, worker, t_req, t_start, t_body);
+    uint64_t t_run = t_start;
+    Sched<Elem, SCAT>::run(pv, v, smem, s_tmp, true, &t_run, &t_body, worker);
+    trace_record(pv, v, worker, t_req, t_run, t_body);
   }
 }
 
@@ -797,8 +832,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
   const int W = p.workers;
   const bool ref = (p.flags & kFlagRefSync) && W >= 2;
   const int wm = max(1, p.fixed_mem > 0 ? min(p.fixed_mem, W - 1) : W / 8);
-  const int n_route = p.n_rt * p.rsk;
-  const int nA = n_route + p.n_sup;
+  const int n_route = p.n_route;
+  const int n_rfin = p.route_wide ? p.n_rt : 0;
+  const int nA = n_route + n_rfin + p.n_sup;
   enum { ST_A, ST_BUILD, ST_POS, ST_PERM, ST_UP, ST_DOWN, ST_COMB, ST_NORM };
   int st = ST_A, i = w, gen = 0;
   int n_mt = 0, n_perm = 0, n_up = 0, n_down = 0;
@@ -809,9 +845,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
     const int* dep = nullptr;
     for (;;) {
       if (st == ST_A) {
-        // router tiles and shared-expert UP tiles
+        // router tasks, the finish tasks of 256-token router groups, and
+        // shared-expert UP tiles
         if (i < nA) {
-          task = i < n_route ? make_task(TK_ROUTE, i) : make_task(TK_SUP, i - n_route);
+          task = i < n_route          ? make_task(TK_ROUTE, i)
+                 : i < n_route + n_rfin ? make_task(TK_RFIN, i - n_route)
+                                        : make_task(TK_SUP, i - n_route - n_rfin);
           i += W;
           break;
         }
@@ -913,9 +952,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_static(Params p) {
       consume_fence();
     }
     const uint64_t t0 = rtc();
-    uint64_t t_body;
-    Sched<Elem, SCAT>::run(params_view(p), task, smem, s_tmp, false, &t_body, w);
-    trace_record(p, task, w, t0, t0, t_body);
+    uint64_t t_run = t0, t_body;
+    Sched<Elem, SCAT>::run(params_view(p), task, smem, s_tmp, false, &t_run, &t_body, w);
+    trace_record(p, task, w, t0, t_run, t_body);
   }
 }
 
@@ -934,6 +973,20 @@ __global__ __launch_bounds__(kThreads) void k_stage_route(Params p) {
     if (!arrive_last(p, p.cnt_route + rt, -1, 1, s_tmp)) return;
     Stages<Elem>::route_finish(p, rt, smem);
   }
+}
+
+// 256-token router groups: the K-slice tasks (the 256-row tile's LDS), then
+// the per-tile finish tasks in a launch of their own.
+template <typename Elem>
+__global__ __launch_bounds__(kThreads, 1) void k_stage_route_wide(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kSmem];
+  Stages<Elem>::route_wide(p, blockIdx.x / p.rsk, blockIdx.x % p.rsk, smem, p.comb_scatter != 0);
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void k_stage_rfin(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[Stages<Elem>::kRouteSmem];
+  Stages<Elem>::route_finish_wide(p, blockIdx.x, smem);
 }
 
 template <typename Elem>
@@ -1005,7 +1058,12 @@ __global__ __launch_bounds__(kThreads) void k_stage_comb(Params p) {
 // stream s; the launch boundaries are its only synchronisation.
 template <typename Elem>
 hipError_t launch_stage_sequence(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_rt * p.rsk), dim3(kThreads), 0, s, p);
+  if (p.route_wide) {
+    hipLaunchKernelGGL(k_stage_route_wide<Elem>, dim3(p.n_route), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_stage_rfin<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(k_stage_route<Elem>, dim3(p.n_route), dim3(kThreads), 0, s, p);
+  }
   hipLaunchKernelGGL(k_stage_build<Elem>, dim3(1), dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL(k_stage_pos<Elem>, dim3(p.n_rt), dim3(kThreads), 0, s, p);
   if (!p.gather_a)

@@ -270,23 +270,26 @@ struct Stages {
     return p.route_part + ((size_t)rt * p.rsk + ks) * kTB * p.E;
   }
 
+  // Scatter-add combine: router slice ks zeroes its share (rows ks, ks +
+  // rsk, ...) of the y rows of its tokens [t0, t0 + rows), which the DOWN
+  // tiles then accumulate into (with a fused residual the rows start from
+  // the residual instead).
+  static DEV void zero_y_rows(const Params& p, int t0, int rows, int ks) {
+    for (int r = ks; r < rows; r += p.rsk) {
+      float* yr = p.y + (size_t)(t0 + r) * p.d;
+      const uint4* rr = p.resid ? reinterpret_cast<const uint4*>(p.resid + (size_t)(t0 + r) * p.d)
+                                : nullptr;
+      for (int i = tidx(); i < p.d / 4; i += kThreads)
+        st_wt16(yr, i * 16, rr ? rr[i] : make_uint4(0, 0, 0, 0));
+    }
+  }
+
   static TASKFN void route(const Params& p, int rt, int ks, char* smem, bool scat) {
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     // the bias load is issued first, so its latency hides under the GEMM
     const float bias_v = (p.rsk == 1 && p.bias && tidx() < p.E) ? p.bias[tidx()] : 0.f;
-    // scatter-add combine: this slice zeroes its share of the tile's y rows
-    // (rows ks, ks + rsk, ...), which the DOWN tiles then accumulate into
-    // (with a fused residual the rows start from the residual instead)
-    if (scat) {
-      for (int r = ks; r < rows; r += p.rsk) {
-        float* yr = p.y + (size_t)(t0 + r) * p.d;
-        const uint4* rr = p.resid ? reinterpret_cast<const uint4*>(p.resid + (size_t)(t0 + r) * p.d)
-                                  : nullptr;
-        for (int i = tidx(); i < p.d / 4; i += kThreads)
-          st_wt16(yr, i * 16, rr ? rr[i] : make_uint4(0, 0, 0, 0));
-      }
-    }
+    if (scat) zero_y_rows(p, t0, rows, ks);
     const int Ks = p.d / p.rsk;
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);     // [32][E]
     float* part = p.rsk > 1 ? route_part_block(p, rt, ks) : nullptr;
@@ -335,6 +338,87 @@ struct Stages {
     route_topk(p, rt, smem);
   }
 
+  // ROUTE(g, ks) with 256-token router groups (bf16, E = 128 or 256): the
+  // router logits of tokens [256 g, 256 g + 256) over K slice ks of rsk, on
+  // the 256-row tile the expert GEMMs use, stored as the fp32 partial
+  // route_part[ks][t][e].  A 32-token router task streams the whole of W_r
+  // (d x E) for 32 tokens; a group task streams its K slice of W_r once for
+  // 256 tokens, an eighth of the router's W_r traffic.  The TK_RFIN tasks of
+  // the group's eight 32-token tiles then sum the slices and route.
+  static TASKFN void route_wide(const Params& p, int g, int ks, char* smem, bool scat) {
+    const int t0 = g * 256;
+    const int rows = min(256, p.T - t0);
+    if (scat) zero_y_rows(p, t0, rows, ks);
+    if constexpr (TR::kBf16) {
+      const int Ks = p.d / p.rsk;
+      const Elem* x = reinterpret_cast<const Elem*>(p.x) + (size_t)t0 * p.d + (size_t)ks * Ks;
+      const Elem* wr = reinterpret_cast<const Elem*>(p.wr) + (size_t)ks * Ks * p.E;
+      float* out = p.route_part + ((size_t)ks * p.T + t0) * p.E;
+      if (p.E == 256) down_tile<256, 2>(x, p.d, rows, wr, p.E, Ks, out, p.E, smem);
+      else down_tile<256, 1>(x, p.d, rows, wr, p.E, Ks, out, p.E, smem);
+    }
+  }
+
+  // RFIN(rt): logits of tokens [32 rt, 32 rt + 32) = the group's K-slice
+  // partials summed in slice order (the same order as route_finish, so the
+  // logits do not depend on which slice finished last), then bias and
+  // top-k.  Each pass reads four whole slices of the tile, every thread's
+  // 4 x IT loads issued before any is used: the loads are unconditional
+  // (items past the tile re-read its last item and are never stored) --
+  // guarded loads each got a wait of their own from the compiler, one
+  // memory round trip per load.
+  static constexpr int kMaxRouteSlicesWide = 8;
+  static TASKFN void route_finish_wide(const Params& p, int rt, char* smem) {
+    constexpr int IT = kTB * kMaxE / 4 / kThreads;     // float4 items per thread
+    const int t0 = rt * kTB;
+    const int rows = min(kTB, p.T - t0);
+    float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
+    float* bias_s = reinterpret_cast<float*>(smem + kRouteTile + 32 * kMaxE * 4 + kMaxE * 4);
+    const float bias_v = (p.bias && tidx() < p.E) ? p.bias[tidx()] : 0.f;
+    const int n4 = rows * p.E / 4;
+    const size_t slice4 = (size_t)p.T * p.E / 4;
+    const float4* src = reinterpret_cast<const float4*>(p.route_part) + (size_t)t0 * p.E / 4;
+    const int tid = tidx();
+    int item[IT];
+    float4 acc[IT];
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      item[j] = min(tid + j * kThreads, n4 - 1);
+      acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    auto add = [&](float4& a, const float4& v) __attribute__((always_inline)) {
+      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    };
+    int ks = 0;
+    for (; ks + 3 < p.rsk; ks += 4) {
+      float4 v[4][IT];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int j = 0; j < IT; ++j) v[s4][j] = src[(ks + s4) * slice4 + item[j]];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int j = 0; j < IT; ++j) add(acc[j], v[s4][j]);
+    }
+    for (; ks < p.rsk; ++ks) {
+      const float4* s0 = src + ks * slice4;
+      float4 v0[IT];
+#pragma unroll
+      for (int j = 0; j < IT; ++j) v0[j] = s0[item[j]];
+#pragma unroll
+      for (int j = 0; j < IT; ++j) add(acc[j], v0[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < n4) *reinterpret_cast<float4*>(Ls + 4 * i) = acc[j];
+    }
+    if (tid < p.E) bias_s[tid] = bias_v;
+    __syncthreads();
+    route_topk(p, rt, smem);
+  }
+
   // Bias, exported logits, top-k and the tile histogram from Ls (the bias
   // already staged in LDS).
   static DEV void route_topk(const Params& p, int rt, char* smem) {
@@ -345,10 +429,19 @@ struct Stages {
     const float* bias_s = reinterpret_cast<const float*>(hist_s + kMaxE);
     for (int e = tidx(); e < p.E_loc; e += kThreads) hist_s[e] = 0;
     __syncthreads();
-    for (int i = tidx(); i < rows * p.E; i += kThreads) {
-      const float v = Ls[i] + bias_s[i % p.E];
-      Ls[i] = v;
-      p.logits[(size_t)t0 * p.E + i] = v;
+    // element i = r * E + c; the thread's column advances by 256 mod E per
+    // pass (no integer division per element)
+    {
+      const int E = p.E;
+      const int step = kThreads % E;
+      int c = tidx() % E;
+      for (int i = tidx(); i < rows * E; i += kThreads) {
+        const float v = Ls[i] + bias_s[c];
+        Ls[i] = v;
+        p.logits[(size_t)t0 * E + i] = v;
+        c += step;
+        if (c >= E) c -= E;
+      }
     }
     __syncthreads();
     topk(p, t0, rows, Ls, p.E, hist_s);

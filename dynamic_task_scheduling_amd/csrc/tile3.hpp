@@ -44,6 +44,11 @@
 
 namespace moe {
 
+DEV uint64_t uniform_u64(uint64_t v) {
+  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+}
+
 // One 16-byte global->LDS load per lane from sbase + voff + OFF to the LDS
 // address M0 + OFF (+ 16 * lane), M0 left as the caller set it.  Only the
 // 256-row tile's K loop, which contains nothing else that reads or writes
@@ -51,7 +56,11 @@ namespace moe {
 template <int OFF>
 DEV void dma16_m0(uint32_t voff, uint64_t sbase) {
   static_assert(OFF >= -4096 && OFF < 4096, "13-bit signed instruction offset");
-  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(sbase), "i"(OFF));
+  // sbase is wave-uniform by construction; re-asserting it keeps the
+  // operand in SGPRs where the compiler's uniformity analysis loses track
+  // (a no-op for a value already in SGPRs)
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(uniform_u64(sbase)),
+               "i"(OFF));
 }
 
 // The same load, first setting M0 = lds (wave-uniform).  s_nop 0 is the one
@@ -60,7 +69,7 @@ template <int OFF>
 DEV void dma16_set_m0(uint32_t lds, uint32_t voff, uint64_t sbase) {
   static_assert(OFF >= -4096 && OFF < 4096, "13-bit signed instruction offset");
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3" ::"s"(lds),
-               "v"(voff), "s"(sbase), "i"(OFF));
+               "v"(voff), "s"(uniform_u64(sbase)), "i"(OFF));
 }
 
 DEV uint32_t save_m0() {
@@ -69,11 +78,6 @@ DEV uint32_t save_m0() {
   return v;
 }
 DEV void restore_m0(uint32_t v) { asm volatile("s_mov_b32 m0, %0" ::"s"(v)); }
-
-DEV uint64_t uniform_u64(uint64_t v) {
-  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
-         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-}
 
 template <int NB>
 struct Tile3 {

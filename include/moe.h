@@ -110,6 +110,9 @@ typedef enum {
                                            memory workers; default: the gather is fused
                                            into the UP tiles' row loads (x rows read through
                                            perm), with no Xp and no permute tasks */
+#define MOE_FLAG_NARROW_ROUTER 0x800u /* router tasks over 32-token tiles (each streams all
+                                         of W_r) even where 256-token router groups
+                                         apply (bf16, E = 128 or 256, T >= 2048) */
 #define MOE_FLAG_PERTURB 0x200u  /* dynamic: race perturbation for tests -- pseudo-random
                                     sleeps before claims and dependency decrements,
                                     pushed bursts in reverse order (m.xxqk.cn/news/657744
@@ -225,6 +228,9 @@ typedef struct moe_info {
   int bands;            /* token bands of the row-tile order               */
   int gather_fused;     /* 1: the UP tiles gather x rows themselves (no
                            permute tasks, no Xp); 0: explicit permute    */
+  int route_groups;     /* router tasks over 256-token groups (each group's
+                           route_splits K slices, then one finish task per
+                           32-token tile); 0: over 32-token router tiles */
 } moe_info;
 
 /* Bytes of workspace a call with this descriptor needs (0 on a bad

@@ -6,7 +6,7 @@ import numpy as np
 
 from dynamic_task_scheduling_amd.analysis import decode_trace
 
-ROUTE, POS, PERM, UP, DOWN, SUP, SDOWN, COMB, NORM = 1, 2, 3, 4, 5, 6, 7, 9, 10
+ROUTE, POS, PERM, UP, DOWN, SUP, SDOWN, COMB, NORM, RFIN = 1, 2, 3, 4, 5, 6, 7, 9, 10, 11
 
 
 def check_trace(raw, layer, routing, fused_norm=False):
@@ -28,7 +28,10 @@ def check_trace(raw, layer, routing, fused_norm=False):
     n_smt = (s.T + th - 1) // th
     n_sup_n = (s.f_shared // 128) if s.n_shared else 0
     n_cc = info["combine_chunks"]
-    expect = {ROUTE: n_rt * info["route_splits"], POS: n_rt, UP: n_mt * n_up,
+    n_rg = info["route_groups"]      # 256-token router groups (0: 32-token router tiles)
+    rsk = info["route_splits"]
+    expect = {ROUTE: (n_rg if n_rg else n_rt) * rsk, RFIN: n_rt if n_rg else 0, POS: n_rt,
+              UP: n_mt * n_up,
               DOWN: n_mt * n_down * sk,
               SUP: s.n_shared * n_smt * n_sup_n, SDOWN: s.n_shared * n_smt * n_down,
               COMB: 0 if info["combine"] == 1 else n_rt * n_cc,
@@ -41,7 +44,12 @@ def check_trace(raw, layer, routing, fused_norm=False):
             k, int((kinds == k).sum()), n)
     start = {int(t): int(v) for t, v in zip(tr["task"], tr["t_start"])}
     end = {int(t): int(v) for t, v in zip(tr["task"], tr["t_end"])}
-    route_end = max(int(e) for e, k in zip(tr["t_end"], kinds) if k == ROUTE)
+    # routing is done when every router task (and every group finish) is
+    route_end = max(int(e) for e, k in zip(tr["t_end"], kinds) if k in (ROUTE, RFIN))
+    group_end = defaultdict(int)   # 256-token router group -> latest K-slice end
+    for t, k, p in zip(tr["task"], kinds, pl):
+        if k == ROUTE and n_rg:
+            group_end[int(p) // rsk] = max(group_end[int(p) // rsk], end[int(t)])
     pos_end = max(end[(POS << 27) | i] for i in range(n_rt))
     perm_end = defaultdict(int)
     for t, k, p in zip(tr["task"], kinds, pl):
@@ -92,7 +100,9 @@ def check_trace(raw, layer, routing, fused_norm=False):
     for t, k, p in zip(tr["task"], kinds, pl):
         t, p = int(t), int(p)
         st = start[t]
-        if k == POS:
+        if k == RFIN:
+            assert st >= group_end[p // 8], "RFIN before one of its group's K slices"
+        elif k == POS:
             assert st >= route_end
         elif k == PERM:
             assert st >= pos_end

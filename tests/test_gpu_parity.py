@@ -202,6 +202,38 @@ def test_router_256_wide_k_sliced():
         run_and_check(s, g, None, mode, split, label="router256")
 
 
+ROUTER_GROUPS = {
+    128: LayerShape(T=2200, d=512, E=128, k=4, f=128, zipf_s=1.2),
+    256: LayerShape(T=2200, d=768, E=256, k=6, f=128, e_begin=32, e_end=160, zipf_s=1.2),
+}
+
+
+@pytest.mark.parametrize("E", [128, 256])
+def test_router_groups(E):
+    """Router tasks over 256-token groups (nine groups, the last one ragged)
+    on the 256-row tile, their K slices summed per 32-token tile by finish
+    tasks: logits and y against the oracle in every mode; in the dynamic
+    kernel the trace shows each finish task after its group's K slices and
+    every position task after the last finish; the 32-token router on the
+    same inputs matches the oracle too."""
+    from analysis_util import check_trace
+    from dynamic_task_scheduling_amd import _abi
+    s = ROUTER_GROUPS[E]
+    g, n = gen_and_host(s, "router_groups%d" % E, 21)
+    layer = MoELayer(s, g)
+    assert layer.info["route_groups"] == 9 and layer.info["route_splits"] > 1
+    for mode, split in (("dynamic", "cost_model"), ("static", "fixed"), ("multi_kernel", "none")):
+        run_and_check(s, g, n, mode, split, label="router_groups%d" % E)
+    trace = torch.zeros(4 * 20000, dtype=torch.int64, device="cuda")
+    layer = MoELayer(s, g, mode="dynamic", trace=trace, timeout_ms=3000)
+    y, r = layer(g["x"], return_routing=True, check_errors=True)
+    torch.cuda.synchronize()
+    check_trace(trace.cpu().numpy().reshape(-1, 4).view(np.uint64), layer, r)
+    assert MoELayer(s, g, flags=_abi.FLAG_NARROW_ROUTER).info["route_groups"] == 0
+    run_and_check(s, g, n, "dynamic", "cost_model", label="router_narrow%d" % E,
+                  flags=_abi.FLAG_NARROW_ROUTER)
+
+
 def test_split_k_uneven():
     s = LayerShape(T=96, d=256, E=4, k=2, f=1024, zipf_s=0.5)
     g = gen_inputs(s, "splitk", 3)
