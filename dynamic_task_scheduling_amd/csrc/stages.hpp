@@ -1271,34 +1271,60 @@ struct Stages {
   // not depend on the schedule.  `coherent`: y was accumulated with atomics
   // (scatter combine), so it is read with device-coherent loads.
   static TASKFN void norm(const Params& p, int rt, bool coherent) {
+    if (coherent) norm_rows<true>(p, rt);
+    else norm_rows<false>(p, rt);
+  }
+  template <bool COHERENT>
+  static DEV void norm_rows(const Params& p, int rt) {
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     const int wave = tidx() >> 6, lane = tidx() & 63;
+    // one wave per row; a row's float4 chunks in passes of U per lane, the
+    // U loads of a pass unconditional (chunks past the row re-read its last
+    // chunk and are dropped) and in flight together
+    constexpr int U = 8;
+    const int n4 = p.d / 4;
+    auto load = [&](const float* yr, int c) __attribute__((always_inline)) {
+      if constexpr (COHERENT) return ld_coherent4(yr + 4 * c);
+      else return *reinterpret_cast<const float4*>(yr + 4 * c);
+    };
     for (int r = wave; r < rows; r += kThreads / 64) {
       const float* yr = p.y + (size_t)(t0 + r) * p.d;
       float ss = 0.f;
-      for (int c = lane * 4; c < p.d; c += 256) {
-        const float4 v = coherent ? ld_coherent4(yr + c) : *reinterpret_cast<const float4*>(yr + c);
-        ss += v.x * v.x;
-        ss += v.y * v.y;
-        ss += v.z * v.z;
-        ss += v.w * v.w;
+      for (int c0 = 0; c0 < n4; c0 += 64 * U) {
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = load(yr, min(c0 + u * 64 + lane, n4 - 1));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (c0 + u * 64 + lane < n4)
+            ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) ss += wave_xor(ss, o);
       const float scale = 1.0f / sqrtf(ss / (float)p.d + p.norm_eps);
       Elem* out = reinterpret_cast<Elem*>(p.y_norm) + (size_t)(t0 + r) * p.d;
-      for (int c = lane * 4; c < p.d; c += 256) {
-        const float4 v = coherent ? ld_coherent4(yr + c) : *reinterpret_cast<const float4*>(yr + c);
-        const float4 g = *reinterpret_cast<const float4*>(p.norm_w + c);
-        const float o0 = v.x * scale * g.x, o1 = v.y * scale * g.y;
-        const float o2 = v.z * scale * g.z, o3 = v.w * scale * g.w;
-        if constexpr (TR::kBf16) {
-          *reinterpret_cast<uint2*>(out + c) =
-              make_uint2((uint32_t)f2bf(o0) | ((uint32_t)f2bf(o1) << 16),
-                         (uint32_t)f2bf(o2) | ((uint32_t)f2bf(o3) << 16));
-        } else {
-          *reinterpret_cast<float4*>(out + c) = make_float4(o0, o1, o2, o3);
+      for (int c0 = 0; c0 < n4; c0 += 64 * U) {
+        float4 v[U], g[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = min(c0 + u * 64 + lane, n4 - 1);
+          v[u] = load(yr, c);
+          g[u] = *reinterpret_cast<const float4*>(p.norm_w + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c >= n4) continue;
+          const float o0 = v[u].x * scale * g[u].x, o1 = v[u].y * scale * g[u].y;
+          const float o2 = v[u].z * scale * g[u].z, o3 = v[u].w * scale * g[u].w;
+          if constexpr (TR::kBf16) {
+            *reinterpret_cast<uint2*>(out + 4 * c) =
+                make_uint2((uint32_t)f2bf(o0) | ((uint32_t)f2bf(o1) << 16),
+                           (uint32_t)f2bf(o2) | ((uint32_t)f2bf(o3) << 16));
+          } else {
+            *reinterpret_cast<float4*>(out + 4 * c) = make_float4(o0, o1, o2, o3);
+          }
         }
       }
     }
