@@ -155,9 +155,8 @@ void make_layout(const moe_desc* d, Layout* L) {
   // Router tasks over 256-token groups on the 256-row tile (bf16, E = 128
   // or 256, at least 8 groups): K slices of a multiple of 32, at most 8,
   // about 256 tasks in all.  Otherwise over 32-token tiles: K slices enough
-  // for ~256 router tasks, each slice at least 256 deep, slices a divisor of
-  // d/64, and one tile's partials small enough to be staged in LDS at once
-  // by its reduction.
+  // for ~256 router tasks, each slice at least 256 deep and a divisor of
+  // d/64.
   p.route_wide = d->dtype == MOE_BF16 && (d->E == 128 || d->E == 256) && d->T >= 2048 &&
                  !(d->flags & MOE_FLAG_NARROW_ROUTER);
   p.n_rg = (d->T + 255) / 256;
@@ -170,11 +169,9 @@ void make_layout(const moe_desc* d, Layout* L) {
   } else {
     const int ksteps = d->d / 64;
     const int want = std::max(1, (256 + std::max(p.n_rt, 1) - 1) / std::max(p.n_rt, 1));
-    const int stage = d->dtype == MOE_BF16 ? Stages<bf16_t>::kRouteStage : Stages<float>::kRouteStage;
-    const int max_rsk = std::max(1, stage / (kTB * d->E * 4));
     p.rsk = 1;
     for (int sl = 1; sl <= ksteps; ++sl)
-      if (ksteps % sl == 0 && sl <= want && sl <= max_rsk && d->d / sl >= 256) p.rsk = sl;
+      if (ksteps % sl == 0 && sl <= want && d->d / sl >= 256) p.rsk = sl;
   }
   p.n_route = (p.route_wide ? p.n_rg : p.n_rt) * p.rsk;
   // Expert row tiles: 256 rows for large bf16 layers (the 256 x 256 task

@@ -196,8 +196,6 @@ DEV int claim(const Params& p, int q, Reserve& r, bool steal) {
       htot = ld_relaxed(cw(p, CW_TOTAL + QH));
       if (r.h >= 0) vh = ld_relaxed(p.slots + (size_t)QH * p.q_cap + r.h);
     }
-    const int err = ld_relaxed(cw(p, CW_ERROR));
-    if (err != 0) return kClaimAbort;
     if (vh != 0) {                     // the reserved continuation task is there
       r.h = -1;
       return vh - 1;
@@ -218,9 +216,13 @@ DEV int claim(const Params& p, int q, Reserve& r, bool steal) {
       r.pb = add_relaxed(cw(p, CW_HEAD + q), batch);
       r.pe = r.pb + batch;
     }
+    // the slot, the queue's total and the error word in one round trip
+    // (after the head increment, not before it: a claim is two round trips)
     const int h = r.pb;
     const int v = h < p.q_cap ? ld_relaxed(p.slots + (size_t)q * p.q_cap + h) : 0;
     const int total = ld_relaxed(cw(p, CW_TOTAL + q));
+    const int err = ld_relaxed(cw(p, CW_ERROR));
+    if (err != 0) return kClaimAbort;
     if (v != 0) {            // a filled slot is always below the total
       ++r.pb;
       return v - 1;
@@ -394,12 +396,17 @@ DEV void push_tile_ready(const Params& p, int rt, bool scat) {
 // next tasks (dynamic mode).  An expert's rows are sorted by token, so
 // the tile's token tiles are the runs of perm[r] / 32.
 DEV void combine_arrive_rows(const Params& p, int row0, int rows, bool dyn, bool scat) {
+  // the rows' tokens (written long before this task) load while the task's
+  // own stores drain
+  const int r = tidx();
+  int blk = -1, prev = -1;
+  if (r < rows) {
+    blk = p.perm[row0 + r] / kTB;
+    prev = r > 0 ? p.perm[row0 + r - 1] / kTB : -1;
+  }
   publish_fence();
   __syncthreads();
-  const int r = tidx();
   if (r < rows) {
-    const int blk = p.perm[row0 + r] / kTB;
-    const int prev = r > 0 ? p.perm[row0 + r - 1] / kTB : -1;
     if (blk != prev) {
       perturb(p, 0x3000u + blk);
       if (add_relaxed(p.cnt_comb + blk, -1) == 1 && dyn) push_tile_ready(p, blk, scat);
@@ -509,20 +516,43 @@ struct Sched {
     }
   }
 
+  // Thread 0 of a dynamic worker on the plain compute queue (FIFO; no
+  // continuation-priority, local or per-XCD queues), whose reserved slots
+  // are used up: increment the compute queue's head for its next claim now,
+  // before this task's publication, so that the increment's round trip
+  // overlaps the publication's store drain; the claim then only reads the
+  // slot.  Returns the first reserved slot, or -1.
+  static DEV int pre_reserve(const Params& p, const int* s_tmp, bool pre) {
+    if (!pre || tidx() != 0 || s_tmp[4] < s_tmp[5]) return -1;
+    return add_relaxed(cw(p, CW_HEAD + QC), p.claim_batch);
+  }
+  static DEV void pre_commit(const Params& p, int* s_tmp, int slot) {
+    if (tidx() == 0 && slot >= 0) {
+      s_tmp[4] = slot;
+      s_tmp[5] = slot + p.claim_batch;
+    }
+  }
+
   // Run one task; in dynamic mode also publish it and push what it enables.
   // *t_body receives the clock at the end of the task body, before any
   // publication, so a trace can check producer-end <= consumer-start; a
   // task that first waits for its producers moves *t_start past the wait.
+  // pre: this worker claims from the plain compute queue (see pre_reserve).
   static DEV void run(const Params& p, int task, char* smem, int* s_tmp, bool dyn,
-                      uint64_t* t_start, uint64_t* t_body, int worker) {
+                      uint64_t* t_start, uint64_t* t_body, int worker, bool pre = false) {
+    int slot = -1;   // pre-reserved compute-queue slot (thread 0)
     const int kind = task_kind(task);
     const int pl = task_payload(task);
     *t_body = 0;
     switch (kind) {
       case TK_ROUTE:
       case TK_RFIN: {
-        // one call site of the builder (tile_routed) for every router path
+        // one call site each of the partial summation + top-k and of the
+        // builder (tile_routed) for every router path
         bool routed = true;
+        int fin = -1;                 // tile whose partials are summed here
+        const float* part0 = nullptr;
+        size_t stride = 0;
         if (kind == TK_RFIN) {
           // every router task precedes the finish tasks (in the router
           // queue and in the static order), so the group's K slices are all
@@ -534,8 +564,9 @@ struct Sched {
           if (!ok) break;
           consume_fence();
           *t_start = rtc();
-          S::route_finish_wide(p, pl, smem);
-          *t_body = rtc();
+          fin = pl;
+          part0 = p.route_part + (size_t)pl * kTB * p.E;
+          stride = (size_t)p.T * p.E;
         } else if (p.route_wide) {
           // a K slice of a 256-token group: its partial is published by the
           // group's count; the group's TK_RFIN tasks wait for it to reach 0
@@ -551,11 +582,17 @@ struct Sched {
             // the last K slice of this tile reduces the partials and routes
             routed = arrive_last(p, p.cnt_route + rt, -1, 1, s_tmp);
             if (routed) {
-              const uint64_t tf = rtc();
-              S::route_finish(p, rt, smem);
-              trace_mark(p, kPhaseRouteFinish + rt, worker, tf, rtc());
+              fin = rt;
+              part0 = S::route_part_block(p, rt, 0);
+              stride = (size_t)kTB * p.E;
             }
           }
+        }
+        if (fin >= 0) {
+          const uint64_t tf = rtc();
+          S::route_sum_topk(p, fin, part0, stride, smem);
+          if (kind == TK_RFIN) *t_body = rtc();
+          else trace_mark(p, kPhaseRouteFinish + fin, worker, tf, rtc());
         }
         if (routed) tile_routed(p, smem, s_tmp, dyn, worker);
         break;
@@ -620,6 +657,7 @@ struct Sched {
         const int mt = pl / p.n_up_n, n = pl % p.n_up_n;
         S::up(p, mt, n, smem);
         *t_body = rtc();
+        slot = pre_reserve(p, s_tmp, pre);
         const int ks = slice_of(n, p.n_up_n, p.splitk);
         if (arrive_last(p, p.cnt_down + mt * p.splitk + ks, -1, 1, s_tmp) && dyn)
           push_burst(p, qcont(p), p.n_down_n, s_tmp, [&](int nn) {
@@ -633,6 +671,7 @@ struct Sched {
         const int mt = r / p.n_down_n;
         S::down(p, mt, r % p.n_down_n, ks, smem, SCAT);
         *t_body = rtc();
+        slot = pre_reserve(p, s_tmp, pre);
         if (!SCAT || p.fuse_norm) {
           const MTile t = p.mtiles[mt];
           combine_arrive_rows(p, t.row0, t.rows, dyn, SCAT);
@@ -644,6 +683,7 @@ struct Sched {
         const int sm = pl / p.n_s_up_n;          // s * n_smt + m
         S::shared_up(p, sm / p.n_smt, sm % p.n_smt, n, smem);
         *t_body = rtc();
+        slot = pre_reserve(p, s_tmp, pre);
         if (arrive_last(p, p.cnt_sdown + sm, -1, 1, s_tmp) && dyn)
           push_burst(p, qcont(p), p.n_down_n, s_tmp,
                      [&](int nn) { return make_task(TK_SDOWN, sm * p.n_down_n + nn); });
@@ -654,12 +694,14 @@ struct Sched {
         const int sm = pl / p.n_down_n;
         S::shared_down(p, sm / p.n_smt, sm % p.n_smt, n, smem, SCAT);
         *t_body = rtc();
+        slot = pre_reserve(p, s_tmp, pre);
         if (!SCAT || p.fuse_norm) combine_arrive_shared(p, sm % p.n_smt, dyn, SCAT);
         break;
       }
       case TK_COMB: {
         S::combine(p, pl / p.n_cc, pl % p.n_cc, smem);
         *t_body = rtc();
+        slot = pre_reserve(p, s_tmp, pre);
         // the last column chunk of a token tile releases its NORM task
         if (p.fuse_norm && arrive_last(p, p.cnt_norm + pl / p.n_cc, -1, 1, s_tmp) && dyn)
           push_burst(p, qcont(p), 1, s_tmp, [&](int) { return make_task(TK_NORM, pl / p.n_cc); });
@@ -673,6 +715,7 @@ struct Sched {
       default:
         if (tidx() == 0) set_error(p, 1);
     }
+    pre_commit(p, s_tmp, slot);
     __syncthreads();
   }
 };
@@ -778,7 +821,8 @@ DEV void dynamic_worker(const Params& p, char* smem, int* s_tmp, int* s_worker) 
     uint64_t t_body;
     const int worker = uniform(*s_worker);
     uint64_t t_run = t_start;
-    Sched<Elem, SCAT>::run(pv, v, smem, s_tmp, true, &t_run, &t_body, worker);
+    const bool pre = q == QC && !cont_priority(pv) && !local_queues(pv) && !affinity(pv);
+    Sched<Elem, SCAT>::run(pv, v, smem, s_tmp, true, &t_run, &t_body, worker, pre);
     trace_record(pv, v, worker, t_req, t_run, t_body);
   }
 }

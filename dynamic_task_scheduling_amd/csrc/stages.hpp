@@ -121,9 +121,7 @@ struct Stages {
           : RouteSel<Elem>::T::LDS_BYTES;
   static constexpr int kSmem = kSmemTile;
   // Router LDS: the tile ring, then logits [32][E], histogram [E], bias [E].
-  // route_finish stages a tile's K-slice partials over the (idle) ring.
   static constexpr int kRouteSmem = kRouteTile + 32 * kMaxE * 4 + 2 * kMaxE * 4;
-  static constexpr int kRouteStage = kRouteTile;
   static_assert(kRouteSmem <= kSmemTile, "route LDS");
   // build(): its tables; position(): its per-expert tables
   static constexpr int kBuildSmem = 16384;
@@ -304,38 +302,10 @@ struct Stages {
     }
   }
 
-  // Sum the K-slice partials of tile rt in slice order, then top-k.  Every
-  // partial of the tile is loaded into LDS by one burst of direct
-  // global->LDS loads (one memory round trip), and the bias with them.
+  // Sum the K-slice partials of tile rt (contiguous [rsk][32][E] blocks) in
+  // slice order, then top-k.
   static TASKFN void route_finish(const Params& p, int rt, char* smem) {
-    const int t0 = rt * kTB;
-    const int rows = min(kTB, p.T - t0);
-    float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
-    float* bias_s = reinterpret_cast<float*>(smem + kRouteTile + 32 * kMaxE * 4 + kMaxE * 4);
-    const float bias_v = (p.bias && tidx() < p.E) ? p.bias[tidx()] : 0.f;
-    const int tid = opaque_tid();
-    const int wave = tid >> 6, lane = tid & 63;
-    const int bytes = p.rsk * kTB * p.E * 4;            // <= kRouteStage (host-checked)
-    const char* src = reinterpret_cast<const char*>(route_part_block(p, rt, 0));
-    const int n_inst = (bytes + 1023) / 1024;
-    for (int j = wave; j < n_inst; j += 4) {
-      int off = j * 1024 + lane * 16;
-      if (off >= bytes) off = 0;                        // tail lanes: stay inside the block
-      dma16(src + off, __builtin_amdgcn_readfirstlane(lds_addr(smem + j * 1024)));
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-    const float* st = reinterpret_cast<const float*>(smem);
-    const int n = rows * p.E;
-    const int blk = kTB * p.E;
-    for (int i = tidx(); i < n; i += kThreads) {
-      float v = 0.f;
-      for (int ks = 0; ks < p.rsk; ++ks) v += st[ks * blk + i];
-      Ls[i] = v;
-    }
-    if (tidx() < p.E) bias_s[tidx()] = bias_v;
-    __syncthreads();
-    route_topk(p, rt, smem);
+    route_sum_topk(p, rt, route_part_block(p, rt, 0), (size_t)kTB * p.E, smem);
   }
 
   // ROUTE(g, ks) with 256-token router groups (bf16, E = 128 or 256): the
@@ -360,15 +330,22 @@ struct Stages {
   }
 
   // RFIN(rt): logits of tokens [32 rt, 32 rt + 32) = the group's K-slice
-  // partials summed in slice order (the same order as route_finish, so the
-  // logits do not depend on which slice finished last), then bias and
-  // top-k.  Each pass reads four whole slices of the tile, every thread's
-  // 4 x IT loads issued before any is used: the loads are unconditional
+  // partials summed in slice order (so the logits do not depend on which
+  // slice finished last), then bias and top-k; route_finish does the same
+  // for the 32-token router's partials.  Each pass reads two whole slices
+  // of the tile, every thread's 2 x IT loads issued before any is used:
+  // the loads are unconditional
   // (items past the tile re-read its last item and are never stored) --
   // guarded loads each got a wait of their own from the compiler, one
   // memory round trip per load.
   static constexpr int kMaxRouteSlicesWide = 8;
   static TASKFN void route_finish_wide(const Params& p, int rt, char* smem) {
+    route_sum_topk(p, rt, p.route_part + (size_t)rt * kTB * p.E, (size_t)p.T * p.E, smem);
+  }
+  // Tile rt's logits = sum over ks of the [rows][E] fp32 partial at
+  // part0 + ks * stride (floats), in slice order; then bias and top-k.
+  static DEV void route_sum_topk(const Params& p, int rt, const float* part0, size_t stride,
+                                 char* smem) {
     constexpr int IT = kTB * kMaxE / 4 / kThreads;     // float4 items per thread
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
@@ -376,43 +353,53 @@ struct Stages {
     float* bias_s = reinterpret_cast<float*>(smem + kRouteTile + 32 * kMaxE * 4 + kMaxE * 4);
     const float bias_v = (p.bias && tidx() < p.E) ? p.bias[tidx()] : 0.f;
     const int n4 = rows * p.E / 4;
-    const size_t slice4 = (size_t)p.T * p.E / 4;
-    const float4* src = reinterpret_cast<const float4*>(p.route_part) + (size_t)t0 * p.E / 4;
+    const size_t slice4 = stride / 4;
+    const float4* src = reinterpret_cast<const float4*>(part0);
     const int tid = tidx();
-    int item[IT];
-    float4 acc[IT];
+    if (p.E % 4 != 0) {
+      // router widths that are not a multiple of 4: one float per item
+      const int n = rows * p.E;
+      for (int i = tid; i < n; i += kThreads) {
+        float a = 0.f;
+        for (int ks = 0; ks < p.rsk; ++ks) a += part0[ks * stride + i];
+        Ls[i] = a;
+      }
+    } else {
+      int item[IT];
+      float4 acc[IT];
 #pragma unroll
-    for (int j = 0; j < IT; ++j) {
-      item[j] = min(tid + j * kThreads, n4 - 1);
-      acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    auto add = [&](float4& a, const float4& v) __attribute__((always_inline)) {
-      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-    };
-    int ks = 0;
-    for (; ks + 3 < p.rsk; ks += 4) {
-      float4 v[4][IT];
+      for (int j = 0; j < IT; ++j) {
+        item[j] = min(tid + j * kThreads, n4 - 1);
+        acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      auto add = [&](float4& a, const float4& v) __attribute__((always_inline)) {
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+      };
+      int ks = 0;
+      for (; ks + 1 < p.rsk; ks += 2) {
+        float4 v[2][IT];
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int j = 0; j < IT; ++j) v[s4][j] = src[(ks + s4) * slice4 + item[j]];
+          for (int j = 0; j < IT; ++j) v[s2][j] = src[(ks + s2) * slice4 + item[j]];
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int j = 0; j < IT; ++j) add(acc[j], v[s4][j]);
-    }
-    for (; ks < p.rsk; ++ks) {
-      const float4* s0 = src + ks * slice4;
-      float4 v0[IT];
+          for (int j = 0; j < IT; ++j) add(acc[j], v[s2][j]);
+      }
+      for (; ks < p.rsk; ++ks) {
+        const float4* s0 = src + ks * slice4;
+        float4 v0[IT];
 #pragma unroll
-      for (int j = 0; j < IT; ++j) v0[j] = s0[item[j]];
+        for (int j = 0; j < IT; ++j) v0[j] = s0[item[j]];
 #pragma unroll
-      for (int j = 0; j < IT; ++j) add(acc[j], v0[j]);
-    }
+        for (int j = 0; j < IT; ++j) add(acc[j], v0[j]);
+      }
 #pragma unroll
-    for (int j = 0; j < IT; ++j) {
-      const int i = tid + j * kThreads;
-      if (i < n4) *reinterpret_cast<float4*>(Ls + 4 * i) = acc[j];
+      for (int j = 0; j < IT; ++j) {
+        const int i = tid + j * kThreads;
+        if (i < n4) *reinterpret_cast<float4*>(Ls + 4 * i) = acc[j];
+      }
     }
     if (tid < p.E) bias_s[tid] = bias_v;
     __syncthreads();
