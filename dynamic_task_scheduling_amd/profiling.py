@@ -64,6 +64,17 @@ def kernel_stats(args):
         out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
             _short(name), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / total))
+    if args.trace and args.timed:
+        # per-dispatch durations of the kernel; the last `timed` dispatches
+        # are the timed steps (the ones before them are warm-up)
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in _rows(args.trace)
+             if args.kernel in r["Kernel_Name"]]
+        t = sorted(d[-args.timed:])
+        if t:
+            med = t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+            out += ["", "Timed dispatches of `%s` (the last %d of %d; the rest are warm-up): median %.1f us, "
+                    "mean %.1f us, min %.1f us, max %.1f us." % (args.kernel.rstrip("<"), len(t), len(d), med,
+                                                                  sum(t) / len(t), t[0], t[-1])]
     if args.note:
         out += ["", args.note]
     open(args.out, "w").write("\n".join(out) + "\n")
@@ -144,6 +155,8 @@ def main():
     k.add_argument("--kernel", default="k_dynamic")
     k.add_argument("--command", required=True)
     k.add_argument("--note", default="")
+    k.add_argument("--trace", default="", help="run_kernel_trace.csv of the same run")
+    k.add_argument("--timed", type=int, default=0, help="timed dispatches at the end of the trace")
     k.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--workload", "--out"):

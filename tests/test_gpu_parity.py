@@ -234,6 +234,19 @@ def test_router_groups(E):
                   flags=_abi.FLAG_NARROW_ROUTER)
 
 
+def test_router_groups_scatter_and_fused_tail():
+    """Router groups with the scatter-add combine forced (the group tasks
+    start y rows from zero, or from the residual) and with the fused
+    residual + RMSNorm tail, in the dynamic and static kernels."""
+    s = ROUTER_GROUPS[128]
+    g, n = gen_and_host(s, "router_groups128", 21)
+    run_and_check(s, g, n, "dynamic", "cost_model", combine="scatter", label="groups_scatter")
+    for mode, split in (("dynamic", "cost_model"), ("static", "fixed")):
+        for combine in ("scatter", "tasks"):
+            layer, *_ = check_fused_tail(s, g, n, mode, split, combine, label="groups")
+            assert layer.info["route_groups"] == 9
+
+
 def test_split_k_uneven():
     s = LayerShape(T=96, d=256, E=4, k=2, f=1024, zipf_s=0.5)
     g = gen_inputs(s, "splitk", 3)
