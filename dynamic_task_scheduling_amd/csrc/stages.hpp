@@ -332,31 +332,56 @@ struct Stages {
   // RFIN(rt): logits of tokens [32 rt, 32 rt + 32) = the group's K-slice
   // partials summed in slice order (so the logits do not depend on which
   // slice finished last), then bias and top-k; route_finish does the same
-  // for the 32-token router's partials.  Each pass reads two whole slices
-  // of the tile, every thread's 2 x IT loads issued before any is used:
-  // the loads are unconditional
-  // (items past the tile re-read its last item and are never stored) --
-  // guarded loads each got a wait of their own from the compiler, one
-  // memory round trip per load.
+  // for the 32-token router's partials.
   static constexpr int kMaxRouteSlicesWide = 8;
   static TASKFN void route_finish_wide(const Params& p, int rt, char* smem) {
     route_sum_topk(p, rt, p.route_part + (size_t)rt * kTB * p.E, (size_t)p.T * p.E, smem);
   }
+  // Burst size of the LDS-staged summation (over the idle router-tile ring,
+  // below Ls).
+  static constexpr int kSumBurst = kRouteTile < 65536 ? kRouteTile : 65536;
   // Tile rt's logits = sum over ks of the [rows][E] fp32 partial at
   // part0 + ks * stride (floats), in slice order; then bias and top-k.
+  // When all slices of the tile fit kSumBurst bytes they are staged in LDS
+  // by one burst of direct loads.  Otherwise each thread owns IT float4 items of the tile and reads SL = 16 / IT
+  // slices of them per pass, so 16 loads are in flight per thread whatever
+  // the router width (IT = 8, 4, 2, 1 for E up to 256, 128, 64, 32).  The
+  // loads are unconditional (items past the tile re-read its last item and
+  // are never stored): loads under a per-lane condition were each given a
+  // wait of their own by the compiler, one memory round trip per load.
   static DEV void route_sum_topk(const Params& p, int rt, const float* part0, size_t stride,
                                  char* smem) {
-    constexpr int IT = kTB * kMaxE / 4 / kThreads;     // float4 items per thread
     const int t0 = rt * kTB;
     const int rows = min(kTB, p.T - t0);
     float* Ls = reinterpret_cast<float*>(smem + kRouteTile);
     float* bias_s = reinterpret_cast<float*>(smem + kRouteTile + 32 * kMaxE * 4 + kMaxE * 4);
     const float bias_v = (p.bias && tidx() < p.E) ? p.bias[tidx()] : 0.f;
-    const int n4 = rows * p.E / 4;
-    const size_t slice4 = stride / 4;
-    const float4* src = reinterpret_cast<const float4*>(part0);
     const int tid = tidx();
-    if (p.E % 4 != 0) {
+    const int sb = rows * p.E * 4;                     // bytes of one slice
+    const int sreg = (sb + 1023) & ~1023;              // its LDS region: whole 1 KB loads
+    if (sreg * p.rsk <= kSumBurst) {
+      // every slice of the tile fits one burst of direct global->LDS loads
+      // (a single memory round trip; small router widths): stage them over
+      // the idle router-tile ring, then add them in slice order.  Lanes past
+      // a slice re-load its first bytes into the region's padding.
+      const int wave = tid >> 6, lane = tid & 63;
+      const int ninst = sreg / 1024;
+      for (int j = wave; j < p.rsk * ninst; j += kThreads / 64) {
+        const int sl = j / ninst, q = j % ninst;
+        int off = q * 1024 + lane * 16;
+        if (off >= sb) off = 0;
+        dma16(reinterpret_cast<const char*>(part0 + (size_t)sl * stride) + off,
+              __builtin_amdgcn_readfirstlane(lds_addr(smem + sl * sreg + q * 1024)));
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+      const float* st = reinterpret_cast<const float*>(smem);
+      for (int i = tid; i < rows * p.E; i += kThreads) {
+        float v = 0.f;
+        for (int ks = 0; ks < p.rsk; ++ks) v += st[ks * (sreg / 4) + i];
+        Ls[i] = v;
+      }
+    } else if (p.E % 4 != 0) {
       // router widths that are not a multiple of 4: one float per item
       const int n = rows * p.E;
       for (int i = tid; i < n; i += kThreads) {
@@ -364,46 +389,57 @@ struct Stages {
         for (int ks = 0; ks < p.rsk; ++ks) a += part0[ks * stride + i];
         Ls[i] = a;
       }
+    } else if (p.E > 128) {
+      sum_slices<8>(p, rows, part0, stride, Ls);
+    } else if (p.E > 64) {
+      sum_slices<4>(p, rows, part0, stride, Ls);
+    } else if (p.E > 32) {
+      sum_slices<2>(p, rows, part0, stride, Ls);
     } else {
-      int item[IT];
-      float4 acc[IT];
-#pragma unroll
-      for (int j = 0; j < IT; ++j) {
-        item[j] = min(tid + j * kThreads, n4 - 1);
-        acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      auto add = [&](float4& a, const float4& v) __attribute__((always_inline)) {
-        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-      };
-      int ks = 0;
-      for (; ks + 1 < p.rsk; ks += 2) {
-        float4 v[2][IT];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int j = 0; j < IT; ++j) v[s2][j] = src[(ks + s2) * slice4 + item[j]];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int j = 0; j < IT; ++j) add(acc[j], v[s2][j]);
-      }
-      for (; ks < p.rsk; ++ks) {
-        const float4* s0 = src + ks * slice4;
-        float4 v0[IT];
-#pragma unroll
-        for (int j = 0; j < IT; ++j) v0[j] = s0[item[j]];
-#pragma unroll
-        for (int j = 0; j < IT; ++j) add(acc[j], v0[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < IT; ++j) {
-        const int i = tid + j * kThreads;
-        if (i < n4) *reinterpret_cast<float4*>(Ls + 4 * i) = acc[j];
-      }
+      sum_slices<1>(p, rows, part0, stride, Ls);
     }
     if (tid < p.E) bias_s[tid] = bias_v;
     __syncthreads();
     route_topk(p, rt, smem);
+  }
+  template <int IT>
+  static DEV void sum_slices(const Params& p, int rows, const float* part0, size_t stride,
+                             float* Ls) {
+    constexpr int SL = 16 / IT;
+    const int n4 = rows * p.E / 4;                     // <= IT * kThreads
+    const size_t slice4 = stride / 4;
+    const float4* src = reinterpret_cast<const float4*>(part0);
+    const int tid = tidx();
+    int item[IT];
+    float4 acc[IT];
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      item[j] = min(tid + j * kThreads, n4 - 1);
+      acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int ks = 0; ks < p.rsk; ks += SL) {
+      float4 v[SL][IT];
+#pragma unroll
+      for (int s = 0; s < SL; ++s)
+#pragma unroll
+        for (int j = 0; j < IT; ++j)   // slices past rsk re-read the last one (not added)
+          v[s][j] = src[(size_t)min(ks + s, p.rsk - 1) * slice4 + item[j]];
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        if (ks + s < p.rsk) {
+#pragma unroll
+          for (int j = 0; j < IT; ++j) {
+            acc[j].x += v[s][j].x; acc[j].y += v[s][j].y;
+            acc[j].z += v[s][j].z; acc[j].w += v[s][j].w;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < n4) *reinterpret_cast<float4*>(Ls + 4 * i) = acc[j];
+    }
   }
 
   // Bias, exported logits, top-k and the tile histogram from Ls (the bias
