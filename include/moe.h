@@ -236,7 +236,7 @@ typedef struct moe_info {
 /* Bytes of workspace a call with this descriptor needs (0 on a bad
  * descriptor).  The workspace holds every piece of scheduling state -- queues,
  * dependency counters, task tables -- and the intermediate rows, so the
- * library allocates nothing (the graft/overlap chapter, hncyxsy.com/news/277526,
+ * library allocates nothing (the graph-capture and overlap chapter, hncyxsy.com/news/277526,
  * CUDA Graph section: state resident at fixed addresses, nothing allocated
  * inside a captured region).  Caller-owned, any device allocation, 256-byte
  * aligned; reusable across calls with the same descriptor. */
