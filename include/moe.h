@@ -2,10 +2,13 @@
  * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts megakernel library.
  *
  * One call runs a whole MoE layer on one GPU:
- *   router GEMM -> softmax top-k -> stable count/scan/permute into
- *   expert-contiguous rows -> per-expert SwiGLU GEMM tasks (bf16 MFMA,
- *   fused SiLU-gate epilogue) -> weighted per-token combine of the experts'
- *   output rows (fixed order, no atomics).
+ *   router GEMM -> softmax top-k -> stable count/scan/positions of every
+ *   (token, expert) slot in expert-contiguous order -> per-expert SwiGLU
+ *   GEMM tasks (bf16 MFMA, x rows gathered through the positions in the
+ *   tile's loader, fused SiLU-gate epilogue) -> weighted per-token combine of
+ *   the experts' output rows (fixed order, no atomics; small layers
+ *   scatter-add in the DOWN epilogue instead) -> optionally the residual add
+ *   and RMSNorm (moe_layer_norm).
  *
  * The stages are those the Weave pages place inside one persistent MoE
  * kernel (xxqk.cn/news/665650 section 1; m.xxqk.cn/news/657744 section 2.1).
@@ -13,10 +16,13 @@
  * ready tasks from atomic queues (xxqk.cn/news/665650 section 2.1, the
  * TaskQueue / fetch_task scheme), with per-task dependency counters instead
  * of global barriers (same page, section 2.3; m.xxqk.cn/news/657744 section
- * 2.3), and a post-routing cost model that splits the workers into a
- * memory-bound group (permute = the local stand-in for expert-parallel
- * dispatch) and an MFMA-bound group (expert GEMMs), per the spatial and
- * temporal schedulers of the Weave abstract (arxivdaily.com/papers/2609.21483).
+ * 2.3), and a post-routing cost model that decides whether to split the
+ * workers into a memory-bound group (the gather = the local stand-in for
+ * expert-parallel dispatch, as separate tasks with MOE_FLAG_EXPLICIT_PERMUTE)
+ * and an MFMA-bound group (expert GEMMs), per the spatial and temporal
+ * schedulers of the Weave abstract (arxivdaily.com/papers/2609.21483); with
+ * the gather fused into the GEMM tiles (the default) there is no memory-bound
+ * task to split off.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, row-major, owned by the caller.
