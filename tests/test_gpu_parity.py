@@ -234,6 +234,37 @@ def test_router_groups(E):
                   flags=_abi.FLAG_NARROW_ROUTER)
 
 
+def test_router_groups_ref_sync_and_one_launch():
+    """Router groups in the static kernel with per-task counter waits, and
+    in a multi-layer persistent launch beside a 32-token-router layer: y and
+    the routing tables bit-identical to the layers' own dynamic calls
+    (fixed-order combine), and within the bf16 tolerance of the oracle."""
+    from dynamic_task_scheduling_amd import _abi
+    from dynamic_task_scheduling_amd.moe import MoELayers, alloc_routing
+    s = ROUTER_GROUPS[256]
+    g, n = gen_and_host(s, "router_groups256", 21)
+    run_and_check(s, g, n, "static", "fixed", flags=_abi.FLAG_REF_SYNC, label="groups_ref_sync")
+    small = LayerShape(T=300, d=512, E=16, k=4, f=384, zipf_s=1.0)
+    gs = gen_inputs(small, "groups_small", 22)
+    shapes, inputs = [s, small, s], [g, gs, g]
+    layers = [MoELayer(sh, gi, mode="dynamic", timeout_ms=3000, combine="tasks")
+              for sh, gi in zip(shapes, inputs)]
+    assert layers[0].info["route_groups"] == 9 and layers[1].info["route_groups"] == 0
+    routs = [alloc_routing(sh, torch.device("cuda")) for sh in shapes]
+    ys = MoELayers(layers)([gi["x"] for gi in inputs], routings=routs, check_errors=True)
+    torch.cuda.synchronize()
+    for sh, gi, L, y, r in zip(shapes, inputs, layers, ys, routs):
+        y1, r1 = L(gi["x"], return_routing=True, check_errors=True)
+        torch.cuda.synchronize()
+        for f in ("topk_idx", "expert_counts", "offsets", "slot_pos"):
+            assert torch.equal(getattr(r, f), getattr(r1, f))
+        assert torch.equal(y, y1)
+    ro = oracle.route(routs[0].logits.cpu().numpy(), s.k, s.e_begin, s.local_end)
+    check_routing(routs[0], ro, s)
+    yo = oracle.moe_layer(n["x"], n["w_gate"], n["w_up"], n["w_down"], ro, s.e_begin, None)
+    compare_y(ys[0].cpu().numpy(), yo, "bf16")
+
+
 def test_router_groups_scatter_and_fused_tail():
     """Router groups with the scatter-add combine forced (the group tasks
     start y rows from zero, or from the residual) and with the fused
