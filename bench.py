@@ -15,6 +15,8 @@ ablations follow under extra keys.  Prints ONE JSON line.
 
 `--calibrate-copy MIB` instead runs a plain device copy of known size (the
 reference for scaling the FETCH_SIZE / WRITE_SIZE hardware counters).
+`--vendor-gemm` instead times the vendor BLAS on dense GEMMs with the FLOPs of
+the workload's expert FFNs (a ceiling for comparison, not part of the layer).
 """
 import argparse
 import hashlib
@@ -112,6 +114,41 @@ def calibrate_copy(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_dispatch": n, "reps": 3}), flush=True)
+
+
+def vendor_gemm(R: int, d: int, f: int, steps: int = 10, warmup: int = 3) -> dict:
+    """Dense bf16 GEMMs of the vendor BLAS (torch.matmul) with the FLOPs of one
+    layer's expert FFNs over its R kept rows: [R, d] x [d, 2f], then
+    [R, f] x [f, d].  A comparison point for the expert GEMMs at the clock the
+    chip holds under MFMA load: no gather, no ragged row tiles, no routing or
+    combine, operands of random values.  Never part of the layer's path."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    bf = torch.bfloat16
+    a = torch.randn(R, d, dtype=bf, device="cuda", generator=g)
+    w1 = torch.randn(d, 2 * f, dtype=bf, device="cuda", generator=g)
+    h = torch.randn(R, f, dtype=bf, device="cuda", generator=g)
+    w2 = torch.randn(f, d, dtype=bf, device="cuda", generator=g)
+    out = {}
+    for name, x, w in (("up", a, w1), ("down", h, w2)):
+        for _ in range(warmup):
+            x @ w
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            x @ w
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        fl = 2.0 * x.shape[0] * x.shape[1] * w.shape[1]
+        out[name] = {"shape": [x.shape[0], x.shape[1], w.shape[1]], "ms": round(ms, 4),
+                     "tflops": round(fl / ms / 1e9, 1)}
+    ms = out["up"]["ms"] + out["down"]["ms"]
+    fl = 6.0 * R * d * f
+    out.update({"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                "pct_mfma_peak": round(100.0 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 1)})
+    return out
 
 
 class Runner:
@@ -333,6 +370,8 @@ def main():
                     help="modes timed by --profile-only, comma-separated, in order")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time only the vendor BLAS on dense GEMMs of the layer's expert FLOPs and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -349,6 +388,13 @@ def main():
     torch.cuda.set_device(dev)
     run = Runner(args.config, dev, args.combine, args.bands)
     wl = run.wl
+
+    if args.vendor_gemm:
+        _, _, st, _, _ = run.routed()
+        s0 = wl.layers[0]
+        print(json.dumps({"vendor_gemm": True, "workload": wl.name,
+                          "res": vendor_gemm(st[0]["R"], s0.d, s0.f, args.steps, args.warmup)}), flush=True)
+        return
 
     if args.profile_only:
         res = {}
@@ -407,6 +453,12 @@ def main():
         "roofline": roof,
     }
     out.update(gains(ms))
+    if bf16 and len(wl.layers) == 1 and not args.no_baselines:
+        # context, outside the timed region: the vendor BLAS on dense GEMMs
+        # of the same expert FLOPs on this GPU, and the layer against it
+        vg = vendor_gemm(count_stats[0]["R"], wl.layers[0].d, wl.layers[0].f)
+        vg["layer_tflops_over_vendor_gemm"] = round(out["tflops"] / vg["tflops"], 3)
+        out["context_vendor_dense_gemm"] = vg
     if not args.no_ablations and not args.no_baselines:
         out["ablations"] = ablations(run, max(5, args.steps // 2), max(2, args.warmup // 2))
     n0 = None

@@ -57,9 +57,10 @@ def kernel_stats(args):
            "Source hash of the kernels profiled: `%s` (sha256 of csrc/*.hip + *.hpp, first 16 hex)."
            % source_sha(), "",
            "| Kernel | Calls | Avg (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
+    match = args.match.split(",")
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         name = r["Name"]
-        if "moe::" not in name and "copyBuffer" not in name:
+        if not any(m in name for m in match):
             continue
         out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
             _short(name), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
@@ -155,6 +156,8 @@ def main():
     k.add_argument("--kernel", default="k_dynamic")
     k.add_argument("--command", required=True)
     k.add_argument("--note", default="")
+    k.add_argument("--match", default="moe::,copyBuffer",
+                   help="comma-separated substrings: kernels whose names hold one are listed")
     k.add_argument("--trace", default="", help="run_kernel_trace.csv of the same run")
     k.add_argument("--timed", type=int, default=0, help="timed dispatches at the end of the trace")
     k.add_argument("--out", required=True)
