@@ -95,6 +95,21 @@ DEV void st_wt16(void* base, uint32_t byte_off, uint4 v) {
   const u32x4_t d = {v.x, v.y, v.z, v.w};
   __builtin_amdgcn_raw_buffer_store_b128(d, r, byte_off, 0, 16 /* sc1 */);
 }
+// The same with the non-temporal hint, for data written once and read once
+// much later, which should not displace cached lines that other tasks reuse.
+DEV void st_wt16_stream(void* base, uint32_t byte_off, uint4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  const u32x4_t d = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, byte_off, 0, 16 | 2 /* sc1 nt */);
+}
+
+// 16 bytes read with the non-temporal hint: data read once, which should
+// not displace cached lines that other tasks reuse.
+DEV float4 ld_stream4(const float* p) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 // 16 bytes read coherently with device-scope atomics from every XCD (four
 // agent-scope relaxed atomic loads): for data other workgroups may have

@@ -229,6 +229,12 @@ void make_layout(const moe_desc* d, Layout* L) {
       break;
     }
   p.n_cc = d->d / p.comb_cols;
+  // O (the fp32 DOWN rows) larger than the 256 MiB last-level cache cannot
+  // stay cached until the combine reads it: the DOWN tiles then write it with
+  // streaming stores, so it does not displace the weight panels and A rows
+  // that other tiles reuse.
+  p.o_stream = !p.comb_scatter &&
+               sizeof(float) * (size_t)p.splitk * d->T * d->k * d->d > ((size_t)256 << 20);
   const long long qa = (long long)p.n_route + (long long)p.n_rt * (p.route_wide ? 2 : 1);
   const long long qc = (long long)p.max_mt * (p.n_up_n + p.n_down_n * p.splitk) + p.n_sup +
                        p.n_sdown + p.max_perm + (long long)p.n_rt * p.n_cc;

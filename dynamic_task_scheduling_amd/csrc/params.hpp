@@ -104,6 +104,8 @@ struct Params {
                     //    permute tasks, no Xp); 0: permute tasks fill Xp
   int comb_scatter; // 1: DOWN tiles scatter-add w * (H Wd) into y (small layers);
                     // 0: DOWN tiles write O rows, combine tasks sum them
+  int o_stream;    // 1: O is larger than the last-level cache, so DOWN tiles
+                   //    write it with streaming (non-temporal) stores
   int comb_cols;   // y columns per combine task (divides d)
   int n_cc;        // combine chunks per token tile = d / comb_cols
   int q_cap;       // slots per queue

@@ -981,7 +981,8 @@ struct Stages {
   // the K loop).
   template <int BM, int NB>
   static DEV void down_tile(const Elem* A, int lda, int rows, const Elem* wd, int ldb, int K,
-                            float* out, int ldo, char* smem, bool scatter = false) {
+                            float* out, int ldo, char* smem, bool scatter = false,
+                            bool stream = false) {
     using TL = typename GemmSel<Elem, BM, NB>::T;
     static_assert(TL::LDS_BYTES <= kSmemTile, "DOWN tile fits the tile LDS");
     typename TL::Args g;
@@ -1016,6 +1017,12 @@ struct Stages {
         for (int i = tidx(); i < rows * kBN; i += kThreads) {
           const int r = i / kBN, c = i % kBN;
           unsafeAtomicAdd(out + (size_t)s_tok[r] * ldo + m * kBN + c, s_wt[r] * st[r * SLD + c]);
+        }
+      } else if (stream) {
+        for (int i = tidx(); i < rows * CPR; i += kThreads) {
+          const int r = i / CPR, c = i % CPR;
+          st_wt16_stream(uniform_ptr(out + m * kBN), (uint32_t)(r * ldo * 4 + c * 16),
+                         *reinterpret_cast<const uint4*>(st + r * SLD + c * 4));
         }
       } else {
         for (int i = tidx(); i < rows * CPR; i += kThreads) {
@@ -1056,16 +1063,17 @@ struct Stages {
   }
 
   static DEV void down_any(int bm, int nb, const Elem* A, int lda, int rows, const Elem* wd,
-                           int ldb, int K, float* out, int ldo, char* smem, bool scatter) {
+                           int ldb, int K, float* out, int ldo, char* smem, bool scatter,
+                           bool stream = false) {
     by_class(bm, [&](auto c) __attribute__((always_inline)) {
       constexpr int BM = decltype(c)::value;
       if constexpr (TR::kBf16) {
         if (nb == 2) {
-          down_tile<BM, 2>(A, lda, rows, wd, ldb, K, out, ldo, smem, scatter);
+          down_tile<BM, 2>(A, lda, rows, wd, ldb, K, out, ldo, smem, scatter, stream);
           return;
         }
       }
-      down_tile<BM, 1>(A, lda, rows, wd, ldb, K, out, ldo, smem, scatter);
+      down_tile<BM, 1>(A, lda, rows, wd, ldb, K, out, ldo, smem, scatter, stream);
     });
   }
   static DEV void up_any(int bm, const Elem* A, int lda, int rows, const Elem* wg, const Elem* wu,
@@ -1106,7 +1114,7 @@ struct Stages {
       return;
     }
     float* out = o_slice(p, ks) + (size_t)t.row0 * p.d + n0;
-    down_any(t.bm, p.down_nb, A, p.f, t.rows, wd, p.d, K, out, p.d, smem, false);
+    down_any(t.bm, p.down_nb, A, p.f, t.rows, wd, p.d, K, out, p.d, smem, false, p.o_stream != 0);
   }
 
   // DOWN output rows of K slice ks: [T*k][d] fp32.
@@ -1185,7 +1193,8 @@ struct Stages {
     // own; then the first K slice of every kept slot of all items is issued
     // before any is used, then each further K slice as one burst, then the
     // sums; the shared experts' rows and the residual follow as one more
-    // burst (the expert rows' registers are free by then).
+    // burst (the expert rows' registers are free by then).  Each O row is
+    // read once, with the non-temporal hint.
     constexpr int CU = 2;
     for (int i0 = tidx(); i0 < n; i0 += CU * kThreads) {
       int pos[CU][kMaxK];
@@ -1210,7 +1219,7 @@ struct Stages {
         for (int j = 0; j < kMaxK; ++j) {
           v[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (pos[u][j] >= 0)
-            v[u][j] = *reinterpret_cast<const float4*>(p.O + (size_t)pos[u][j] * p.d + col);
+            v[u][j] = ld_stream4(p.O + (size_t)pos[u][j] * p.d + col);
         }
       }
       // further K slices (only layers with a DOWN split-K and combine tasks)
@@ -1222,8 +1231,7 @@ struct Stages {
 #pragma unroll
           for (int j = 0; j < kMaxK; ++j) {
             if (pos[u][j] >= 0) {
-              const float4 b =
-                  *reinterpret_cast<const float4*>(p.O + ks * slice + (size_t)pos[u][j] * p.d + col);
+              const float4 b = ld_stream4(p.O + ks * slice + (size_t)pos[u][j] * p.d + col);
               v[u][j].x += b.x; v[u][j].y += b.y; v[u][j].z += b.z; v[u][j].w += b.w;
             }
           }
