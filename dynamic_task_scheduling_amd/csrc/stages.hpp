@@ -74,9 +74,13 @@ template <typename Elem, int BM, int NB>
 struct GemmSel {
   using T = Tile<Elem, BM, NB>;
 };
+// Row tiles of at most 64 rows stream their weight panels (non-temporal
+// loads): they are mostly the single tiles of lightly loaded experts, whose
+// panels no other tile reads, and the hint keeps those streams from
+// displacing the panels and rows that the larger tiles reuse.
 template <int BM, int NB>
 struct GemmSel<bf16_t, BM, NB> {
-  using T = Tile2<BM, NB, tile2_stages(BM, NB)>;
+  using T = Tile2<BM, NB, tile2_stages(BM, NB), 32, false, (BM <= 64)>;
 };
 // 256-row tiles: 32-deep stages with the loads interleaved into the MFMAs
 template <int NB>

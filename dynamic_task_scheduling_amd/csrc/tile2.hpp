@@ -99,6 +99,23 @@ DEV void dma16s(uint32_t voff, uint64_t base, uint32_t lds_base) {
       : "s"(lds_base), "v"(voff), "s"(sbase));
 }
 
+// The same with the non-temporal hint, for data that should not displace
+// cached lines other tasks reuse.
+DEV void dma16s_nt(uint32_t voff, uint64_t base, uint32_t lds_base) {
+  const uint64_t sbase =
+      ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(sbase));
+}
+
 // C[BM, 128] (x NB matrices sharing A) = A[BM, K] * B[K, 128], bf16 in, fp32
 // accumulate, v_mfma_f32_32x32x16_bf16 (the 32x32 form keeps the matrix pipe
 // far busier with one wave per SIMD than 16x16x32, and halves LDS fragment
@@ -115,7 +132,10 @@ DEV void dma16s(uint32_t voff, uint64_t base, uint32_t lds_base) {
 // ldb >= b_cols); 16-byte chunks past them reload chunk 0 of the same row, so
 // every load stays inside B and only the (discarded) padded output columns
 // see duplicated values.  Used by the router, whose width E may be < 128.
-template <int BM, int NB, int S, int MF = 32, bool CLAMP_B = false>
+//
+// NT_B: B's loads carry the non-temporal hint (weights this tile streams
+// once; see GemmSel).
+template <int BM, int NB, int S, int MF = 32, bool CLAMP_B = false, bool NT_B = false>
 struct Tile2 {
   static_assert(MF == 32, "32x32x16 MFMA tile");
   static constexpr int BN = kBN;
@@ -222,9 +242,11 @@ struct Tile2 {
 #pragma unroll
     for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-      for (int ii = 0; ii < B_INST; ++ii)
-        dma16s(L.b_src[ii], b_base[mtx],
-               __builtin_amdgcn_readfirstlane(stage + L.b_dst + mtx * B_BYTES + ii * 1024));
+      for (int ii = 0; ii < B_INST; ++ii) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + L.b_dst + mtx * B_BYTES + ii * 1024);
+        if constexpr (NT_B) dma16s_nt(L.b_src[ii], b_base[mtx], dst);
+        else dma16s(L.b_src[ii], b_base[mtx], dst);
+      }
   }
 
   template <int KK>
